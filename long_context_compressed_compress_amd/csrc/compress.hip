@@ -1,0 +1,294 @@
+// csa_compress_insert kernel: raw-token append to the compressor state + fused
+// window compression -> RMSNorm -> RoPE at anchor -> rounding -> paged cache insert.
+//
+// [P1] "GPU Compute Saturation" and [P2] "3.2 內核" describe the compressor, RMSNorm, RoPE and the
+// cache write as one fused elementwise kernel per cache instance. [P1] "DeepSeek V4 Attention
+// Architecture" / [P3] "KV 缓存压缩": c4a entry i = weighted sum of raw tokens 4i .. 4i+7, anchor 4i;
+// c128a entry i = weighted sum of 128 raw tokens starting at 128i. [P2] "3.1 顯存": the compressor
+// residual is kept as raw sliding-window pages.
+//
+// Layout of work (one wavefront per unit, 4 wavefronts per workgroup):
+//   * append units: one new raw token; the wave copies its kv row and role logit rows into the state pages.
+//   * entry units: one (sequence, new entry). Lanes split into NLC channel lanes (CH consecutive
+//     channels each, 16- or 32-byte loads) times G row groups; group g folds window rows
+//     t = g, g+G, ... with an online per-channel softmax, then the G partial states merge with
+//     butterfly shuffles. Rows of positions before start_pos come from the state pages, rows of new
+//     positions straight from the inputs, so append and compress run in the same launch without a
+//     dependency between them.
+#include "csa_internal.h"
+
+namespace csa {
+namespace {
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float get(const float* p, int i) { return p[i]; }
+};
+template <> struct Elem<uint16_t> {
+  static __device__ __forceinline__ float get(const uint16_t* p, int i) { return bf16_to_f32(p[i]); }
+};
+
+// Load N values of type T starting at p (16-byte aligned) into floats.
+template <typename T, int N>
+__device__ __forceinline__ void load_vec(const T* p, float (&v)[N]) {
+  constexpr int per16 = 16 / sizeof(T);
+  static_assert(N % per16 == 0, "vector width");
+#pragma unroll
+  for (int c = 0; c < N / per16; ++c) {
+    const uint4 raw = reinterpret_cast<const uint4*>(p)[c];
+    const T* e = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+    for (int k = 0; k < per16; ++k) v[c * per16 + k] = Elem<T>::get(e, k);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void zero_vec(float (&v)[N]) {
+#pragma unroll
+  for (int k = 0; k < N; ++k) v[k] = 0.f;
+}
+
+__device__ __forceinline__ int find_seq(const int32_t* cu, int batch, int row) {
+  int lo = 0, hi = batch - 1;  // largest b with cu[b] <= row
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= row) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <typename TIn, int OUT, int D, int RATIO, int WINDOW>
+__global__ void __launch_bounds__(256) compress_insert_kernel(CompressArgs a) {
+  constexpr int ROLES = WINDOW / RATIO;
+  constexpr int VEC = 16 / int(sizeof(TIn));
+  constexpr int CH = (D / 64 > VEC) ? D / 64 : VEC;
+  constexpr int NLC = D / CH;
+  constexpr int G = 64 / NLC;
+  constexpr int E = kBlock / RATIO;
+  static_assert(D % CH == 0 && NLC <= 64 && (NLC & (NLC - 1)) == 0, "channel split");
+
+  const int lane = threadIdx.x & 63;
+  const int64_t gw = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t n_append = a.total_new;
+  const TIn* kv_new = reinterpret_cast<const TIn*>(a.kv_new);
+  const TIn* lg_new = reinterpret_cast<const TIn*>(a.logit_new);
+  TIn* st_kv = reinterpret_cast<TIn*>(a.state.kv_pages);
+  TIn* st_lg = reinterpret_cast<TIn*>(a.state.logit_pages);
+
+  if (gw < n_append) {
+    // ---------------- append one raw token to the state pages
+    const int row = int(gw);
+    const int b = find_seq(a.cu_new, a.batch, row);
+    if (b >= a.state.batch) return;
+    const int64_t pos = int64_t(a.start_pos[b]) + (row - a.cu_new[b]);
+    const int64_t r = raw_row(a.state.block_table + int64_t(b) * a.state.bt_stride, a.state.bt_stride, a.state.n_phys, pos);
+    if (r < 0) return;
+    constexpr int V16_ROW = D * int(sizeof(TIn)) / 16;  // 16-byte chunks per D-row
+    const uint4* src_kv = reinterpret_cast<const uint4*>(kv_new + int64_t(row) * D);
+    uint4* dst_kv = reinterpret_cast<uint4*>(st_kv + r * D);
+    for (int c = lane; c < V16_ROW; c += 64) dst_kv[c] = src_kv[c];
+    const uint4* src_lg = reinterpret_cast<const uint4*>(lg_new + int64_t(row) * ROLES * D);
+    uint4* dst_lg = reinterpret_cast<uint4*>(st_lg + r * ROLES * D);
+    for (int c = lane; c < V16_ROW * ROLES; c += 64) dst_lg[c] = src_lg[c];
+    return;
+  }
+
+  // ---------------- build one entry
+  const int64_t unit = gw - n_append;
+  const int bound = a.max_entries_bound;
+  if (unit >= int64_t(a.batch) * bound) return;
+  const int b = int(unit / bound);
+  const int c_idx = int(unit % bound);
+  const int64_t start = a.start_pos[b];
+  const int n_new = a.cu_new[b + 1] - a.cu_new[b];
+  const int64_t e0 = num_eligible(start - 1, RATIO, WINDOW);          // entries complete before this call
+  const int64_t e1 = num_eligible(start + n_new - 1, RATIO, WINDOW);  // after it
+  const int64_t count = e1 - e0;
+  if (c_idx == 0 && lane == 0) {
+    if (a.out_new_entries) a.out_new_entries[b] = int32_t(count);
+    if (a.out_slots)
+      for (int c = bound; c < a.max_entries_out; ++c) a.out_slots[int64_t(b) * a.max_entries_out + c] = -1;
+  }
+  if (c_idx >= count) {
+    if (a.out_slots && lane == 0 && c_idx < a.max_entries_out) a.out_slots[int64_t(b) * a.max_entries_out + c_idx] = -1;
+    return;
+  }
+  const int64_t i = e0 + c_idx;
+  const int64_t first = int64_t(RATIO) * i;
+  const int ch_lane = lane % NLC;
+  const int grp = lane / NLC;
+  const int ch0 = ch_lane * CH;
+  const int cu_b = a.cu_new[b];
+  const int32_t* st_bt = (b < a.state.batch) ? a.state.block_table + int64_t(b) * a.state.bt_stride : nullptr;
+
+  float m[CH], s[CH], acc[CH];
+#pragma unroll
+  for (int k = 0; k < CH; ++k) { m[k] = -INFINITY; s[k] = 0.f; acc[k] = 0.f; }
+
+  for (int t = grp; t < WINDOW; t += G) {
+    const int64_t pos = first + t;
+    const int role = t / RATIO;
+    float x[CH], l[CH];
+    if (pos >= start) {
+      const int64_t row = cu_b + (pos - start);
+      load_vec<TIn, CH>(kv_new + row * D + ch0, x);
+      load_vec<TIn, CH>(lg_new + (row * ROLES + role) * D + ch0, l);
+    } else {
+      const int64_t r = st_bt ? raw_row(st_bt, a.state.bt_stride, a.state.n_phys, pos) : -1;
+      if (r >= 0) {
+        load_vec<TIn, CH>(st_kv + r * D + ch0, x);
+        load_vec<TIn, CH>(st_lg + (r * ROLES + role) * D + ch0, l);
+      } else {
+        zero_vec(x);
+        zero_vec(l);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const float mn = fmaxf(m[k], l[k]);
+      const float f_old = __expf(m[k] - mn);  // exp(-inf) = 0 on the first row
+      const float f_new = __expf(l[k] - mn);
+      s[k] = s[k] * f_old + f_new;
+      acc[k] = acc[k] * f_old + f_new * x[k];
+      m[k] = mn;
+    }
+  }
+  // merge the G row groups (butterfly over the group bits of the lane id)
+#pragma unroll
+  for (int off = NLC; off < 64; off <<= 1) {
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const float m2 = __shfl_xor(m[k], off);
+      const float s2 = __shfl_xor(s[k], off);
+      const float a2 = __shfl_xor(acc[k], off);
+      const float mn = fmaxf(m[k], m2);
+      const float f1 = (m[k] == -INFINITY) ? 0.f : __expf(m[k] - mn);
+      const float f2 = (m2 == -INFINITY) ? 0.f : __expf(m2 - mn);
+      s[k] = s[k] * f1 + s2 * f2;
+      acc[k] = acc[k] * f1 + a2 * f2;
+      m[k] = mn;
+    }
+  }
+  float y[CH];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < CH; ++k) {
+    y[k] = acc[k] / s[k];
+    ss += y[k] * y[k];
+  }
+#pragma unroll
+  for (int off = 1; off < NLC; off <<= 1) ss += __shfl_xor(ss, off);
+  const float rms = sqrtf(ss / float(D) + a.eps);
+#pragma unroll
+  for (int k = 0; k < CH; ++k) y[k] = y[k] / rms * a.gamma[ch0 + k];
+
+  // RoPE at the anchor on dims [D-R, D), interleaved pairs (each lane owns whole pairs)
+  const int R = a.cache.rope_dims;
+  const int base = D - R;
+  if (R > 0 && first < a.rope_rows) {
+    const float* cs = a.rope_cs + first * int64_t(R);  // row stride R/2 pairs * 2 floats
+#pragma unroll
+    for (int k = 0; k < CH; k += 2) {
+      const int c = ch0 + k;
+      if (c >= base) {
+        const int j = (c - base) >> 1;
+        const float co = cs[2 * j], si = cs[2 * j + 1];
+        const float u = y[k], v = y[k + 1];
+        y[k] = u * co - v * si;
+        y[k + 1] = u * si + v * co;
+      }
+    }
+  }
+
+  const int64_t slot = entry_row(a.cache.block_table + int64_t(b) * a.cache.bt_stride, a.cache.bt_stride,
+                                 a.cache.n_phys, i, E);
+  const bool in_table = b < a.cache.batch && slot >= 0;
+  if (OUT == 2) {
+    float amax = 0.f;
+#pragma unroll
+    for (int k = 0; k < CH; ++k) amax = fmaxf(amax, fabsf(y[k]));
+#pragma unroll
+    for (int off = 1; off < NLC; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    if (in_table && grp == 0) {
+      uint8_t* dst = reinterpret_cast<uint8_t*>(a.cache.pages) + slot * D + ch0;
+      uint32_t packed[CH / 4];
+      if (amax > 0.f) {
+        const float inv = 448.0f / amax;
+#pragma unroll
+        for (int k = 0; k < CH / 4; ++k) {
+          packed[k] = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) packed[k] |= f32_to_e4m3_rne(y[4 * k + e] * inv) << (8 * e);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < CH / 4; ++k) packed[k] = 0;
+      }
+#pragma unroll
+      for (int k = 0; k < CH / 4; ++k) reinterpret_cast<uint32_t*>(dst)[k] = packed[k];
+      if (ch_lane == 0) a.cache.scales[slot] = amax > 0.f ? amax / 448.0f : 1.0f;
+    }
+  } else if (OUT == 1) {
+    if (in_table && grp == 0) {
+      uint16_t* dst = reinterpret_cast<uint16_t*>(a.cache.pages) + slot * D + ch0;
+      uint32_t packed[CH / 2];
+#pragma unroll
+      for (int k = 0; k < CH / 2; ++k)
+        packed[k] = uint32_t(f32_to_bf16_rne(y[2 * k])) | (uint32_t(f32_to_bf16_rne(y[2 * k + 1])) << 16);
+#pragma unroll
+      for (int k = 0; k < CH / 2; ++k) reinterpret_cast<uint32_t*>(dst)[k] = packed[k];
+    }
+  } else {
+    if (in_table && grp == 0) {
+      float* dst = reinterpret_cast<float*>(a.cache.pages) + slot * D + ch0;
+#pragma unroll
+      for (int k = 0; k < CH; ++k) dst[k] = y[k];
+    }
+  }
+  if (a.out_slots && lane == 0 && c_idx < a.max_entries_out)
+    a.out_slots[int64_t(b) * a.max_entries_out + c_idx] = in_table ? int32_t(slot) : -1;
+}
+
+template <typename TIn, int OUT, int D>
+hipError_t dispatch_ratio(const CompressArgs& a, hipStream_t stream) {
+  const int64_t units = int64_t(a.total_new) + int64_t(a.batch) * a.max_entries_bound;
+  if (units == 0) return hipSuccess;
+  const int64_t blocks = (units + 3) / 4;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (a.cache.ratio == 4)
+    hipLaunchKernelGGL((compress_insert_kernel<TIn, OUT, D, 4, 8>), dim3(unsigned(blocks)), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((compress_insert_kernel<TIn, OUT, D, 128, 128>), dim3(unsigned(blocks)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename TIn, int OUT>
+hipError_t dispatch_dim(const CompressArgs& a, hipStream_t stream) {
+  switch (a.cache.dim) {
+    case 32: return dispatch_ratio<TIn, OUT, 32>(a, stream);
+    case 64: return dispatch_ratio<TIn, OUT, 64>(a, stream);
+    case 128: return dispatch_ratio<TIn, OUT, 128>(a, stream);
+    case 256: return dispatch_ratio<TIn, OUT, 256>(a, stream);
+    case 512: return dispatch_ratio<TIn, OUT, 512>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename TIn>
+hipError_t dispatch_out(const CompressArgs& a, hipStream_t stream) {
+  switch (a.cache.dtype) {
+    case CSA_F32: return dispatch_dim<TIn, 0>(a, stream);
+    case CSA_BF16: return dispatch_dim<TIn, 1>(a, stream);
+    case CSA_FP8_E4M3: return dispatch_dim<TIn, 2>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_compress(const CompressArgs& a, hipStream_t stream) {
+  if (a.state.dtype == CSA_F32) return dispatch_out<float>(a, stream);
+  return dispatch_out<uint16_t>(a, stream);
+}
+
+}  // namespace csa

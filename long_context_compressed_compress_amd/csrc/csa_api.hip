@@ -1,0 +1,229 @@
+// C ABI of libcsa: host-side argument validation (before any HIP call), workspace sizing and
+// dispatch to the kernel launchers. Declarations and semantics: include/csa.h.
+#include <math.h>
+
+#include "csa_internal.h"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool valid_shape(int ratio, int window) { return (ratio == 4 && window == 8) || (ratio == 128 && window == 128); }
+bool valid_dim(int d) { return d == 32 || d == 64 || d == 128 || d == 256 || d == 512; }
+bool valid_dtype(csa_dtype_t t) { return t == CSA_F32 || t == CSA_BF16 || t == CSA_FP8_E4M3; }
+
+bool valid_cache(const csa_cache_t* c) {
+  if (!c) return false;
+  if (!valid_shape(c->ratio, c->window) || !valid_dim(c->dim)) return false;
+  if (c->rope_dims < 0 || c->rope_dims > c->dim || (c->rope_dims & 1)) return false;
+  if (!valid_dtype(c->dtype) || !c->pages || !aligned(c->pages, 16)) return false;
+  if (c->dtype == CSA_FP8_E4M3 && !c->scales) return false;
+  if (!c->block_table || c->batch < 1 || c->bt_stride < 1 || c->n_phys < 1) return false;
+  return true;
+}
+
+bool valid_raw_common(const csa_raw_t* r, int dim) {
+  if (!r || r->dim != dim || !valid_dtype(r->dtype) || !r->kv_pages || !aligned(r->kv_pages, 16)) return false;
+  if (!r->block_table || r->batch < 1 || r->bt_stride < 1 || r->n_phys < 1) return false;
+  return true;
+}
+
+csa_status_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return CSA_OK;
+  g_last_hip_error = int32_t(e);
+  return CSA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t csa_version(void) { return 1; }
+
+const char* csa_status_string(csa_status_t s) {
+  switch (s) {
+    case CSA_OK: return "ok";
+    case CSA_ERR_INVALID_ARG: return "invalid argument";
+    case CSA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case CSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case CSA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t csa_last_hip_error(void) { return g_last_hip_error; }
+
+int64_t csa_num_entries(int64_t n_raw, int32_t ratio, int32_t window) {
+  if (!valid_shape(ratio, window)) return -1;
+  return n_raw >= window ? (n_raw - window) / ratio + 1 : 0;
+}
+
+int64_t csa_num_eligible(int64_t q_pos, int32_t ratio, int32_t window) {
+  return csa_num_entries(q_pos + 1, ratio, window);
+}
+
+int64_t csa_entry_slot(const int32_t* bt_row, int64_t entry, int32_t ratio) {
+  if (!bt_row || entry < 0 || (ratio != 4 && ratio != 128)) return -1;
+  const int64_t e = csa::kBlock / ratio;
+  return int64_t(bt_row[entry / e]) * e + entry % e;
+}
+
+int64_t csa_raw_slot(const int32_t* bt_row, int64_t pos) {
+  if (!bt_row || pos < 0) return -1;
+  return int64_t(bt_row[pos / csa::kBlock]) * csa::kBlock + pos % csa::kBlock;
+}
+
+csa_status_t csa_compress_insert(const csa_cache_t* cache, const csa_raw_t* state, int32_t batch,
+                                 const int32_t* start_pos, const int32_t* cu_new, int32_t total_new,
+                                 int32_t max_new_per_seq, const void* kv_new, const void* logit_new,
+                                 const float* gamma, float rms_eps, const float* rope_cs, int32_t rope_rows,
+                                 int32_t* out_slots, int32_t max_entries_out, int32_t* out_new_entries,
+                                 hipStream_t stream) {
+  if (!valid_cache(cache) || !valid_raw_common(state, cache ? cache->dim : -1)) return CSA_ERR_INVALID_ARG;
+  if (state->dtype != CSA_F32 && state->dtype != CSA_BF16) return CSA_ERR_INVALID_ARG;
+  if (state->roles != cache->window / cache->ratio || !state->logit_pages || !aligned(state->logit_pages, 16))
+    return CSA_ERR_INVALID_ARG;
+  if (batch < 0 || total_new < 0 || max_new_per_seq < 0) return CSA_ERR_INVALID_ARG;
+  if (batch > 0 && (!start_pos || !cu_new || batch > cache->batch || batch > state->batch)) return CSA_ERR_INVALID_ARG;
+  if (total_new > 0 && (!kv_new || !logit_new || !aligned(kv_new, 16) || !aligned(logit_new, 16)))
+    return CSA_ERR_INVALID_ARG;
+  if (!gamma || !(rms_eps >= 0.f) || !isfinite(rms_eps)) return CSA_ERR_INVALID_ARG;
+  if (cache->rope_dims > 0 && (!rope_cs || rope_rows < 1)) return CSA_ERR_INVALID_ARG;
+  const int bound = (max_new_per_seq + cache->ratio - 1) / cache->ratio;
+  if (out_slots && max_entries_out < bound) return CSA_ERR_INVALID_ARG;
+  if (batch == 0) return CSA_OK;
+  csa::CompressArgs a{*cache, *state, batch, start_pos, cu_new, total_new, max_new_per_seq, bound,
+                      kv_new, logit_new, gamma, rms_eps, rope_cs, rope_rows, out_slots,
+                      out_slots ? max_entries_out : 0, out_new_entries};
+  return hip_status(csa::launch_compress(a, stream));
+}
+
+size_t csa_index_topk_workspace(int32_t n_q, int64_t max_elig, int32_t k, int32_t n_heads) {
+  (void)n_heads;
+  if (n_q < 0 || max_elig < 0 || k < 1) return 0;
+  return csa::index_workspace(n_q, max_elig, k);
+}
+
+}  // extern "C"
+
+namespace {
+
+csa_status_t index_check(const csa_cache_t* idx_cache, int32_t n_q, const int32_t* q_seq, const int32_t* q_pos,
+                         int64_t max_elig, int32_t k, void* workspace, size_t workspace_bytes) {
+  if (!valid_cache(idx_cache) || n_q < 0 || max_elig < 0 || max_elig > 0x7FFFFFFF) return CSA_ERR_INVALID_ARG;
+  if (k < 1 || k > csa::kMaxK) return CSA_ERR_INVALID_ARG;
+  if (n_q > 0 && (!q_seq || !q_pos)) return CSA_ERR_INVALID_ARG;
+  const size_t need = csa::index_workspace(n_q, max_elig, k);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return CSA_ERR_WORKSPACE;
+  return CSA_OK;
+}
+
+csa_status_t score_check(const csa_cache_t* idx_cache, int32_t n_q, const void* q_idx, csa_dtype_t q_dtype,
+                         int32_t n_heads, const float* head_w, csa_score_t mode) {
+  if (n_heads < 1 || n_heads > 128) return CSA_ERR_INVALID_ARG;
+  if (mode != CSA_SCORE_DOT && mode != CSA_SCORE_WRELU) return CSA_ERR_INVALID_ARG;
+  if (mode == CSA_SCORE_DOT && n_heads != 1) return CSA_ERR_INVALID_ARG;
+  if (q_dtype != CSA_F32 && q_dtype != CSA_BF16) return CSA_ERR_INVALID_ARG;
+  if (n_q > 0 && (!q_idx || !aligned(q_idx, 16))) return CSA_ERR_INVALID_ARG;
+  if (n_q > 0 && mode == CSA_SCORE_WRELU && !head_w) return CSA_ERR_INVALID_ARG;
+  if (!csa::index_supported(*idx_cache, q_dtype, n_heads, mode)) return CSA_ERR_UNSUPPORTED;
+  return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+csa_status_t csa_index_workspace_clear(void* workspace, size_t workspace_bytes, int32_t n_q, hipStream_t stream) {
+  if (n_q < 0) return CSA_ERR_INVALID_ARG;
+  if (n_q == 0) return CSA_OK;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < csa::index_clean_bytes(n_q)) return CSA_ERR_WORKSPACE;
+  return hip_status(csa::launch_index_clear(workspace, n_q, stream));
+}
+
+csa_status_t csa_index_score(const csa_cache_t* idx_cache, int32_t n_q, const int32_t* q_seq, const int32_t* q_pos,
+                             int64_t max_elig, const void* q_idx, csa_dtype_t q_dtype, int32_t n_heads,
+                             const float* head_w, csa_score_t mode, int32_t k, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  csa_status_t st = index_check(idx_cache, n_q, q_seq, q_pos, max_elig, k, workspace, workspace_bytes);
+  if (st != CSA_OK) return st;
+  st = score_check(idx_cache, n_q, q_idx, q_dtype, n_heads, head_w, mode);
+  if (st != CSA_OK || n_q == 0) return st;
+  csa::IndexArgs a{*idx_cache, n_q, q_seq, q_pos, max_elig, q_idx, q_dtype, n_heads, head_w, mode, k,
+                   nullptr, nullptr, nullptr, workspace};
+  return hip_status(csa::launch_index_score(a, stream));
+}
+
+csa_status_t csa_index_select(const csa_cache_t* idx_cache, int32_t n_q, const int32_t* q_seq, const int32_t* q_pos,
+                              int64_t max_elig, int32_t k, int32_t* out_idx, int32_t* out_count, float* out_scores,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  csa_status_t st = index_check(idx_cache, n_q, q_seq, q_pos, max_elig, k, workspace, workspace_bytes);
+  if (st != CSA_OK) return st;
+  if (n_q > 0 && !out_idx) return CSA_ERR_INVALID_ARG;
+  if (n_q == 0) return CSA_OK;
+  csa::IndexArgs a{*idx_cache, n_q, q_seq, q_pos, max_elig, nullptr, CSA_BF16, 1, nullptr, CSA_SCORE_DOT, k,
+                   out_idx, out_count, out_scores, workspace};
+  return hip_status(csa::launch_index_select(a, stream));
+}
+
+csa_status_t csa_index_topk(const csa_cache_t* idx_cache, int32_t n_q, const int32_t* q_seq, const int32_t* q_pos,
+                            int64_t max_elig, const void* q_idx, csa_dtype_t q_dtype, int32_t n_heads,
+                            const float* head_w, csa_score_t mode, int32_t k, int32_t* out_idx, int32_t* out_count,
+                            float* out_scores, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  csa_status_t st = index_check(idx_cache, n_q, q_seq, q_pos, max_elig, k, workspace, workspace_bytes);
+  if (st != CSA_OK) return st;
+  st = score_check(idx_cache, n_q, q_idx, q_dtype, n_heads, head_w, mode);
+  if (st != CSA_OK) return st;
+  if (n_q > 0 && !out_idx) return CSA_ERR_INVALID_ARG;
+  if (n_q == 0) return CSA_OK;
+  csa::IndexArgs a{*idx_cache, n_q, q_seq, q_pos, max_elig, q_idx, q_dtype, n_heads, head_w, mode, k,
+                   out_idx, out_count, out_scores, workspace};
+  hipError_t e = csa::launch_index_score(a, stream);
+  if (e == hipSuccess) e = csa::launch_index_select(a, stream);
+  return hip_status(e);
+}
+
+size_t csa_attend_workspace(int32_t n_q, int32_t n_heads, int32_t dim, int32_t max_keys) {
+  (void)n_q; (void)n_heads; (void)dim; (void)max_keys;
+  return 0;
+}
+
+csa_status_t csa_attend(const csa_cache_t* kv_cache, const csa_raw_t* swa, int32_t swa_window, int32_t n_q,
+                        const int32_t* q_seq, const int32_t* q_pos, const void* q, csa_dtype_t q_dtype,
+                        int32_t n_heads, const int32_t* topk_idx, int32_t k, int64_t max_elig, float softmax_scale,
+                        int32_t fuse_inv_rope, const float* rope_cs, int32_t rope_rows, float* out, float* out_lse,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  (void)workspace; (void)workspace_bytes;
+  if (!valid_cache(kv_cache) || !valid_raw_common(swa, kv_cache ? kv_cache->dim : -1)) return CSA_ERR_INVALID_ARG;
+  if (swa->dtype != kv_cache->dtype || swa->roles != 0) return CSA_ERR_INVALID_ARG;
+  if (swa->dtype == CSA_FP8_E4M3 && !swa->scales) return CSA_ERR_INVALID_ARG;
+  if (swa_window < 0 || swa_window > 1024 || n_q < 0 || n_heads < 1 || n_heads > 128) return CSA_ERR_INVALID_ARG;
+  if (topk_idx && (k < 1 || k > csa::kMaxK)) return CSA_ERR_INVALID_ARG;
+  if (max_elig < 0 || !isfinite(softmax_scale) || (fuse_inv_rope != 0 && fuse_inv_rope != 1)) return CSA_ERR_INVALID_ARG;
+  if (q_dtype != CSA_F32 && q_dtype != CSA_BF16) return CSA_ERR_INVALID_ARG;
+  if (n_q > 0 && (!q_seq || !q_pos || !q || !out || !aligned(q, 16))) return CSA_ERR_INVALID_ARG;
+  if (fuse_inv_rope && kv_cache->rope_dims > 0 && (!rope_cs || rope_rows < 1)) return CSA_ERR_INVALID_ARG;
+  if (!csa::attend_supported(*kv_cache, q_dtype, n_heads)) return CSA_ERR_UNSUPPORTED;
+  if (n_q == 0) return CSA_OK;
+  csa::AttendArgs a{*kv_cache, *swa, swa_window, n_q, q_seq, q_pos, q, q_dtype, n_heads, topk_idx,
+                    topk_idx ? k : 0, max_elig, softmax_scale, fuse_inv_rope, rope_cs, rope_rows, out, out_lse};
+  return hip_status(csa::launch_attend(a, stream));
+}
+
+csa_status_t csa_inv_rope(int32_t n_q, int32_t n_heads, int32_t dim, int32_t rope_dims, const int32_t* q_pos,
+                          const float* rope_cs, int32_t rope_rows, float* io, hipStream_t stream) {
+  if (n_q < 0 || n_heads < 1 || dim < 2 || rope_dims < 0 || rope_dims > dim || (rope_dims & 1)) return CSA_ERR_INVALID_ARG;
+  if (n_q > 0 && rope_dims > 0 && (!q_pos || !rope_cs || !io || rope_rows < 1)) return CSA_ERR_INVALID_ARG;
+  if (n_q == 0 || rope_dims == 0) return CSA_OK;
+  return hip_status(csa::launch_inv_rope(n_q, n_heads, dim, rope_dims, q_pos, rope_cs, rope_rows, io, stream));
+}
+
+csa_status_t csa_rope_table(int32_t rows, int32_t rope_dims, double theta, float* rope_cs, hipStream_t stream) {
+  if (rows < 0 || rope_dims < 2 || (rope_dims & 1) || !(theta > 0.0) || !isfinite(theta)) return CSA_ERR_INVALID_ARG;
+  if (rows > 0 && !rope_cs) return CSA_ERR_INVALID_ARG;
+  if (rows == 0) return CSA_OK;
+  return hip_status(csa::launch_rope_table(rows, rope_dims, theta, rope_cs, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,172 @@
+"""Host-side checks of the C ABI (no GPU needed): exports, pure helpers, argument validation.
+
+Every invalid call must return its status before any HIP call is made, so these run on a CPU-only
+machine: a call that reached a kernel launch would come back as CSA_ERR_HIP instead.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import long_context_compressed_compress_amd as csa
+from oracle import paging
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 1 << 20  # aligned non-null pointer value that is never dereferenced on these paths
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(csa.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return csa.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    with open(os.path.join(ROOT, "include", "csa.h")) as f:
+        text = f.read()
+    names = set(re.findall(r"^\s*(?:[A-Za-z_][A-Za-z0-9_ ]*[\s*])?(csa_[a-z_]+)\(", text, flags=re.M))
+    names |= set(re.findall(r"\b(csa_[a-z_]+)\s*\(", text))
+    names = {n for n in names if not n.endswith("_t")}
+    assert {"csa_compress_insert", "csa_index_topk", "csa_attend", "csa_inv_rope", "csa_rope_table"} <= names
+    for n in sorted(names):
+        assert hasattr(L, n), n
+
+
+def test_host_helpers_match_oracle(L):
+    for m, w in ((4, 8), (128, 128)):
+        for n in (0, 1, 7, 8, 9, 127, 128, 129, 255, 256, 131073, 1048577):
+            assert L.csa_num_entries(n, m, w) == paging.num_entries(n, m, w)
+            assert L.csa_num_eligible(n, m, w) == paging.num_eligible(n, m, w)
+    assert L.csa_num_entries(100, 4, 4) == -1
+    bt = np.array([7, 3, 11, 0], dtype=np.int32)
+    p = bt.ctypes.data_as(ctypes.c_void_p)
+    for m in (4, 128):
+        for i in range(4 * 256 // m):
+            assert L.csa_entry_slot(p, i, m) == paging.entry_slot(bt, i, m)
+    for j in (0, 1, 255, 256, 700, 1023):
+        assert L.csa_raw_slot(p, j) == paging.raw_slot(bt, j)
+    assert L.csa_entry_slot(None, 0, 4) == -1
+    assert L.csa_status_string(3) == b"workspace missing or too small"
+    assert L.csa_version() >= 1
+
+
+def _cache(**kw):
+    d = dict(ratio=4, window=8, dim=128, rope_dims=64, dtype=csa.BF16, pages=FAKE, scales=None, block_table=FAKE,
+             batch=2, bt_stride=4, n_phys=8)
+    d.update(kw)
+    return csa.CacheDesc(**d)
+
+
+def _raw(**kw):
+    d = dict(dtype=csa.BF16, dim=128, roles=2, kv_pages=FAKE, logit_pages=FAKE, scales=None, block_table=FAKE,
+             batch=2, bt_stride=4, n_phys=8)
+    d.update(kw)
+    return csa.RawDesc(**d)
+
+
+def _compress(L, cache=None, state=None, **kw):
+    a = dict(batch=2, start_pos=FAKE, cu_new=FAKE, total_new=2, max_new=1, kv=FAKE, lg=FAKE, gamma=FAKE, eps=1e-6,
+             cs=FAKE, rows=10, slots=FAKE, max_out=1, counts=FAKE)
+    a.update(kw)
+    c = cache if cache is not None else _cache()
+    s = state if state is not None else _raw()
+    return L.csa_compress_insert(ctypes.byref(c), ctypes.byref(s), a["batch"], a["start_pos"], a["cu_new"],
+                                 a["total_new"], a["max_new"], a["kv"], a["lg"], a["gamma"], a["eps"], a["cs"],
+                                 a["rows"], a["slots"], a["max_out"], a["counts"], None)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(cache=_cache(ratio=4, window=4)), dict(cache=_cache(ratio=128, window=8)), dict(cache=_cache(dim=96)),
+    dict(cache=_cache(rope_dims=3)), dict(cache=_cache(rope_dims=256)), dict(cache=_cache(dtype=7)),
+    dict(cache=_cache(pages=None)), dict(cache=_cache(pages=FAKE + 4)), dict(cache=_cache(dtype=csa.FP8, scales=None)),
+    dict(cache=_cache(block_table=None)), dict(cache=_cache(n_phys=0)), dict(cache=_cache(batch=1)),
+    dict(state=_raw(dim=64)), dict(state=_raw(roles=1)), dict(state=_raw(dtype=csa.FP8)),
+    dict(state=_raw(logit_pages=None)), dict(batch=-1), dict(total_new=-1), dict(start_pos=None), dict(kv=None),
+    dict(kv=FAKE + 2), dict(gamma=None), dict(eps=-1.0), dict(eps=float("nan")), dict(cs=None), dict(rows=0),
+    dict(max_new=5, max_out=1),
+])
+def test_compress_validation(L, bad):
+    assert _compress(L, **bad) == INVALID
+
+
+def test_compress_empty_batch_is_ok_without_launch(L):
+    assert _compress(L, batch=0, start_pos=None, cu_new=None, total_new=0) == OK
+
+
+def _index(L, cache=None, **kw):
+    a = dict(n_q=2, q_seq=FAKE, q_pos=FAKE, max_elig=1000, q=FAKE, q_dtype=csa.BF16, heads=64, w=FAKE,
+             mode=csa.SCORE_WRELU, k=512, out=FAKE, cnt=None, sc=None, ws=FAKE, ws_bytes=None)
+    a.update(kw)
+    c = cache if cache is not None else _cache()
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = L.csa_index_topk_workspace(a["n_q"], a["max_elig"], a["k"], a["heads"])
+    return L.csa_index_topk(ctypes.byref(c), a["n_q"], a["q_seq"], a["q_pos"], a["max_elig"], a["q"], a["q_dtype"],
+                            a["heads"], a["w"], a["mode"], a["k"], a["out"], a["cnt"], a["sc"], a["ws"],
+                            a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(k=0), INVALID), (dict(k=2049), INVALID), (dict(heads=0), INVALID), (dict(heads=129), INVALID),
+    (dict(mode=5), INVALID), (dict(mode=csa.SCORE_DOT, heads=2), INVALID), (dict(w=None), INVALID),
+    (dict(q_dtype=csa.FP8), INVALID), (dict(out=None), INVALID), (dict(max_elig=-1), INVALID),
+    (dict(q=FAKE + 8), INVALID), (dict(q_dtype=csa.F32), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=100), WORKSPACE), (dict(ws=FAKE + 16), WORKSPACE),
+])
+def test_index_validation(L, bad, code):
+    assert _index(L, **bad) == code
+
+
+def test_index_unsupported_shape(L):
+    # fp32 cache with a bf16 query, and a too-wide VALU head block
+    assert _index(L, cache=_cache(dtype=csa.F32), q_dtype=csa.BF16) == UNSUPPORTED
+    assert _index(L, cache=_cache(dim=512), heads=64) == UNSUPPORTED
+
+
+def test_index_workspace_grows_with_inputs(L):
+    a = L.csa_index_topk_workspace(4, 262143, 512, 64)
+    b = L.csa_index_topk_workspace(4, 262143 * 2, 512, 64)
+    assert 0 < a < b
+    assert a >= 4 * 262143 * 12  # keys + candidate pairs
+
+
+def _attend(L, cache=None, swa=None, **kw):
+    a = dict(win=128, n_q=2, q_seq=FAKE, q_pos=FAKE, q=FAKE, q_dtype=csa.BF16, heads=64, topk=FAKE, k=512,
+             max_elig=1000, scale=0.05, fuse=1, cs=FAKE, rows=10, out=FAKE, lse=None)
+    a.update(kw)
+    c = cache if cache is not None else _cache(dim=512)
+    s = swa if swa is not None else _raw(dim=512, roles=0, logit_pages=None)
+    return L.csa_attend(ctypes.byref(c), ctypes.byref(s), a["win"], a["n_q"], a["q_seq"], a["q_pos"], a["q"],
+                        a["q_dtype"], a["heads"], a["topk"], a["k"], a["max_elig"], a["scale"], a["fuse"], a["cs"],
+                        a["rows"], a["out"], a["lse"], None, 0, None)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(win=-1), dict(win=1025), dict(heads=0), dict(k=0), dict(k=4096), dict(max_elig=-1),
+    dict(scale=float("inf")), dict(fuse=2), dict(cs=None), dict(out=None), dict(q=None), dict(q_dtype=csa.FP8),
+    dict(swa=_raw(dim=512, roles=0, logit_pages=None, dtype=csa.F32)), dict(swa=_raw(dim=128, roles=0)),
+    dict(swa=_raw(dim=512, roles=2)), dict(cache=_cache(dim=512, dtype=csa.FP8, scales=FAKE),
+                                             swa=_raw(dim=512, roles=0, dtype=csa.FP8, scales=None)),
+])
+def test_attend_validation(L, bad):
+    assert _attend(L, **bad) == INVALID
+
+
+def test_attend_unsupported(L):
+    assert _attend(L, cache=_cache(dim=512, dtype=csa.F32), swa=_raw(dim=512, roles=0, dtype=csa.F32),
+                   q_dtype=csa.BF16) == UNSUPPORTED
+
+
+def test_inv_rope_and_table_validation(L):
+    assert L.csa_inv_rope(2, 4, 128, 3, FAKE, FAKE, 10, FAKE, None) == INVALID
+    assert L.csa_inv_rope(2, 4, 128, 256, FAKE, FAKE, 10, FAKE, None) == INVALID
+    assert L.csa_inv_rope(2, 4, 128, 64, None, FAKE, 10, FAKE, None) == INVALID
+    assert L.csa_inv_rope(0, 4, 128, 64, None, None, 0, None, None) == OK
+    assert L.csa_rope_table(10, 3, 10000.0, FAKE, None) == INVALID
+    assert L.csa_rope_table(10, 64, -1.0, FAKE, None) == INVALID
+    assert L.csa_rope_table(10, 64, 10000.0, None, None) == INVALID
+    assert L.csa_rope_table(0, 64, 10000.0, None, None) == OK
