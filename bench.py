@@ -147,6 +147,8 @@ def run_gpu(args, lens):
     topk = torch.empty((B, K_TOP), dtype=torch.int32, device="cuda")
     out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
     scale = 1.0 / math.sqrt(D)
+    att_ws_bytes = csa.attend_workspace(B, H, D, K_TOP + SWA)
+    att_ws = torch.empty(max(att_ws_bytes, 1), dtype=torch.uint8, device="cuda")
 
     def step(ly, ev=None):
         if ev: ev[0].record()
@@ -157,7 +159,8 @@ def run_gpu(args, lens):
         if ev: ev[2].record()
         csa.index_select(ly.icache, ly.seq, ly.pos, max_elig, K_TOP, topk, ws)
         if ev: ev[3].record()
-        csa.attend(ly.cache, ly.swa, SWA, ly.seq, ly.pos, ly.q, topk, max_elig, scale, True, rope_main, out)
+        csa.attend(ly.cache, ly.swa, SWA, ly.seq, ly.pos, ly.q, topk, max_elig, scale, True, rope_main, out,
+                   workspace=att_ws)
         if ev: ev[4].record()
 
     for i in range(args.warmup):

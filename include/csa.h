@@ -179,7 +179,10 @@ csa_status_t csa_index_select(const csa_cache_t* idx_cache, int32_t n_q, const i
  * out [n_q][n_heads][D] fp32; out_lse [n_q][n_heads] natural-log sum of exp of the scaled
  * logits (may be NULL). fuse_inv_rope = 1 applies the inverse rotation at q_pos to out.
  * swa_window in [0, 1024]; n_heads in [1, 128]; k in [1, 2048] when topk_idx != NULL.
- * Workspace: csa_attend_workspace(...) bytes (may be 0 -> workspace may be NULL).
+ * Workspace: csa_attend_workspace(n_q, n_heads, dim, max_keys) bytes, 16-byte aligned, with
+ * max_keys = (topk_idx ? k : max_elig) + swa_window. It is non-zero only for dim 512 with a multiple
+ * of 64 heads and few enough queries that each query's keys are split over several workgroups
+ * (partial softmax states are merged by a second kernel); 0 means workspace may be NULL.
  * ------------------------------------------------------------------------------------------- */
 size_t csa_attend_workspace(int32_t n_q, int32_t n_heads, int32_t dim, int32_t max_keys);
 csa_status_t csa_attend(const csa_cache_t* kv_cache, const csa_raw_t* swa, int32_t swa_window,

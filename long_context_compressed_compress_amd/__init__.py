@@ -212,14 +212,22 @@ def index_select(cache: Cache, q_seq: torch.Tensor, q_pos: torch.Tensor, max_eli
 
 def attend(cache: Cache, swa: Raw, swa_window: int, q_seq: torch.Tensor, q_pos: torch.Tensor, q: torch.Tensor,
            topk_idx: Optional[torch.Tensor], max_elig: int, softmax_scale: float, fuse_inv_rope: bool,
-           rope_cs: torch.Tensor, out: torch.Tensor, out_lse: Optional[torch.Tensor] = None, stream=None) -> None:
+           rope_cs: torch.Tensor, out: torch.Tensor, out_lse: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     n_q, n_heads = q.shape[0], q.shape[1]
     cd, sd = cache.desc(), swa.desc()
     k = 0 if topk_idx is None else topk_idx.shape[1]
+    if workspace is None:
+        need = attend_workspace(n_q, n_heads, q.shape[2], (k if topk_idx is not None else max_elig) + swa_window)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
     _check("csa_attend", lib().csa_attend(
         ctypes.byref(cd), ctypes.byref(sd), swa_window, n_q, _ptr(q_seq), _ptr(q_pos), _ptr(q), dtype_code(q),
         n_heads, _ptr(topk_idx), k, max_elig, softmax_scale, int(fuse_inv_rope), _ptr(rope_cs), rope_cs.shape[0],
-        _ptr(out), _ptr(out_lse), None, 0, _stream(stream)))
+        _ptr(out), _ptr(out_lse), _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))
+
+
+def attend_workspace(n_q: int, n_heads: int, dim: int, max_keys: int) -> int:
+    return int(lib().csa_attend_workspace(n_q, n_heads, dim, max_keys))
 
 
 def inv_rope(io: torch.Tensor, q_pos: torch.Tensor, rope_dims: int, rope_cs: torch.Tensor, stream=None) -> None:

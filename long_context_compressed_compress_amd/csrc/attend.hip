@@ -64,6 +64,10 @@ constexpr int kTile = 64;                      // keys per tile
 constexpr int kD = 512;                        // head dim of the MFMA path
 constexpr int kRowStride = kD * 2 + 16;        // LDS bytes per key row (bf16 + 16 B pad)
 constexpr int kPStride = 64 + 8;               // bf16 elements per P row (16 B pad)
+constexpr int kMaxKeys = kMaxK + 1024;         // top-k entries + largest window
+
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 // Position, inside a 32-key PV k-step, of key kk in the A/B operand order: lane group g holds
 // keys 2g, 2g+1, 2g+8, 2g+9, 2g+16, 2g+17, 2g+24, 2g+25 as its elements 0..7.
@@ -74,15 +78,52 @@ __device__ __forceinline__ int perm_pos(int kk) {
 }
 __device__ __forceinline__ int perm_key(int g, int j) { return 2 * g + (j & 1) + 8 * (j >> 1); }
 
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element (i % 4) of the 64-bit words
+// addressed by lanes i/4 + 4j (j = 0..3) of its group, as its elements j.
+__device__ __forceinline__ uint2 lds_tr16(const char* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// Reductions over the 16 lanes of a DPP row (lanes 16r .. 16r+15): quad swaps, half-row and row mirrors.
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)));
+  return v;
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
+  return v;
+}
+// Value of the lane whose index differs in bit 0 (quad_perm [1,0,3,2]).
+__device__ __forceinline__ float pair_swap(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+
+template <bool FP8>
+struct TileRegs;
+template <>
+struct TileRegs<false> { uint4 v[16]; };  // 64 rows x 1 KiB / 256 threads
+template <>
+struct TileRegs<true> { uint4 v[8]; };    // 64 rows x 512 B / 256 threads
+
 template <bool FP8>
 __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a) {
+  constexpr int kPassKeys = kMaxKeys;           // keys whose rows are resolved per pass
+  constexpr int kPerThread = kPassKeys / 256;
   __shared__ __attribute__((aligned(16))) char k_lds[kTile * kRowStride];
   __shared__ __attribute__((aligned(16))) uint16_t p_hi[16 * kPStride];
   __shared__ __attribute__((aligned(16))) uint16_t p_lo[16 * kPStride];
+  __shared__ int32_t key_row[kPassKeys];   // page row of every key of the pass, -1 = masked
+  __shared__ uint8_t key_kind[kPassKeys];  // 0 compressed entry, 1 window row
   __shared__ float k_scale[kTile];
-  __shared__ int64_t k_row[kTile];
-  __shared__ int k_kind[kTile];
-  __shared__ float red[4][16];
+  __shared__ float red_max[4][16];
+  __shared__ float red_sum[4][16];
 
   const int HG = a.n_heads / 16;
   const int L = blockIdx.x;
@@ -102,10 +143,10 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a) {
   const int64_t n_elig = attend_elig(a, q);
   const int64_t n_c = a.topk ? a.k : n_elig;
   const int64_t lo = (a.swa_window > 0) ? max<int64_t>(0, p - a.swa_window + 1) : p + 1;
-  const int64_t n_swa = (a.swa_window > 0) ? p - lo + 1 : 0;
+  const int64_t n_swa = (a.swa_window > 0) ? max<int64_t>(0, p - lo + 1) : 0;
   const int64_t n_keys = n_c + n_swa;
+  // rows are kept as int32 in LDS; larger pools are rejected at the host (attend_supported)
 
-  // Q fragments: lane holds Q[head hg*16 + col][ks*32 + kg*8 .. +8], ks = 0..15
   bf16x8 qa[16];
   const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + (int64_t(q) * a.n_heads + hg * 16 + col) * kD;
 #pragma unroll
@@ -118,166 +159,219 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) { m_run[i] = -INFINITY; l_run[i] = 0.f; }
   const float scale = a.scale;
+  // descriptor fields as locals: selecting between struct fields per lane would turn into vector loads
+  // from the kernel-argument block, each followed by a full wait
+  const int32_t* bt_c = a.cache.block_table + int64_t(seq) * a.cache.bt_stride;
+  const int32_t* bt_w = a.swa.block_table + int64_t(seq) * a.swa.bt_stride;
+  const int bts_c = a.cache.bt_stride, bts_w = a.swa.bt_stride;
+  const int nph_c = a.cache.n_phys, nph_w = a.swa.n_phys;
+  const bool seq_c = seq >= 0 && seq < a.cache.batch;
+  const bool seq_w = seq >= 0 && seq < a.swa.batch;
+  const int per_block = kBlock / a.cache.ratio;
+  const int32_t* topk_q = a.topk ? a.topk + int64_t(q) * a.k : nullptr;
+  const int32_t* idx_src = topk_q ? topk_q : a.q_pos;  // any readable int32 when there is no top-k list
+  // The window pool is addressed as an integer offset from the cache pool so that choosing a pool per lane
+  // is a register select (a per-lane choice between two pointers otherwise becomes an indexed stack load).
+  const char* pages_c = static_cast<const char*>(a.cache.pages);
+  const int64_t pages_dw = int64_t(reinterpret_cast<uintptr_t>(a.swa.kv_pages)) - int64_t(reinterpret_cast<uintptr_t>(pages_c));
+  const float* scales_c = a.cache.scales;
+  const int64_t scales_dw = FP8 ? (int64_t(reinterpret_cast<uintptr_t>(a.swa.scales)) - int64_t(reinterpret_cast<uintptr_t>(scales_c))) : 0;
 
-  for (int64_t t0 = 0; t0 < n_keys; t0 += kTile) {
-    // ---- gather the tile into LDS
-    if (tid < kTile) {
-      const int64_t t = t0 + tid;
-      KeyRef r = (t < n_keys) ? key_ref(a, q, seq, t, n_c, n_elig, lo) : KeyRef{-1, 0};
-      k_row[tid] = r.row;
-      k_kind[tid] = r.kind;
-      float sc = 1.f;
-      if (FP8 && r.row >= 0) sc = r.kind == 0 ? a.cache.scales[r.row] : a.swa.scales[r.row];
-      k_scale[tid] = sc;
-    }
-    __syncthreads();
-    if (!FP8) {
-      // 64 rows x 64 chunks of 16 B; each wave copies whole rows
-#pragma unroll 4
-      for (int c = tid; c < kTile * 64; c += 256) {
-        const int r = c >> 6, cc = c & 63;
-        const int64_t row = k_row[r];
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (row >= 0) {
-          const uint16_t* base = reinterpret_cast<const uint16_t*>(k_kind[r] == 0 ? a.cache.pages : a.swa.kv_pages);
-          v = reinterpret_cast<const uint4*>(base + row * kD)[cc];
-        }
-        *reinterpret_cast<uint4*>(k_lds + r * kRowStride + cc * 16) = v;
-      }
-    } else {
-      // 64 rows x 32 chunks of 16 codes -> 32 bf16 each
-#pragma unroll 2
-      for (int c = tid; c < kTile * 32; c += 256) {
-        const int r = c >> 5, cc = c & 31;
-        const int64_t row = k_row[r];
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (row >= 0) {
-          const uint8_t* base = reinterpret_cast<const uint8_t*>(k_kind[r] == 0 ? a.cache.pages : a.swa.kv_pages);
-          v = reinterpret_cast<const uint4*>(base + row * kD)[cc];
-        }
-        uint32_t w[8];
-        const uint32_t src[4] = {v.x, v.y, v.z, v.w};
+  for (int64_t pass0 = 0; pass0 < n_keys; pass0 += kPassKeys) {
+    const int n_pass = int(min<int64_t>(kPassKeys, n_keys - pass0));
+    // ---- resolve the page rows of this pass: entry ids first, then block-table lookups. Every load is
+    // unconditional (indices clamped into range) so that a thread's loads are all in flight together.
+    {
+      int32_t ent[kPerThread];  // entry ids and window positions are below 2^31
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          uint32_t b0 = 0, b1 = 0;
-          const float f0 = e4m3_to_f32(src[h] & 0xFF), f1 = e4m3_to_f32((src[h] >> 8) & 0xFF);
-          const float f2 = e4m3_to_f32((src[h] >> 16) & 0xFF), f3 = e4m3_to_f32(src[h] >> 24);
-          b0 = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
-          b1 = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xFFFF0000u);
-          w[2 * h] = b0;
-          w[2 * h + 1] = b1;
+      for (int j = 0; j < kPerThread; ++j) {
+        const int64_t t = pass0 + tid + 256 * j;
+        const int32_t v = idx_src[t < n_c ? t : 0];  // unconditional load
+        int64_t e = topk_q ? int64_t(v) : t;
+        if (t >= n_c) e = (t < n_keys) ? lo + (t - n_c) : -1;
+        ent[j] = int32_t(e);
+      }
+      int32_t phys[kPerThread];
+#pragma unroll
+      for (int j = 0; j < kPerThread; ++j) {
+        const int64_t t = pass0 + tid + 256 * j;
+        const bool is_c = t < n_c;
+        const int64_t blk = ent[j] < 0 ? 0 : ent[j] / (is_c ? per_block : kBlock);
+        const int32_t* bt = is_c ? bt_c : bt_w;
+        const int bts = is_c ? bts_c : bts_w;
+        phys[j] = bt[blk < bts ? blk : bts - 1];
+      }
+#pragma unroll
+      for (int j = 0; j < kPerThread; ++j) {
+        const int local = tid + 256 * j;
+        const int64_t t = pass0 + local;
+        const bool is_c = t < n_c;
+        const int64_t e = ent[j];
+        const int per = is_c ? per_block : kBlock;
+        const int64_t blk = e < 0 ? 0 : e / per;
+        bool ok = e >= 0 && t < n_keys && blk < (is_c ? bts_c : bts_w) && phys[j] >= 0 &&
+                  phys[j] < (is_c ? nph_c : nph_w) && (is_c ? (seq_c && e < n_elig) : seq_w);
+        const int64_t row = ok ? int64_t(phys[j]) * per + (e - blk * per) : -1;
+        if (local < kPassKeys) {
+          key_row[local] = int32_t(row);
+          key_kind[local] = uint8_t(is_c ? 0 : 1);
         }
-        uint4* dst = reinterpret_cast<uint4*>(k_lds + r * kRowStride + cc * 32);
-        dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-        dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
       }
     }
     __syncthreads();
 
-    // ---- S = Q K^T for this wave's 16 keys
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-    {
-      const char* krow = k_lds + (wave * 16 + col) * kRowStride + kg * 16;
+    // Global loads of one tile into registers: thread tid covers rows (tid>>6) + 4i, 16-byte chunk (tid & 63)
+    // (bf16) or rows (tid>>5) + 8i, chunk (tid & 31) (fp8). Masked rows read row 0 and are zeroed at stash.
+    auto issue = [=](int t0, TileRegs<FP8>& R, uint32_t& valid_mask, float& my_scale) {
+      valid_mask = 0u;
+      constexpr int N = FP8 ? 8 : 16;
 #pragma unroll
-      for (int ks = 0; ks < 16; ++ks) {
-        const bf16x8 kb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + ks * 64));
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb, s, 0, 0, 0);
+      for (int i = 0; i < N; ++i) {
+        const int r = FP8 ? (tid >> 5) + 8 * i : (tid >> 6) + 4 * i;
+        const int cc = FP8 ? (tid & 31) : (tid & 63);
+        const int t = t0 + r;
+        const int64_t row = t < n_pass ? key_row[t] : -1;
+        const int kind = t < n_pass ? key_kind[t] : 0;
+        const bool ok = row >= 0;
+        valid_mask |= uint32_t(ok) << i;
+        const int64_t off = (kind == 0 ? 0 : pages_dw) + (ok ? row : 0) * (FP8 ? kD : 2 * kD) + cc * 16;
+        R.v[i] = *reinterpret_cast<const uint4*>(pages_c + off);
       }
-    }
-    const int key_local = wave * 16 + col;
-    const bool kvalid = k_row[key_local] >= 0;
-    const float ksc = k_scale[key_local];
-    float lg[4];
+      my_scale = -1.f;  // a negative scale marks a masked key
+      if (tid < kTile) {
+        const int t = t0 + tid;
+        const int64_t row = t < n_pass ? key_row[t] : -1;
+        if (row >= 0) {
+          my_scale = 1.f;
+          if (FP8) my_scale = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(scales_c) +
+                                                               (key_kind[t] == 0 ? 0 : scales_dw) + row * 4);
+        }
+      }
+    };
+    auto stash = [=](const TileRegs<FP8>& R, uint32_t valid_mask, float my_scale) {
+      constexpr int N = FP8 ? 8 : 16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lg[i] = kvalid ? s[i] * (scale * ksc) : -INFINITY;
-    // tile max per head (lane holds heads kg*4+i for key col)
-    float mx[4];
+      for (int i = 0; i < N; ++i) {
+        const bool ok = (valid_mask >> i) & 1u;
+        if (!FP8) {
+          const int r = (tid >> 6) + 4 * i, cc = tid & 63;
+          *reinterpret_cast<uint4*>(k_lds + r * kRowStride + cc * 16) = ok ? R.v[i] : make_uint4(0, 0, 0, 0);
+        } else {
+          const int r = (tid >> 5) + 8 * i, cc = tid & 31;
+          const uint4 v = ok ? R.v[i] : make_uint4(0, 0, 0, 0);
+          const uint32_t src[4] = {v.x, v.y, v.z, v.w};
+          uint32_t w[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v = lg[i];
+          for (int h = 0; h < 4; ++h) {
+            const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(int(src[h]), false);
+            const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(int(src[h]), true);
+            w[2 * h] = __builtin_amdgcn_perm(__float_as_uint(f01[1]), __float_as_uint(f01[0]), 0x07060302u);
+            w[2 * h + 1] = __builtin_amdgcn_perm(__float_as_uint(f23[1]), __float_as_uint(f23[0]), 0x07060302u);
+          }
+          uint4* dst = reinterpret_cast<uint4*>(k_lds + r * kRowStride + cc * 32);
+          dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+          dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        }
+      }
+      if (tid < kTile) k_scale[tid] = my_scale;
+    };
+
+    TileRegs<FP8> R;
+    uint32_t vmask = 0;
+    float my_scale = -1.f;
+    issue(0, R, vmask, my_scale);
+    for (int t0 = 0; t0 < n_pass; t0 += kTile) {
+      lds_barrier();  // previous tile's readers of k_lds / p / red are done
+      stash(R, vmask, my_scale);
+      lds_barrier();
+      if (t0 + kTile < n_pass) issue(t0 + kTile, R, vmask, my_scale);  // next tile's loads overlap this tile's math
+
+      // ---- S = Q K^T for this wave's 16 keys (two independent accumulation chains)
+      f32x4 s = {0.f, 0.f, 0.f, 0.f}, s2 = {0.f, 0.f, 0.f, 0.f};
+      {
+        const char* krow = k_lds + (wave * 16 + col) * kRowStride + kg * 16;
 #pragma unroll
-      for (int off = 1; off < 16; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
-      mx[i] = v;
-    }
-    if (col == 0)
+        for (int ks = 0; ks < 16; ks += 2) {
+          const bf16x8 kb0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + ks * 64));
+          const bf16x8 kb1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + ks * 64 + 64));
+          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb0, s, 0, 0, 0);
+          s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks + 1], kb1, s2, 0, 0, 0);
+        }
+      }
+      const int key_local = wave * 16 + col;
+      const float ksc = k_scale[key_local];
+      const bool kvalid = ksc >= 0.f;
+      float lg[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[wave][kg * 4 + i] = mx[i];
-    __syncthreads();
-    float corr[4], pv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = kg * 4 + i;
-      const float tmax = fmaxf(fmaxf(red[0][h], red[1][h]), fmaxf(red[2][h], red[3][h]));
-      const float mnew = fmaxf(m_run[i], tmax);
-      corr[i] = (m_run[i] == -INFINITY) ? 0.f : __expf(m_run[i] - mnew);
-      pv[i] = (lg[i] == -INFINITY) ? 0.f : __expf(lg[i] - mnew);
-      m_run[i] = mnew;
-    }
-    __syncthreads();  // everyone has read red[] before it is reused for sums
-    float sm[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v = pv[i];
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off);
-      sm[i] = v;
-    }
-    if (col == 0)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) red[wave][kg * 4 + i] = sm[i];
-    // probabilities (times the fp8 row scale) to LDS as bf16 hi + lo, in the PV operand order
-    {
-      const int ks2 = key_local >> 5;
-      const int pos = ks2 * 32 + perm_pos(key_local & 31);
+      for (int i = 0; i < 4; ++i) lg[i] = kvalid ? (s[i] + s2[i]) * (scale * ksc) : -INFINITY;
+      // tile max per head (lane holds heads kg*4+i of key col; the 16 keys of a head sit in one DPP row)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float w = pv[i] * ksc;
-        const uint16_t hi = f32_to_bf16_rne(w);
-        const uint16_t lo16 = f32_to_bf16_rne(w - bf16_to_f32(hi));
-        p_hi[(kg * 4 + i) * kPStride + pos] = hi;
-        p_lo[(kg * 4 + i) * kPStride + pos] = lo16;
+        const float mx = row_max16(lg[i]);
+        if (col == 0) red_max[wave][kg * 4 + i] = mx;
       }
-    }
-    __syncthreads();
+      lds_barrier();
+      float corr[4], pv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = kg * 4 + i;
-      l_run[i] = l_run[i] * corr[i] + (red[0][h] + red[1][h] + red[2][h] + red[3][h]);
-    }
-    // ---- O = O * corr + P K over this wave's 128 dims
+      for (int i = 0; i < 4; ++i) {
+        const int h = kg * 4 + i;
+        const float tmax = fmaxf(fmaxf(red_max[0][h], red_max[1][h]), fmaxf(red_max[2][h], red_max[3][h]));
+        const float mnew = fmaxf(m_run[i], tmax);
+        corr[i] = (m_run[i] == -INFINITY) ? 0.f : __expf(m_run[i] - mnew);
+        pv[i] = (lg[i] == -INFINITY) ? 0.f : __expf(lg[i] - mnew);
+        m_run[i] = mnew;
+        const float sm = row_sum16(pv[i]);
+        if (col == 0) red_sum[wave][h] = sm;
+      }
+      {
+        const int ks2 = key_local >> 5;
+        const int pos = ks2 * 32 + perm_pos(key_local & 31);
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[nt][i] *= corr[i];
-#pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) {
-      const bf16x8 ah = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p_hi + col * kPStride + ks2 * 32 + kg * 8));
-      const bf16x8 al = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p_lo + col * kPStride + ks2 * 32 + kg * 8));
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        const int d = wave * 128 + nt * 16 + col;
-        uint32_t w[4];
-#pragma unroll
-        for (int j2 = 0; j2 < 4; ++j2) {
-          const int r0 = ks2 * 32 + perm_key(kg, 2 * j2);
-          const int r1 = ks2 * 32 + perm_key(kg, 2 * j2 + 1);
-          const uint32_t e0 = *reinterpret_cast<const uint16_t*>(k_lds + r0 * kRowStride + d * 2);
-          const uint32_t e1 = *reinterpret_cast<const uint16_t*>(k_lds + r1 * kRowStride + d * 2);
-          w[j2] = e0 | (e1 << 16);
+        for (int i = 0; i < 4; ++i) {
+          const float w = kvalid ? pv[i] * ksc : 0.f;  // fp8: the row scale multiplies the value side too
+          const uint16_t hi = f32_to_bf16_rne(w);
+          const uint16_t lo16 = f32_to_bf16_rne(w - bf16_to_f32(hi));
+          p_hi[(kg * 4 + i) * kPStride + pos] = hi;
+          p_lo[(kg * 4 + i) * kPStride + pos] = lo16;
         }
-        const bf16x8 kb = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
-        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, kb, o[nt], 0, 0, 0);
-        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, kb, o[nt], 0, 0, 0);
+      }
+      lds_barrier();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = kg * 4 + i;
+        l_run[i] = l_run[i] * corr[i] + (red_sum[0][h] + red_sum[1][h] + red_sum[2][h] + red_sum[3][h]);
+      }
+      // ---- O = O * corr + P K over this wave's 128 dims (B operand by transposing LDS reads)
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[nt][i] *= corr[i];
+      const int s_lane = lane & 15;
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        const bf16x8 ah = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p_hi + col * kPStride + ks2 * 32 + kg * 8));
+        const bf16x8 al = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p_lo + col * kPStride + ks2 * 32 + kg * 8));
+        const int r0 = ks2 * 32 + perm_key(kg, s_lane >> 2);
+        const int r1 = ks2 * 32 + perm_key(kg, 4 + (s_lane >> 2));
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          const int dcol = wave * 128 + nt * 16 + 4 * (s_lane & 3);
+          const uint2 e0 = lds_tr16(k_lds + r0 * kRowStride + dcol * 2);
+          const uint2 e1 = lds_tr16(k_lds + r1 * kRowStride + dcol * 2);
+          const bf16x8 kb = __builtin_bit_cast(bf16x8, make_uint4(e0.x, e0.y, e1.x, e1.y));
+          o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, kb, o[nt], 0, 0, 0);
+          o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, kb, o[nt], 0, 0, 0);
+        }
       }
     }
-    __syncthreads();  // before the next tile overwrites k_lds / p / red
+    __syncthreads();  // the next pass rewrites the row table
   }
 
   // ---- epilogue: normalise, optional inverse RoPE, store
-  const int R = a.cache.rope_dims;
-  const int base = kD - R;
-  const bool rot = a.fuse_inv_rope && R > 0 && p >= 0 && p < a.rope_rows;
-  const float* cs = rot ? a.rope_cs + p * int64_t(R) : a.rope_cs;
+  const int R_ = a.cache.rope_dims;
+  const int base = kD - R_;
+  const bool rot = a.fuse_inv_rope && R_ > 0 && p >= 0 && p < a.rope_rows;
+  const float* cs = rot ? a.rope_cs + p * int64_t(R_) : a.rope_cs;
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) {
     const int d = wave * 128 + nt * 16 + col;
@@ -285,7 +379,7 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a) {
     for (int i = 0; i < 4; ++i) {
       const float inv_l = (l_run[i] > 0.f) ? 1.f / l_run[i] : 0.f;
       const float v = o[nt][i] * inv_l;
-      const float partner = __shfl_xor(v, 1);
+      const float partner = pair_swap(v);
       float r = v;
       if (rot && d >= base) {
         const int j = (d - base) >> 1;
@@ -303,6 +397,393 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a) {
       a.out_lse[int64_t(q) * a.n_heads + h] = (l_run[i] > 0.f) ? m_run[i] + logf(l_run[i]) : -INFINITY;
     }
   }
+}
+
+// ------------------------------------------------------------------ split MFMA path (64 heads per block)
+// One 512-thread workgroup per (query, 64-head chunk, key split): every key row is gathered once per query
+// chunk and feeds all 64 heads. Wave w serves head group hg = w/2 (16 heads) and half sw = w%2: in S it owns
+// keys 32sw..32sw+31 of the 64-key tile, in PV dims 256sw..256sw+255. Splits of one query write partial
+// (max, sum, unnormalised output) to the workspace and attend_combine merges them; with one split the block
+// writes the final output itself.
+struct SplitPlan {
+  int n_split;      // key splits per query
+  int split_keys;   // keys per split (multiple of the tile)
+};
+
+__host__ __device__ inline SplitPlan split_plan(int n_q, int n_hchunk, int64_t max_keys) {
+  SplitPlan sp;
+  const int64_t tiles = (max_keys + kTile - 1) / kTile;
+  const int64_t want = (512 + int64_t(n_q) * n_hchunk - 1) / (int64_t(n_q) * n_hchunk);  // about two blocks per CU
+  int64_t ns = want < 1 ? 1 : want;
+  const int64_t max_split = (tiles + 1) / 2;  // at least two tiles per split
+  if (ns > max_split) ns = max_split < 1 ? 1 : max_split;
+  const int64_t tiles_per = (tiles + ns - 1) / ns;
+  sp.split_keys = int(tiles_per * kTile);
+  sp.n_split = int((tiles + tiles_per - 1) / tiles_per);
+  if (sp.n_split < 1) sp.n_split = 1;
+  return sp;
+}
+
+template <bool FP8>
+struct TileRegs8;
+template <>
+struct TileRegs8<false> { uint4 v[8]; };  // 64 rows x 1 KiB / 512 threads
+template <>
+struct TileRegs8<true> { uint4 v[4]; };   // 64 rows x 512 B / 512 threads
+
+template <bool FP8>
+__global__ void __launch_bounds__(512) attend_split_kernel(AttendArgs a, SplitPlan sp, float* part_o, float* part_ml) {
+  __shared__ __attribute__((aligned(16))) char k_lds[kTile * kRowStride];
+  __shared__ __attribute__((aligned(16))) uint16_t p_hi[4][16 * kPStride];
+  __shared__ __attribute__((aligned(16))) uint16_t p_lo[4][16 * kPStride];
+  __shared__ int32_t key_row[kMaxKeys];
+  __shared__ uint8_t key_kind[kMaxKeys];
+  __shared__ float k_scale[kTile];
+  __shared__ float red_max[4][2][16];
+  __shared__ float red_sum[4][2][16];
+
+  const int n_hchunk = a.n_heads / 64;
+  const int split = blockIdx.x % sp.n_split;
+  const int hc = (blockIdx.x / sp.n_split) % n_hchunk;
+  const int q = blockIdx.x / (sp.n_split * n_hchunk);
+  if (q >= a.n_q) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int hg = wave >> 1;
+  const int sw = wave & 1;
+  const int col = lane & 15;
+  const int kg = lane >> 4;
+  const int seq = a.q_seq[q];
+  const int64_t p = a.q_pos[q];
+  const int64_t n_elig = attend_elig(a, q);
+  const int64_t n_c = a.topk ? a.k : n_elig;
+  const int64_t lo = (a.swa_window > 0) ? max<int64_t>(0, p - a.swa_window + 1) : p + 1;
+  const int64_t n_swa = (a.swa_window > 0) ? max<int64_t>(0, p - lo + 1) : 0;
+  const int64_t n_keys = n_c + n_swa;
+  const int64_t k_begin = int64_t(split) * sp.split_keys;
+  const int64_t k_end = min<int64_t>(n_keys, k_begin + sp.split_keys);
+
+  const int32_t* bt_c = a.cache.block_table + int64_t(seq) * a.cache.bt_stride;
+  const int32_t* bt_w = a.swa.block_table + int64_t(seq) * a.swa.bt_stride;
+  const int bts_c = a.cache.bt_stride, bts_w = a.swa.bt_stride;
+  const int nph_c = a.cache.n_phys, nph_w = a.swa.n_phys;
+  const bool seq_c = seq >= 0 && seq < a.cache.batch;
+  const bool seq_w = seq >= 0 && seq < a.swa.batch;
+  const int per_block = kBlock / a.cache.ratio;
+  const int32_t* topk_q = a.topk ? a.topk + int64_t(q) * a.k : nullptr;
+  const int32_t* idx_src = topk_q ? topk_q : a.q_pos;
+  const char* pages_c = static_cast<const char*>(a.cache.pages);
+  const int64_t pages_dw = int64_t(reinterpret_cast<uintptr_t>(a.swa.kv_pages)) - int64_t(reinterpret_cast<uintptr_t>(pages_c));
+  const float* scales_c = a.cache.scales;
+  const int64_t scales_dw = FP8 ? (int64_t(reinterpret_cast<uintptr_t>(a.swa.scales)) - int64_t(reinterpret_cast<uintptr_t>(scales_c))) : 0;
+
+  bf16x8 qa[16];
+  const int head0 = hc * 64 + hg * 16;
+  const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + (int64_t(q) * a.n_heads + head0 + col) * kD;
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) qa[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + ks * 32 + kg * 8));
+
+  f32x4 o[16];
+#pragma unroll
+  for (int nt = 0; nt < 16; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[4], l_run[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { m_run[i] = -INFINITY; l_run[i] = 0.f; }
+  const float scale = a.scale;
+
+  for (int64_t pass0 = k_begin; pass0 < k_end; pass0 += kMaxKeys) {
+    const int n_pass = int(min<int64_t>(kMaxKeys, k_end - pass0));
+    // ---- resolve page rows of this pass (all loads unconditional, indices clamped)
+    {
+      constexpr int PER = (kMaxKeys + 511) / 512;
+      int32_t ent[PER];
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int64_t t = pass0 + tid + 512 * j;
+        const int32_t v = idx_src[t < n_c ? t : 0];
+        int64_t e = topk_q ? int64_t(v) : t;
+        if (t >= n_c) e = (t < n_keys) ? lo + (t - n_c) : -1;
+        ent[j] = int32_t(e);
+      }
+      int32_t phys[PER];
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int64_t t = pass0 + tid + 512 * j;
+        const bool is_c = t < n_c;
+        const int64_t blk = ent[j] < 0 ? 0 : ent[j] / (is_c ? per_block : kBlock);
+        const int32_t* bt = is_c ? bt_c : bt_w;
+        const int bts = is_c ? bts_c : bts_w;
+        phys[j] = bt[blk < bts ? blk : bts - 1];
+      }
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int local = tid + 512 * j;
+        const int64_t t = pass0 + local;
+        const bool is_c = t < n_c;
+        const int64_t e = ent[j];
+        const int per = is_c ? per_block : kBlock;
+        const int64_t blk = e < 0 ? 0 : e / per;
+        const bool ok = e >= 0 && t < n_keys && blk < (is_c ? bts_c : bts_w) && phys[j] >= 0 &&
+                        phys[j] < (is_c ? nph_c : nph_w) && (is_c ? (seq_c && e < n_elig) : seq_w);
+        if (local < kMaxKeys) {
+          key_row[local] = int32_t(ok ? int64_t(phys[j]) * per + (e - blk * per) : -1);
+          key_kind[local] = uint8_t(is_c ? 0 : 1);
+        }
+      }
+    }
+    __syncthreads();
+
+    auto issue = [=](int t0, TileRegs8<FP8>& R, uint32_t& valid_mask, float& my_scale) {
+      valid_mask = 0u;
+      constexpr int N = FP8 ? 4 : 8;
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int r = FP8 ? (tid >> 5) + 16 * i : (tid >> 6) + 8 * i;
+        const int cc = FP8 ? (tid & 31) : (tid & 63);
+        const int t = t0 + r;
+        const int64_t row = t < n_pass ? key_row[t] : -1;
+        const int kind = t < n_pass ? key_kind[t] : 0;
+        const bool ok = row >= 0;
+        valid_mask |= uint32_t(ok) << i;
+        const int64_t off = (kind == 0 ? 0 : pages_dw) + (ok ? row : 0) * (FP8 ? kD : 2 * kD) + cc * 16;
+        R.v[i] = *reinterpret_cast<const uint4*>(pages_c + off);
+      }
+      my_scale = -1.f;  // a negative scale marks a masked key
+      if (tid < kTile) {
+        const int t = t0 + tid;
+        const int64_t row = t < n_pass ? key_row[t] : -1;
+        if (row >= 0) {
+          my_scale = 1.f;
+          if (FP8)
+            my_scale = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(scales_c) +
+                                                        (key_kind[t] == 0 ? 0 : scales_dw) + row * 4);
+        }
+      }
+    };
+    auto stash = [=](const TileRegs8<FP8>& R, uint32_t valid_mask, float my_scale) {
+      constexpr int N = FP8 ? 4 : 8;
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const bool ok = (valid_mask >> i) & 1u;
+        if (!FP8) {
+          const int r = (tid >> 6) + 8 * i, cc = tid & 63;
+          *reinterpret_cast<uint4*>(k_lds + r * kRowStride + cc * 16) = ok ? R.v[i] : make_uint4(0, 0, 0, 0);
+        } else {
+          const int r = (tid >> 5) + 16 * i, cc = tid & 31;
+          const uint4 v = ok ? R.v[i] : make_uint4(0, 0, 0, 0);
+          const uint32_t src[4] = {v.x, v.y, v.z, v.w};
+          uint32_t w[8];
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(int(src[h]), false);
+            const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(int(src[h]), true);
+            w[2 * h] = __builtin_amdgcn_perm(__float_as_uint(f01[1]), __float_as_uint(f01[0]), 0x07060302u);
+            w[2 * h + 1] = __builtin_amdgcn_perm(__float_as_uint(f23[1]), __float_as_uint(f23[0]), 0x07060302u);
+          }
+          uint4* dst = reinterpret_cast<uint4*>(k_lds + r * kRowStride + cc * 32);
+          dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+          dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        }
+      }
+      if (tid < kTile) k_scale[tid] = my_scale;
+    };
+
+    TileRegs8<FP8> R;
+    uint32_t vmask = 0;
+    float my_scale = -1.f;
+    issue(0, R, vmask, my_scale);
+    for (int t0 = 0; t0 < n_pass; t0 += kTile) {
+      lds_barrier();
+      stash(R, vmask, my_scale);
+      lds_barrier();
+      if (t0 + kTile < n_pass) issue(t0 + kTile, R, vmask, my_scale);
+
+      // ---- S for this wave's 32 keys (two 16-key column tiles) and its 16 heads
+      f32x4 s[2];
+#pragma unroll
+      for (int n16 = 0; n16 < 2; ++n16) {
+        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+        const char* krow = k_lds + (sw * 32 + n16 * 16 + col) * kRowStride + kg * 16;
+#pragma unroll
+        for (int ks = 0; ks < 16; ks += 2) {
+          const bf16x8 kb0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + ks * 64));
+          const bf16x8 kb1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(krow + ks * 64 + 64));
+          a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb0, a0, 0, 0, 0);
+          a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks + 1], kb1, a1, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[n16][i] = a0[i] + a1[i];
+      }
+      float ksc[2];
+      bool kval[2];
+      float lg[2][4];
+#pragma unroll
+      for (int n16 = 0; n16 < 2; ++n16) {
+        ksc[n16] = k_scale[sw * 32 + n16 * 16 + col];
+        kval[n16] = ksc[n16] >= 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lg[n16][i] = kval[n16] ? s[n16][i] * (scale * ksc[n16]) : -INFINITY;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float mx = row_max16(fmaxf(lg[0][i], lg[1][i]));
+        if (col == 0) red_max[hg][sw][kg * 4 + i] = mx;
+      }
+      lds_barrier();
+      float corr[4], pv[2][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = kg * 4 + i;
+        const float tmax = fmaxf(red_max[hg][0][h], red_max[hg][1][h]);
+        const float mnew = fmaxf(m_run[i], tmax);
+        corr[i] = (m_run[i] == -INFINITY) ? 0.f : __expf(m_run[i] - mnew);
+        pv[0][i] = (lg[0][i] == -INFINITY) ? 0.f : __expf(lg[0][i] - mnew);
+        pv[1][i] = (lg[1][i] == -INFINITY) ? 0.f : __expf(lg[1][i] - mnew);
+        m_run[i] = mnew;
+        const float sm = row_sum16(pv[0][i] + pv[1][i]);
+        if (col == 0) red_sum[hg][sw][h] = sm;
+      }
+#pragma unroll
+      for (int n16 = 0; n16 < 2; ++n16) {
+        const int key_local = sw * 32 + n16 * 16 + col;
+        const int pos = (key_local >> 5) * 32 + perm_pos(key_local & 31);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float w = kval[n16] ? pv[n16][i] * ksc[n16] : 0.f;
+          const uint16_t hi = f32_to_bf16_rne(w);
+          const uint16_t lo16 = f32_to_bf16_rne(w - bf16_to_f32(hi));
+          p_hi[hg][(kg * 4 + i) * kPStride + pos] = hi;
+          p_lo[hg][(kg * 4 + i) * kPStride + pos] = lo16;
+        }
+      }
+      lds_barrier();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = kg * 4 + i;
+        l_run[i] = l_run[i] * corr[i] + red_sum[hg][0][h] + red_sum[hg][1][h];
+      }
+      // ---- O (16 heads x this wave's 256 dims) = O * corr + P K
+#pragma unroll
+      for (int nt = 0; nt < 16; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[nt][i] *= corr[i];
+      const int s_lane = lane & 15;
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        const bf16x8 ah = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&p_hi[hg][col * kPStride + ks2 * 32 + kg * 8]));
+        const bf16x8 al = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&p_lo[hg][col * kPStride + ks2 * 32 + kg * 8]));
+        const int r0 = ks2 * 32 + perm_key(kg, s_lane >> 2);
+        const int r1 = ks2 * 32 + perm_key(kg, 4 + (s_lane >> 2));
+#pragma unroll
+        for (int nt = 0; nt < 16; ++nt) {
+          const int dcol = sw * 256 + nt * 16 + 4 * (s_lane & 3);
+          const uint2 e0 = lds_tr16(k_lds + r0 * kRowStride + dcol * 2);
+          const uint2 e1 = lds_tr16(k_lds + r1 * kRowStride + dcol * 2);
+          const bf16x8 kb = __builtin_bit_cast(bf16x8, make_uint4(e0.x, e0.y, e1.x, e1.y));
+          o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, kb, o[nt], 0, 0, 0);
+          o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, kb, o[nt], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();  // the next pass rewrites the row table
+  }
+
+  // ---- epilogue
+  if (sp.n_split == 1) {
+    const int R_ = a.cache.rope_dims;
+    const int base = kD - R_;
+    const bool rot = a.fuse_inv_rope && R_ > 0 && p >= 0 && p < a.rope_rows;
+    const float* cs = rot ? a.rope_cs + p * int64_t(R_) : a.rope_cs;
+#pragma unroll
+    for (int nt = 0; nt < 16; ++nt) {
+      const int d = sw * 256 + nt * 16 + col;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float inv_l = (l_run[i] > 0.f) ? 1.f / l_run[i] : 0.f;
+        const float v = o[nt][i] * inv_l;
+        const float partner = pair_swap(v);
+        float r = v;
+        if (rot && d >= base) {
+          const int j = (d - base) >> 1;
+          const float c = cs[2 * j], sn = cs[2 * j + 1];
+          r = (d & 1) ? (-partner * sn + v * c) : (v * c + partner * sn);
+        }
+        a.out[(int64_t(q) * a.n_heads + head0 + kg * 4 + i) * kD + d] = r;
+      }
+    }
+    if (a.out_lse && sw == 0 && col == 0)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        a.out_lse[int64_t(q) * a.n_heads + head0 + kg * 4 + i] = (l_run[i] > 0.f) ? m_run[i] + logf(l_run[i]) : -INFINITY;
+  } else {
+    // partial: unnormalised output relative to this split's running max, plus (max, sum)
+    const int64_t slot = int64_t(q) * sp.n_split + split;
+#pragma unroll
+    for (int nt = 0; nt < 16; ++nt) {
+      const int d = sw * 256 + nt * 16 + col;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        part_o[(slot * a.n_heads + head0 + kg * 4 + i) * kD + d] = o[nt][i];
+    }
+    if (sw == 0 && col == 0)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t h = slot * a.n_heads + head0 + kg * 4 + i;
+        part_ml[2 * h] = m_run[i];
+        part_ml[2 * h + 1] = l_run[i];
+      }
+  }
+}
+
+// Merge the key splits of each (query, head): o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s, then the
+// optional inverse RoPE. One 256-thread workgroup per (query, 4 heads); a thread owns 8 consecutive dims.
+__global__ void __launch_bounds__(256) attend_combine_kernel(AttendArgs a, SplitPlan sp, const float* part_o,
+                                                             const float* part_ml) {
+  const int hq = a.n_heads / 4;
+  const int q = blockIdx.x / hq;
+  const int h = (blockIdx.x % hq) * 4 + (threadIdx.x >> 6);
+  const int d0 = (threadIdx.x & 63) * 8;
+  if (q >= a.n_q) return;
+  float M = -INFINITY;
+  for (int s = 0; s < sp.n_split; ++s) M = fmaxf(M, part_ml[2 * ((int64_t(q) * sp.n_split + s) * a.n_heads + h)]);
+  float L = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < sp.n_split; ++s) {
+    const int64_t slot = (int64_t(q) * sp.n_split + s) * a.n_heads + h;
+    const float m = part_ml[2 * slot], l = part_ml[2 * slot + 1];
+    const float w = (m == -INFINITY) ? 0.f : __expf(m - M);
+    L += w * l;
+    const float4* src = reinterpret_cast<const float4*>(part_o + slot * kD + d0);
+    const float4 x0 = src[0], x1 = src[1];
+    acc[0] += w * x0.x; acc[1] += w * x0.y; acc[2] += w * x0.z; acc[3] += w * x0.w;
+    acc[4] += w * x1.x; acc[5] += w * x1.y; acc[6] += w * x1.z; acc[7] += w * x1.w;
+  }
+  const float inv = (L > 0.f) ? 1.f / L : 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] *= inv;
+  const int64_t p = a.q_pos[q];
+  const int R_ = a.cache.rope_dims;
+  const int base = kD - R_;
+  if (a.fuse_inv_rope && R_ > 0 && p >= 0 && p < a.rope_rows) {
+    const float* cs = a.rope_cs + p * int64_t(R_);
+#pragma unroll
+    for (int k = 0; k < 8; k += 2) {
+      const int d = d0 + k;
+      if (d >= base) {
+        const int j = (d - base) >> 1;
+        const float c = cs[2 * j], sn = cs[2 * j + 1];
+        const float u = acc[k], v = acc[k + 1];
+        acc[k] = u * c + v * sn;
+        acc[k + 1] = -u * sn + v * c;
+      }
+    }
+  }
+  float4* dst = reinterpret_cast<float4*>(a.out + (int64_t(q) * a.n_heads + h) * kD + d0);
+  dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  if (a.out_lse && d0 == 0) a.out_lse[int64_t(q) * a.n_heads + h] = (L > 0.f) ? M + logf(L) : -INFINITY;
 }
 
 // ------------------------------------------------------------------ VALU path
@@ -420,12 +901,46 @@ __global__ void __launch_bounds__(256) attend_valu_kernel(AttendArgs a) {
 }  // namespace
 
 bool attend_supported(const csa_cache_t& c, csa_dtype_t q_dtype, int n_heads) {
+  if (int64_t(c.n_phys) * (kBlock / c.ratio) > 0x7FFFFFFF) return false;  // page rows are 32-bit
   if (c.dtype == CSA_F32) return q_dtype == CSA_F32 && c.dim <= 512;
   return q_dtype == CSA_BF16 && c.dim <= 512 && n_heads >= 1;
 }
 
-hipError_t launch_attend(const AttendArgs& a, hipStream_t stream) {
+static bool use_split_path(const AttendArgs& a) {
+  return a.cache.dtype != CSA_F32 && a.cache.dim == kD && a.n_heads % 64 == 0;
+}
+
+static int64_t max_keys_of(const AttendArgs& a) {
+  return (a.topk ? int64_t(a.k) : a.max_elig) + a.swa_window;
+}
+
+size_t attend_workspace(int n_q, int n_heads, int dim, int64_t max_keys) {
+  if (n_q <= 0 || n_heads % 64 != 0 || dim != kD) return 0;
+  const SplitPlan sp = split_plan(n_q, n_heads / 64, max_keys);
+  if (sp.n_split <= 1) return 0;
+  const size_t slots = size_t(n_q) * sp.n_split * n_heads;
+  return slots * kD * 4 + slots * 8 + 256;
+}
+
+hipError_t launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (a.n_q == 0) return hipSuccess;
+  if (use_split_path(a)) {
+    const int n_hchunk = a.n_heads / 64;
+    SplitPlan sp = split_plan(a.n_q, n_hchunk, max_keys_of(a));
+    const size_t need = attend_workspace(a.n_q, a.n_heads, kD, max_keys_of(a));
+    if (sp.n_split > 1 && (ws == nullptr || ws_bytes < need)) return hipErrorInvalidValue;
+    float* part_o = static_cast<float*>(ws);
+    float* part_ml = part_o ? part_o + size_t(a.n_q) * sp.n_split * a.n_heads * kD : nullptr;
+    const dim3 grid(unsigned(int64_t(a.n_q) * n_hchunk * sp.n_split));
+    if (a.cache.dtype == CSA_FP8_E4M3)
+      hipLaunchKernelGGL((attend_split_kernel<true>), grid, dim3(512), 0, stream, a, sp, part_o, part_ml);
+    else
+      hipLaunchKernelGGL((attend_split_kernel<false>), grid, dim3(512), 0, stream, a, sp, part_o, part_ml);
+    if (sp.n_split > 1)
+      hipLaunchKernelGGL(attend_combine_kernel, dim3(unsigned(int64_t(a.n_q) * (a.n_heads / 4))), dim3(256), 0, stream,
+                         a, sp, part_o, part_ml);
+    return hipGetLastError();
+  }
   const bool mfma = a.cache.dtype != CSA_F32 && a.cache.dim == kD && a.n_heads % 16 == 0;
   if (mfma) {
     const int HG = a.n_heads / 16;

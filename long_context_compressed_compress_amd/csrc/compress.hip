@@ -125,23 +125,26 @@ __global__ void __launch_bounds__(256) compress_insert_kernel(CompressArgs a) {
 #pragma unroll
   for (int k = 0; k < CH; ++k) { m[k] = -INFINITY; s[k] = 0.f; acc[k] = 0.f; }
 
-  for (int t = grp; t < WINDOW; t += G) {
+  constexpr int ROWS = (WINDOW + G - 1) / G;  // window rows per lane group
+#pragma unroll
+  for (int tt = 0; tt < ROWS; ++tt) {
+    const int t = grp + tt * G;
+    if (t >= WINDOW) break;
     const int64_t pos = first + t;
     const int role = t / RATIO;
+    // rows of new positions come from the inputs, older ones from the state pages
+    const bool from_new = pos >= start;
+    const int64_t r = from_new ? -1 : (st_bt ? raw_row(st_bt, a.state.bt_stride, a.state.n_phys, pos) : -1);
+    const bool have = from_new || r >= 0;
+    const TIn* xs = from_new ? kv_new + (cu_b + (pos - start)) * D : st_kv + (r >= 0 ? r : 0) * D;
+    const TIn* ls = from_new ? lg_new + ((cu_b + (pos - start)) * ROLES + role) * D
+                             : st_lg + ((r >= 0 ? r : 0) * ROLES + role) * D;
     float x[CH], l[CH];
-    if (pos >= start) {
-      const int64_t row = cu_b + (pos - start);
-      load_vec<TIn, CH>(kv_new + row * D + ch0, x);
-      load_vec<TIn, CH>(lg_new + (row * ROLES + role) * D + ch0, l);
-    } else {
-      const int64_t r = st_bt ? raw_row(st_bt, a.state.bt_stride, a.state.n_phys, pos) : -1;
-      if (r >= 0) {
-        load_vec<TIn, CH>(st_kv + r * D + ch0, x);
-        load_vec<TIn, CH>(st_lg + (r * ROLES + role) * D + ch0, l);
-      } else {
-        zero_vec(x);
-        zero_vec(l);
-      }
+    load_vec<TIn, CH>(xs + ch0, x);
+    load_vec<TIn, CH>(ls + ch0, l);
+    if (!have) {
+      zero_vec(x);
+      zero_vec(l);
     }
 #pragma unroll
     for (int k = 0; k < CH; ++k) {

@@ -185,8 +185,8 @@ csa_status_t csa_index_topk(const csa_cache_t* idx_cache, int32_t n_q, const int
 }
 
 size_t csa_attend_workspace(int32_t n_q, int32_t n_heads, int32_t dim, int32_t max_keys) {
-  (void)n_q; (void)n_heads; (void)dim; (void)max_keys;
-  return 0;
+  if (n_q < 0 || n_heads < 1 || max_keys < 0) return 0;
+  return csa::attend_workspace(n_q, n_heads, dim, max_keys);
 }
 
 csa_status_t csa_attend(const csa_cache_t* kv_cache, const csa_raw_t* swa, int32_t swa_window, int32_t n_q,
@@ -194,7 +194,6 @@ csa_status_t csa_attend(const csa_cache_t* kv_cache, const csa_raw_t* swa, int32
                         int32_t n_heads, const int32_t* topk_idx, int32_t k, int64_t max_elig, float softmax_scale,
                         int32_t fuse_inv_rope, const float* rope_cs, int32_t rope_rows, float* out, float* out_lse,
                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  (void)workspace; (void)workspace_bytes;
   if (!valid_cache(kv_cache) || !valid_raw_common(swa, kv_cache ? kv_cache->dim : -1)) return CSA_ERR_INVALID_ARG;
   if (swa->dtype != kv_cache->dtype || swa->roles != 0) return CSA_ERR_INVALID_ARG;
   if (swa->dtype == CSA_FP8_E4M3 && !swa->scales) return CSA_ERR_INVALID_ARG;
@@ -205,10 +204,14 @@ csa_status_t csa_attend(const csa_cache_t* kv_cache, const csa_raw_t* swa, int32
   if (n_q > 0 && (!q_seq || !q_pos || !q || !out || !aligned(q, 16))) return CSA_ERR_INVALID_ARG;
   if (fuse_inv_rope && kv_cache->rope_dims > 0 && (!rope_cs || rope_rows < 1)) return CSA_ERR_INVALID_ARG;
   if (!csa::attend_supported(*kv_cache, q_dtype, n_heads)) return CSA_ERR_UNSUPPORTED;
+  if (int64_t(swa->n_phys) * csa::kBlock > 0x7FFFFFFF) return CSA_ERR_UNSUPPORTED;  // window rows are 32-bit
+  const int64_t max_keys = (topk_idx ? int64_t(k) : max_elig) + swa_window;
+  const size_t need = max_keys <= 0x7FFFFFFF ? csa::attend_workspace(n_q, n_heads, kv_cache->dim, max_keys) : 0;
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16))) return CSA_ERR_WORKSPACE;
   if (n_q == 0) return CSA_OK;
   csa::AttendArgs a{*kv_cache, *swa, swa_window, n_q, q_seq, q_pos, q, q_dtype, n_heads, topk_idx,
                     topk_idx ? k : 0, max_elig, softmax_scale, fuse_inv_rope, rope_cs, rope_rows, out, out_lse};
-  return hip_status(csa::launch_attend(a, stream));
+  return hip_status(csa::launch_attend(a, workspace, workspace_bytes, stream));
 }
 
 csa_status_t csa_inv_rope(int32_t n_q, int32_t n_heads, int32_t dim, int32_t rope_dims, const int32_t* q_pos,

@@ -17,6 +17,13 @@ constexpr int kHistBits = 12;    // first radix digit of the top-k select (bits 
 constexpr int kHistBins = 1 << kHistBits;
 constexpr int kMaxK = 2048;
 
+// ------------------------------------------------------------------ synchronisation
+// Workgroup barrier that orders LDS only. __syncthreads() also fences global memory, which on gfx950
+// waits for every outstanding vector load (vmcnt(0)) and so drains prefetches issued before it; kernels
+// whose waves share nothing but LDS across a barrier use this instead. The "memory" clobber keeps the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // ------------------------------------------------------------------ element codecs
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
@@ -157,7 +164,8 @@ struct AttendArgs {
   float* out_lse;
 };
 bool attend_supported(const csa_cache_t& c, csa_dtype_t q_dtype, int n_heads);
-hipError_t launch_attend(const AttendArgs& a, hipStream_t stream);
+size_t attend_workspace(int n_q, int n_heads, int dim, int64_t max_keys);
+hipError_t launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t stream);
 
 hipError_t launch_inv_rope(int n_q, int n_heads, int dim, int rope_dims, const int32_t* q_pos, const float* rope_cs,
                            int rope_rows, float* io, hipStream_t stream);

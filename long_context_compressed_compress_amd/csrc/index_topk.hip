@@ -11,13 +11,12 @@
 //                   per instruction, fp8 codes widened exactly to bf16); other shapes run on a VALU path.
 //                   Each score becomes an order-preserving 32-bit key; a 4096-bin LDS histogram of
 //                   the top 12 key bits is flushed into the query's global histogram.
-//   2. select    -- one workgroup per (query, run of keys): find the histogram bin that holds the
-//                   k-th largest key, append keys above it to a "sure" list and keys inside it to a
-//                   candidate list. The last workgroup of each query (atomic arrival count) refines the
-//                   boundary bin with 8/8/4-bit digit passes over the candidates, breaks exact ties by
-//                   ascending index, bitonic-sorts the chosen entries by index and writes the output,
-//                   then re-zeroes that query's histogram and counters. The workspace's histogram region
-//                   therefore only needs zeroing once (csa_index_workspace_clear) and stays clean.
+//   2. select    -- one 1024-thread workgroup per query: find the histogram bin that holds the k-th
+//                   largest key, keep keys above it ("sure") and keys inside it (candidates) in LDS in one
+//                   pass over the query's keys, refine the boundary bin with 8/8/4-bit digit passes over
+//                   the candidates, break exact ties by ascending index, bitonic-sort the chosen entries
+//                   by index and write the output, then re-zero the query's histogram. The workspace's
+//                   histogram region therefore only needs zeroing once (csa_index_workspace_clear).
 // The chosen set is unique (score order plus index order is total), so the result does not depend
 // on how work is split or on the order of atomics.
 #include "csa_internal.h"
@@ -28,8 +27,6 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
-constexpr int kScoreChunk = 1024;   // entries per score workgroup
-constexpr int kSelectChunk = 8192;  // keys per select workgroup
 
 struct Workspace {
   uint32_t* keys;   // [n_q][max_elig]
@@ -87,44 +84,107 @@ __device__ __forceinline__ void flush_hist(uint32_t* hist_s, uint32_t* hist_q) {
   }
 }
 
-// fp8 e4m3fn code -> bf16 bits (exact: every e4m3fn value is a bf16 value).
-__device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t c) {
-  const uint32_t s = (c & 0x80u) << 8;
-  const uint32_t mag = c & 0x7Fu;
-  if (mag >= 8u) return s | ((mag << 4) + (120u << 7));
-  // subnormal m * 2^-9 (m = mag < 8)
-  return s | (__float_as_uint(float(mag) * 0.001953125f) >> 16);
+// ------------------------------------------------------------------ MFMA score (WRELU, dim 128, c4a pages)
+// Work unit: one 64-entry page (bf16: 16 KiB, fp8: 8 KiB, contiguous). A wavefront walks its pages with the
+// next page's loads in flight while the current page runs through MFMA. Lane l feeds MFMA column l%16 of
+// each 16-entry tile with dims (l/16)*8 .. +8 of every 32-dim k-step; after the head reduction all four lane
+// groups hold the 16 scores of a tile, and lane l keeps the score of entry l of the page, so each page ends
+// in one coalesced 256-byte key store.
+constexpr int kPagesPerBlock = 32;
+
+template <bool FP8>
+struct PageBuf;
+template <>
+struct PageBuf<false> { uint4 v[4][4]; };  // [tile][k-step] 16 B
+template <>
+struct PageBuf<true> { uint2 v[4][4]; float sc[4]; };  // 8 B codes + per-tile-column scale
+
+template <bool FP8>
+__device__ __forceinline__ void load_page(PageBuf<FP8>& b, const void* pages, const float* scales, int64_t row0,
+                                          int col, int kg) {
+  constexpr int DIM = 128;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t row = row0 + u * 16 + col;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (FP8) {
+        reinterpret_cast<PageBuf<true>&>(b).v[u][ks] =
+            *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(pages) + row * DIM + ks * 32 + kg * 8);
+      } else {
+        reinterpret_cast<PageBuf<false>&>(b).v[u][ks] =
+            *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(pages) + row * DIM + ks * 32 + kg * 8);
+      }
+    }
+    if (FP8) reinterpret_cast<PageBuf<true>&>(b).sc[u] = scales[row];
+  }
 }
 
-__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint2 v) {
+// 8 e4m3fn codes -> 8 bf16 (hardware OCP e4m3 -> f32 conversion, then exact truncation to bf16).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8_hw(uint2 v) {
   uint32_t w[4];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const uint32_t x = h ? v.y : v.x;
-    w[2 * h] = e4m3_to_bf16_bits(x & 0xFF) | (e4m3_to_bf16_bits((x >> 8) & 0xFF) << 16);
-    w[2 * h + 1] = e4m3_to_bf16_bits((x >> 16) & 0xFF) | (e4m3_to_bf16_bits(x >> 24) << 16);
+    const int x = int(h ? v.y : v.x);
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(x, false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(x, true);
+    w[2 * h] = __builtin_amdgcn_perm(__float_as_uint(lo[1]), __float_as_uint(lo[0]), 0x07060302u);
+    w[2 * h + 1] = __builtin_amdgcn_perm(__float_as_uint(hi[1]), __float_as_uint(hi[0]), 0x07060302u);
   }
-  uint4 u = make_uint4(w[0], w[1], w[2], w[3]);
-  return __builtin_bit_cast(bf16x8, u);
+  return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
 }
 
-// ------------------------------------------------------------------ MFMA score (WRELU, dim 128)
-// One wavefront handles 16-entry tiles (always inside one 64-entry page, so 4 KiB / 2 KiB contiguous).
-// Lane l feeds MFMA row/col l%16 and dims (l/16)*8 .. +8 of each 32-dim k-step; accumulator lane l
-// holds heads (l/16)*4 + i of each 16-head tile for entry l%16.
 template <bool FP8, int HT>
-__global__ void __launch_bounds__(256) score_mfma_kernel(IndexArgs a, Workspace ws) {
+__device__ __forceinline__ uint32_t score_page(const PageBuf<FP8>& b, const bf16x8 (&qa)[HT][4],
+                                               const float (&wv)[HT][4], int kg) {
+  uint32_t mine = 0u;
+  float mine_f = 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    bf16x8 kb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (FP8) kb[ks] = fp8x8_to_bf16x8_hw(reinterpret_cast<const PageBuf<true>&>(b).v[u][ks]);
+      else kb[ks] = __builtin_bit_cast(bf16x8, reinterpret_cast<const PageBuf<false>&>(b).v[u][ks]);
+    }
+    float part = 0.f;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ht][ks], kb[ks], acc, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part += wv[ht][i] * fmaxf(acc[i], 0.f);
+    }
+    part += __shfl_xor(part, 16);
+    part += __shfl_xor(part, 32);
+    if (FP8) part *= reinterpret_cast<const PageBuf<true>&>(b).sc[u];
+    if (kg == u) mine_f = part;
+  }
+  mine = score_key(mine_f);
+  return mine;
+}
+
+template <bool FP8, int HT>
+__global__ void __launch_bounds__(256, 2) score_mfma_kernel(IndexArgs a, Workspace ws) {
   constexpr int DIM = 128;
-  constexpr int KS = DIM / 32;
-  constexpr int TILES_PER_ITER = 2;
+  constexpr int E = 64;
   __shared__ uint32_t hist_s[kHistBins];
+  __shared__ int32_t pg_phys[kPagesPerBlock];  // physical page of each page of this block, -1 if unmapped
   const int q = blockIdx.y;
   int seq;
   const int64_t n_elig = query_elig(a, q, &seq);
-  const int64_t e_begin = int64_t(blockIdx.x) * kScoreChunk;
-  if (e_begin >= n_elig) return;  // uniform per block
-  const int64_t e_end = min(n_elig, e_begin + kScoreChunk);
+  const int64_t n_pages = (n_elig + E - 1) / E;
+  const int64_t pg_begin = int64_t(blockIdx.x) * kPagesPerBlock;
+  if (pg_begin >= n_pages) return;  // uniform per block
+  const int64_t pg_end = min(n_pages, pg_begin + kPagesPerBlock);
   for (int b = threadIdx.x; b < kHistBins; b += blockDim.x) hist_s[b] = 0u;
+  if (threadIdx.x < kPagesPerBlock) {
+    const int64_t pg = pg_begin + threadIdx.x;
+    const int32_t* bt = a.cache.block_table + int64_t(seq) * a.cache.bt_stride;
+    const int32_t phys = (pg < pg_end && pg < a.cache.bt_stride) ? bt[pg] : -1;
+    pg_phys[threadIdx.x] = (phys >= 0 && phys < a.cache.n_phys) ? phys : -1;
+  }
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -132,13 +192,12 @@ __global__ void __launch_bounds__(256) score_mfma_kernel(IndexArgs a, Workspace 
   const int kg = lane >> 4;
   const int H = HT * 16;
 
-  // query fragments (A operand) and head weights
-  bf16x8 qa[HT][KS];
+  bf16x8 qa[HT][4];
   const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + int64_t(q) * H * DIM;
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int ks = 0; ks < 4; ++ks)
       qa[ht][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + (ht * 16 + col) * DIM + ks * 32 + kg * 8));
   float wv[HT][4];
 #pragma unroll
@@ -147,60 +206,33 @@ __global__ void __launch_bounds__(256) score_mfma_kernel(IndexArgs a, Workspace 
     for (int i = 0; i < 4; ++i) wv[ht][i] = a.head_w[int64_t(q) * H + ht * 16 + kg * 4 + i];
   __syncthreads();
 
-  const int32_t* bt = a.cache.block_table + int64_t(seq) * a.cache.bt_stride;
-  const char* pages = reinterpret_cast<const char*>(a.cache.pages);
   uint32_t* keys_q = ws.keys + int64_t(q) * a.max_elig;
-
-  const int per_block = kBlock / a.cache.ratio;
-  const int64_t t_begin = e_begin >> 4;
-  const int64_t t_end = (e_end + 15) >> 4;
-  for (int64_t t0 = t_begin + wave * TILES_PER_ITER; t0 < t_end; t0 += 4 * TILES_PER_ITER) {
-    bf16x8 kb[TILES_PER_ITER][KS];
-    float scl[TILES_PER_ITER];
-    bool valid[TILES_PER_ITER];
-#pragma unroll
-    for (int u = 0; u < TILES_PER_ITER; ++u) {
-      const int64_t e = (t0 + u) * 16 + col;
-      const int64_t row = (e < e_end) ? entry_row(bt, a.cache.bt_stride, a.cache.n_phys, e, per_block) : -1;
-      valid[u] = row >= 0;
-      scl[u] = 1.f;
-      if (FP8) {
-        const uint8_t* rp = reinterpret_cast<const uint8_t*>(pages) + (valid[u] ? row : 0) * DIM;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const uint2 raw = valid[u] ? *reinterpret_cast<const uint2*>(rp + ks * 32 + kg * 8) : make_uint2(0, 0);
-          kb[u][ks] = fp8x8_to_bf16x8(raw);
-        }
-        if (valid[u]) scl[u] = a.cache.scales[row];
-      } else {
-        const uint16_t* rp = reinterpret_cast<const uint16_t*>(pages) + (valid[u] ? row : 0) * DIM;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const uint4 raw = valid[u] ? *reinterpret_cast<const uint4*>(rp + ks * 32 + kg * 8) : make_uint4(0, 0, 0, 0);
-          kb[u][ks] = __builtin_bit_cast(bf16x8, raw);
-        }
-      }
+  // this wave's pages: pg_begin + wave, +4, ... < pg_end
+  const int64_t first = __builtin_amdgcn_readfirstlane(int(pg_begin + wave));
+  const int n_mine = first < pg_end ? int((pg_end - 1 - first) / 4 + 1) : 0;
+  auto page_row = [&](int j, bool* ok) -> int64_t {
+    const int slot = wave + 4 * (j < n_mine ? j : n_mine - 1);
+    const int32_t phys = pg_phys[slot];
+    *ok = phys >= 0;
+    return int64_t(*ok ? phys : 0) * E;
+  };
+  auto finish = [&](int j, uint32_t key, bool ok) {
+    const int64_t e = (first + 4 * int64_t(j)) * E + lane;
+    if (e < n_elig) {
+      const uint32_t k2 = ok ? key : 0u;
+      keys_q[e] = k2;
+      atomicAdd(&hist_s[k2 >> (32 - kHistBits)], 1u);
     }
-#pragma unroll
-    for (int u = 0; u < TILES_PER_ITER; ++u) {
-      float part = 0.f;
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ht][ks], kb[u][ks], acc, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) part += wv[ht][i] * fmaxf(acc[i], 0.f);
-      }
-      part += __shfl_xor(part, 16);
-      part += __shfl_xor(part, 32);
-      if (FP8) part *= scl[u];
-      const int64_t e = (t0 + u) * 16 + col;
-      if (kg == 0 && e < e_end) {
-        const uint32_t key = valid[u] ? score_key(part) : 0u;
-        keys_q[e] = key;
-        atomicAdd(&hist_s[key >> (32 - kHistBits)], 1u);
-      }
+  };
+  if (n_mine > 0) {
+    PageBuf<FP8> b0, b1;
+    bool ok0, ok1;
+    load_page<FP8>(b0, a.cache.pages, a.cache.scales, page_row(0, &ok0), col, kg);
+    for (int j = 0; j < n_mine; j += 2) {
+      load_page<FP8>(b1, a.cache.pages, a.cache.scales, page_row(j + 1, &ok1), col, kg);
+      finish(j, score_page<FP8, HT>(b0, qa, wv, kg), ok0);
+      load_page<FP8>(b0, a.cache.pages, a.cache.scales, page_row(j + 2, &ok0), col, kg);
+      if (j + 1 < n_mine) finish(j + 1, score_page<FP8, HT>(b1, qa, wv, kg), ok1);
     }
   }
   flush_hist(hist_s, ws.hist + int64_t(q) * kHistBins);
@@ -253,18 +285,95 @@ __global__ void __launch_bounds__(256) score_valu_kernel(IndexArgs a, Workspace 
 }
 
 // ------------------------------------------------------------------ select
-// Wave-aggregated append of the lanes with `take` set; slots at or beyond `cap` are dropped.
-__device__ __forceinline__ void wave_append(bool take, uint2 item, uint32_t* counter, uint2* list, uint32_t cap) {
-  const uint64_t mask = __ballot(take);
-  if (!mask) return;
-  const int lane = threadIdx.x & 63;
-  uint32_t base = 0;
-  const int leader = __ffsll((unsigned long long)mask) - 1;
-  if (lane == leader) base = atomicAdd(counter, uint32_t(__popcll(mask)));
-  base = __shfl(base, leader);
-  if (take) {
-    const uint32_t off = __popcll(mask & ((1ull << lane) - 1ull));
-    if (base + off < cap) list[base + off] = item;
+// One 1024-thread workgroup per query: boundary bin from the score histogram, one pass over the query's
+// keys that keeps keys above the bin ("sure", at most k) and keys inside it (candidates) in LDS, then the
+// exact refinement of the boundary bin, an index sort and the output -- no cross-workgroup hand-off.
+constexpr int kSelThreads = 1024;
+constexpr int kSelKeysPerThread = 16;
+constexpr int kCandLds = 8192;  // candidates held in LDS; more spill to the workspace list
+
+__device__ __forceinline__ uint32_t dpp_sum16(uint32_t v) {
+  v += uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v += uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v += uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v += uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0x140, 0xF, 0xF, false));  // row_mirror
+  return v;
+}
+
+// Block-wide (kSelThreads) exclusive prefix sum of one value per thread; returns the block total.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, uint32_t* excl) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int NW = kSelThreads / 64;
+  uint32_t incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t t = __shfl_up(incl, off);
+    if (lane >= off) incl += t;
+  }
+  if (lane == 63) tmp[wave] = incl;
+  __syncthreads();
+  uint32_t base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t t = tmp[w];
+    base += (w < wave) ? t : 0u;
+    total += t;
+  }
+  *excl = base + incl - v;
+  __syncthreads();
+  return total;
+}
+
+// Threshold digit of a descending radix step, found by wave 0: the largest d with
+// count(digits >= d) >= need. Writes {d, count(digits > d), count(digit == d)} to out[0..2].
+__device__ __forceinline__ void wave0_digit_desc(const uint32_t* dig, int nbins, uint32_t need, uint32_t* out) {
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  const int per = (nbins + 63) / 64;
+  uint32_t own = 0;
+  for (int j = 0; j < per; ++j) {
+    const int b = lane * per + j;
+    if (b < nbins) own += dig[b];
+  }
+  uint32_t suf = own;  // inclusive suffix over lanes
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t t = __shfl_down(suf, off);
+    if (lane + off < 64) suf += t;
+  }
+  uint32_t run = suf - own;  // digits above this lane's range
+  for (int j = per - 1; j >= 0; --j) {
+    const int b = lane * per + j;
+    if (b >= nbins) continue;
+    const uint32_t c = dig[b];
+    if (run < need && run + c >= need) { out[0] = uint32_t(b); out[1] = run; out[2] = c; }
+    run += c;
+  }
+}
+
+// Ascending counterpart: the smallest d with count(digits <= d) >= want. Writes {d, count(digits < d)}.
+__device__ __forceinline__ void wave0_digit_asc(const uint32_t* dig, int nbins, uint32_t want, uint32_t* out) {
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  const int per = (nbins + 63) / 64;
+  uint32_t own = 0;
+  for (int j = 0; j < per; ++j) {
+    const int b = lane * per + j;
+    if (b < nbins) own += dig[b];
+  }
+  uint32_t pre = own;  // inclusive prefix over lanes
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t t = __shfl_up(pre, off);
+    if (lane >= off) pre += t;
+  }
+  uint32_t run = pre - own;
+  for (int j = 0; j < per; ++j) {
+    const int b = lane * per + j;
+    if (b >= nbins) continue;
+    const uint32_t c = dig[b];
+    if (run < want && run + c >= want) { out[0] = uint32_t(b); out[1] = run; }
+    run += c;
   }
 }
 
@@ -288,166 +397,150 @@ __device__ void bitonic_by_index(uint32_t* idx, uint32_t* key, int n) {
   __syncthreads();
 }
 
-__global__ void __launch_bounds__(256) select_kernel(IndexArgs a, Workspace ws) {
-  __shared__ uint32_t part[256];
+// Wave-aggregated append into an LDS list through an LDS counter; returns the slot of this lane's item.
+__device__ __forceinline__ uint32_t wave_slot(bool take, uint32_t* counter) {
+  const uint64_t mask = __ballot(take);
+  const int lane = threadIdx.x & 63;
+  uint32_t base = 0;
+  if (mask) {
+    const int leader = __ffsll((unsigned long long)mask) - 1;
+    if (lane == leader) base = atomicAdd(counter, uint32_t(__popcll(mask)));
+    base = __shfl(base, leader);
+  }
+  return base + uint32_t(__popcll(mask & ((1ull << lane) - 1ull)));
+}
+
+__global__ void __launch_bounds__(kSelThreads) select_kernel(IndexArgs a, Workspace ws) {
+  __shared__ uint32_t tmp[kSelThreads / 64];
   __shared__ uint32_t dig[256];
-  __shared__ int s_b0;
-  __shared__ int s_last;
-  __shared__ uint32_t s_sel_n;
+  __shared__ uint32_t res[4];
+  __shared__ uint32_t s_cnt[3];                 // sure count, candidate count, selected count
   __shared__ uint32_t sel_idx[kMaxK];
   __shared__ uint32_t sel_key[kMaxK];
+  __shared__ uint2 cand_s[kCandLds];
 
-  const int q = blockIdx.y;
+  const int q = blockIdx.x;
   int seq;
   const int64_t n_elig = query_elig(a, q, &seq);
   const int64_t kk = min<int64_t>(a.k, n_elig);  // entries to choose
-  const uint32_t* hist = ws.hist + int64_t(q) * kHistBins;
   const int tid = threadIdx.x;
+  uint2* cand_g = ws.cand + int64_t(q) * a.max_elig;  // overflow of the candidate list
+  const uint32_t* keys_q = ws.keys + int64_t(q) * a.max_elig;
+  if (tid < 3) s_cnt[tid] = 0u;
 
   // ---- boundary bin: largest b0 with count(bins >= b0) >= kk
-  if (tid == 0) s_b0 = -1;
+  int b0 = -1;
   if (n_elig > a.k) {
-    uint32_t h[16];
+    const uint32_t* hist = ws.hist + int64_t(q) * kHistBins;
+    constexpr int PER = kHistBins / kSelThreads;
+    uint32_t h[PER];
     uint32_t local = 0;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) { h[j] = hist[tid * 16 + j]; local += h[j]; }
-    part[tid] = local;
+    for (int j = 0; j < PER; ++j) { h[j] = hist[tid * PER + j]; local += h[j]; }
+    uint32_t excl;
+    const uint32_t total = block_excl_scan(local, tmp, &excl);
+    uint32_t run = total - excl - local;  // keys in bins above this thread's range
+    if (tid == 0) res[0] = 0xFFFFFFFFu;
     __syncthreads();
-    // inclusive suffix sums over threads (Hillis-Steele from the top)
-    for (int off = 1; off < 256; off <<= 1) {
-      const uint32_t v = (tid + off < 256) ? part[tid + off] : 0u;
-      __syncthreads();
-      part[tid] += v;
-      __syncthreads();
-    }
-    uint32_t run = part[tid] - local;  // keys in bins above this thread's range
-    for (int j = 15; j >= 0; --j) {
-      if (run < uint32_t(kk) && run + h[j] >= uint32_t(kk)) s_b0 = tid * 16 + j;
+    for (int j = PER - 1; j >= 0; --j) {
+      if (run < uint32_t(kk) && run + h[j] >= uint32_t(kk)) res[0] = uint32_t(tid * PER + j);
       run += h[j];
     }
+    __syncthreads();
+    b0 = int(res[0]);
   }
   __syncthreads();
-  const int b0 = s_b0;
 
-  // ---- partition this block's run of keys
-  const uint32_t* keys_q = ws.keys + int64_t(q) * a.max_elig;
-  uint32_t* ctr = ws.ctr + 4 * q;
-  uint2* sure = ws.sure + int64_t(q) * a.k;
-  uint2* cand = ws.cand + int64_t(q) * a.max_elig;
-  const int64_t r_begin = int64_t(blockIdx.x) * kSelectChunk;
-  const int64_t r_end = min(n_elig, r_begin + kSelectChunk);
-  for (int64_t base = r_begin; base < r_end; base += blockDim.x) {
-    const int64_t i = base + tid;
-    const bool in = i < r_end;
-    const uint32_t key = in ? keys_q[i] : 0u;
-    const int bin = int(key >> (32 - kHistBits));
-    const bool is_sure = in && (b0 < 0 || bin > b0);
-    const bool is_cand = in && b0 >= 0 && bin == b0;
-    wave_append(is_sure, make_uint2(key, uint32_t(i)), ctr + 0, sure, uint32_t(a.k));
-    wave_append(is_cand, make_uint2(key, uint32_t(i)), ctr + 1, cand, uint32_t(a.max_elig));
+  // ---- one pass over the keys: sure entries (above the bin) to LDS, candidates (in the bin) to LDS/workspace
+  for (int64_t base = 0; base < n_elig; base += int64_t(kSelThreads) * kSelKeysPerThread) {
+    uint32_t key[kSelKeysPerThread];
+#pragma unroll
+    for (int j = 0; j < kSelKeysPerThread; ++j) {
+      const int64_t i = base + tid + int64_t(kSelThreads) * j;
+      key[j] = keys_q[i < n_elig ? i : 0];  // clamped, unconditional load
+    }
+#pragma unroll
+    for (int j = 0; j < kSelKeysPerThread; ++j) {
+      const int64_t i = base + tid + int64_t(kSelThreads) * j;
+      const bool in = i < n_elig;
+      const int bin = int(key[j] >> (32 - kHistBits));
+      const bool is_sure = in && (b0 < 0 || bin > b0);
+      const bool is_cand = in && b0 >= 0 && bin == b0;
+      const uint32_t ss = wave_slot(is_sure, &s_cnt[0]);
+      if (is_sure && ss < uint32_t(kMaxK)) { sel_idx[ss] = uint32_t(i); sel_key[ss] = key[j]; }
+      const uint32_t cs = wave_slot(is_cand, &s_cnt[1]);
+      if (is_cand) {
+        const uint2 item = make_uint2(key[j], uint32_t(i));
+        if (cs < uint32_t(kCandLds)) cand_s[cs] = item;
+        else if (cs - kCandLds < uint32_t(a.max_elig)) cand_g[cs - kCandLds] = item;
+      }
+    }
   }
-
-  // ---- last arriving block of this query finishes the selection
-  __threadfence();
+  __threadfence_block();
   __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = atomicAdd(ctr + 2, 1u);
-    s_last = (prev == gridDim.x - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
 
-  const uint32_t n_sure = min(__hip_atomic_load(ctr + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), uint32_t(a.k));
-  const uint32_t n_cand = min(__hip_atomic_load(ctr + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), uint32_t(a.max_elig));
+  const uint32_t n_sure = min(s_cnt[0], uint32_t(min<int64_t>(kk, kMaxK)));
+  const uint32_t n_cand = min<uint32_t>(s_cnt[1], uint32_t(min<int64_t>(int64_t(kCandLds) + a.max_elig, 0xFFFFFFFFll)));
+  auto cand_at = [&](uint32_t j) -> uint2 { return j < uint32_t(kCandLds) ? cand_s[j] : cand_g[j - kCandLds]; };
   int64_t need = kk - int64_t(n_sure);
   uint32_t prefix = uint32_t(b0 < 0 ? 0 : b0) << (32 - kHistBits);
   uint32_t pmask = (b0 < 0) ? 0u : (0xFFFFFFFFu << (32 - kHistBits));
-  uint32_t tie_count = 0;
   uint32_t idx_limit = 0xFFFFFFFFu;
   if (need > 0) {
-    // digit passes over key bits 19..12, 11..4, 3..0 among candidates matching the prefix
+    uint32_t tie_count = 0;
     const int shifts[3] = {12, 4, 0};
     const uint32_t dmasks[3] = {0xFFu, 0xFFu, 0xFu};
     for (int p = 0; p < 3; ++p) {
-      dig[tid] = 0u;
+      if (tid < 256) dig[tid] = 0u;
+      if (tid < 3) res[tid] = 0u;
       __syncthreads();
       for (uint32_t j = tid; j < n_cand; j += blockDim.x) {
-        const uint32_t key = cand[j].x;
-        if ((key & pmask) == prefix) atomicAdd(&dig[(key >> shifts[p]) & dmasks[p]], 1u);
+        const uint32_t k2 = cand_at(j).x;
+        if ((k2 & pmask) == prefix) atomicAdd(&dig[(k2 >> shifts[p]) & dmasks[p]], 1u);
       }
       __syncthreads();
-      if (tid == 0) {
-        uint32_t run = 0;
-        int d = int(dmasks[p]);
-        for (; d > 0; --d) {
-          if (run + dig[d] >= uint32_t(need)) break;
-          run += dig[d];
-        }
-        part[0] = uint32_t(d);
-        part[1] = run;
-        part[2] = dig[d];
-      }
+      wave0_digit_desc(dig, int(dmasks[p]) + 1, uint32_t(need), res);
       __syncthreads();
-      const uint32_t d = part[0];
-      need -= part[1];
-      prefix |= d << shifts[p];
+      need -= res[1];
+      prefix |= res[0] << shifts[p];
       pmask |= dmasks[p] << shifts[p];
-      tie_count = part[2];
+      tie_count = res[2];
       __syncthreads();
     }
-    // prefix is now the exact threshold key; take `need` of its tie_count ties, lowest index first
+    // prefix is the exact threshold key; take `need` of its tie_count ties, lowest index first
     if (uint32_t(need) < tie_count) {
       uint32_t ipre = 0, imask = 0;
       int64_t want = need;
       for (int shift = 24; shift >= 0; shift -= 8) {
-        dig[tid] = 0u;
+        if (tid < 256) dig[tid] = 0u;
+        if (tid < 3) res[tid] = 0u;
         __syncthreads();
         for (uint32_t j = tid; j < n_cand; j += blockDim.x) {
-          const uint2 c = cand[j];
+          const uint2 c = cand_at(j);
           if (c.x == prefix && (c.y & imask) == ipre) atomicAdd(&dig[(c.y >> shift) & 0xFFu], 1u);
         }
         __syncthreads();
-        if (tid == 0) {
-          uint32_t run = 0;
-          int d = 0;
-          for (; d < 255; ++d) {
-            if (run + dig[d] >= uint32_t(want)) break;
-            run += dig[d];
-          }
-          part[0] = uint32_t(d);
-          part[1] = run;
-        }
+        wave0_digit_asc(dig, 256, uint32_t(want), res);
         __syncthreads();
-        want -= part[1];
-        ipre |= part[0] << shift;
+        want -= res[1];
+        ipre |= res[0] << shift;
         imask |= 0xFFu << shift;
         __syncthreads();
       }
       idx_limit = ipre;
     }
-  }
-
-  // ---- gather the chosen entries into LDS
-  if (tid == 0) s_sel_n = 0;
-  __syncthreads();
-  for (uint32_t j = tid; j < n_sure; j += blockDim.x) {
-    const uint2 c = sure[j];
-    const uint32_t slot = atomicAdd(&s_sel_n, 1u);
-    if (slot < kMaxK) { sel_idx[slot] = c.y; sel_key[slot] = c.x; }
-  }
-  if (kk - int64_t(n_sure) > 0) {
+    // append the chosen candidates after the sure entries
     for (uint32_t j = tid; j < n_cand; j += blockDim.x) {
-      const uint2 c = cand[j];
+      const uint2 c = cand_at(j);
       const bool take = (c.x > prefix) || (c.x == prefix && c.y <= idx_limit);
       if (take) {
-        const uint32_t slot = atomicAdd(&s_sel_n, 1u);
-        if (slot < kMaxK) { sel_idx[slot] = c.y; sel_key[slot] = c.x; }
+        const uint32_t slot = n_sure + atomicAdd(&s_cnt[2], 1u);
+        if (slot < uint32_t(kMaxK)) { sel_idx[slot] = c.y; sel_key[slot] = c.x; }
       }
     }
   }
   __syncthreads();
-  const int n_sel = int(min<uint32_t>(s_sel_n, uint32_t(kk)));
+  const int n_sel = int(min<int64_t>(int64_t(n_sure) + s_cnt[2], kk));
   int p2 = 1;
   while (p2 < n_sel) p2 <<= 1;
   for (int j = n_sel + tid; j < p2; j += blockDim.x) { sel_idx[j] = 0xFFFFFFFFu; sel_key[j] = 0u; }
@@ -459,10 +552,9 @@ __global__ void __launch_bounds__(256) select_kernel(IndexArgs a, Workspace ws) 
     if (a.out_scores) a.out_scores[int64_t(q) * a.k + j] = ok ? key_score(sel_key[j]) : __uint_as_float(0x7FC00000u);
   }
   if (tid == 0 && a.out_count) a.out_count[q] = n_sel;
-  // leave this query's histogram and counters zeroed for the next call on this workspace
+  // leave this query's histogram zeroed for the next score pass on this workspace
   uint32_t* hq = ws.hist + int64_t(q) * kHistBins;
   for (int b = tid; b < kHistBins; b += blockDim.x) hq[b] = 0u;
-  if (tid < 4) ctr[tid] = 0u;
 }
 
 // Queries with no eligible entry never reach the select kernel's last-block path when the grid
@@ -491,7 +583,7 @@ size_t index_clean_bytes(int n_q) { return clean_bytes(n_q); }
 bool index_supported(const csa_cache_t& c, csa_dtype_t q_dtype, int n_heads, csa_score_t mode) {
   if (c.dtype == CSA_F32) return q_dtype == CSA_F32 && n_heads * c.dim <= 8192;
   if (q_dtype != CSA_BF16) return false;
-  const bool mfma = mode == CSA_SCORE_WRELU && c.dim == 128 && n_heads % 16 == 0 && n_heads <= 64;
+  const bool mfma = mode == CSA_SCORE_WRELU && c.ratio == 4 && c.dim == 128 && n_heads % 16 == 0 && n_heads <= 64;
   return mfma || n_heads * c.dim <= 8192;
 }
 
@@ -508,10 +600,11 @@ hipError_t launch_index_clear(void* ws_base, int n_q, hipStream_t stream) {
 hipError_t launch_index_score(const IndexArgs& a, hipStream_t stream) {
   if (a.n_q == 0 || a.max_elig == 0) return hipSuccess;
   Workspace ws = carve(a.ws, a.n_q, a.max_elig, a.k);
-  const bool mfma = a.cache.dtype != CSA_F32 && a.mode == CSA_SCORE_WRELU && a.cache.dim == 128 &&
-                    a.n_heads % 16 == 0 && a.n_heads <= 64;
+  const bool mfma = a.cache.dtype != CSA_F32 && a.mode == CSA_SCORE_WRELU && a.cache.ratio == 4 &&
+                    a.cache.dim == 128 && a.n_heads % 16 == 0 && a.n_heads <= 64;
   if (mfma) {
-    const dim3 grid(unsigned((a.max_elig + kScoreChunk - 1) / kScoreChunk), unsigned(a.n_q));
+    const int64_t max_pages = (a.max_elig + 63) / 64;
+    const dim3 grid(unsigned((max_pages + kPagesPerBlock - 1) / kPagesPerBlock), unsigned(a.n_q));
     const bool fp8 = a.cache.dtype == CSA_FP8_E4M3;
     switch (a.n_heads / 16) {
       case 1: if (fp8) hipLaunchKernelGGL((score_mfma_kernel<true, 1>), grid, dim3(256), 0, stream, a, ws);
@@ -540,8 +633,7 @@ hipError_t launch_index_select(const IndexArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   Workspace ws = carve(a.ws, a.n_q, a.max_elig, a.k);
-  const dim3 sgrid(unsigned((a.max_elig + kSelectChunk - 1) / kSelectChunk), unsigned(a.n_q));
-  hipLaunchKernelGGL(select_kernel, sgrid, dim3(256), 0, stream, a, ws);
+  hipLaunchKernelGGL(select_kernel, dim3(a.n_q), dim3(kSelThreads), 0, stream, a, ws);
   return hipGetLastError();
 }
 

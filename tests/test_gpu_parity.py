@@ -230,6 +230,8 @@ ATTEND_CASES = [
     (128, 512, 32, "fp8", 0, [3000, 127]),
     (4, 256, 4, "bf16", 100, [2000]),
     (4, 512, 16, "bf16", 2048, [9000]),
+    # many queries: one key split per query, output written directly by the attention workgroup
+    (4, 512, 64, "bf16", 64, [300 + (37 * i) % 400 for i in range(520)]),
 ]
 
 
