@@ -163,6 +163,21 @@ def run_gpu(args, lens):
                    workspace=att_ws)
         if ev: ev[4].record()
 
+    # achievable copy bandwidth of this device (1 GiB device-to-device, read + write counted)
+    src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * (1 << 30) / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+
     for i in range(args.warmup):
         step(layers[i % len(layers)])
     torch.cuda.synchronize()
@@ -179,7 +194,7 @@ def run_gpu(args, lens):
     total_ms = t_start.elapsed_time(t_end)
     names = ["compress", "score", "select", "attend"]
     stage_ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
-    return total_ms, wall, stage_ms
+    return total_ms, wall, stage_ms, copy_gbs
 
 
 # ------------------------------------------------------------------ CPU baseline: the oracle, untuned
@@ -245,7 +260,7 @@ def main():
               f"parallelism), and multi-GPU runs are not part of this build; got --gpus {args.gpus}.", file=sys.stderr)
         sys.exit(2)
     lens = workload_lengths()
-    total_ms, wall, stage_ms = run_gpu(args, lens)
+    total_ms, wall, stage_ms, copy_gbs = run_gpu(args, lens)
     ms_step = total_ms / args.steps
     qps = B * args.steps / (total_ms / 1e3)
     ab = algorithmic_bytes(lens)
@@ -272,11 +287,13 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "score_mfma_kernel (index score)",
                      "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(score_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "alg_bytes_per_launch": ab["score"], "avg_launch_us": round(stage_ms["score"] * 1e3, 2)},
+                     "alg_bytes_per_launch": ab["score"], "avg_launch_us": round(stage_ms["score"] * 1e3, 2),
+                     "frac_of_copy_bw": round(score_gbs / copy_gbs, 4)},
         "gathered_path": {"hbm_gbs": round(path_bytes / (path_ms * 1e-3) / 1e9, 1),
                           "frac_peak": round(path_bytes / (path_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                           "alg_bytes": path_bytes, "us": round(path_ms * 1e3, 2)},
         "stages_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
+        "copy_gbs": round(copy_gbs, 1),
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu_baseline:
