@@ -12,11 +12,12 @@
 //                   Each score becomes an order-preserving 32-bit key; a 4096-bin LDS histogram of
 //                   the top 12 key bits is flushed into the query's global histogram.
 //   2. select    -- one 1024-thread workgroup per query: find the histogram bin that holds the k-th
-//                   largest key, keep keys above it ("sure") and keys inside it (candidates) in LDS in one
-//                   pass over the query's keys, refine the boundary bin with 8/8/4-bit digit passes over
-//                   the candidates, break exact ties by ascending index, bitonic-sort the chosen entries
-//                   by index and write the output, then re-zero the query's histogram. The workspace's
-//                   histogram region therefore only needs zeroing once (csa_index_workspace_clear).
+//                   largest key; in one pass over the query's keys mark the keys above it in a bitmap of
+//                   chosen entries and list the keys inside it (candidates) with a second histogram of
+//                   their next 12 bits; resolve the last 8 bits and exact ties (ascending index) over the
+//                   candidates, read the bitmap in word order for an index-sorted output, then re-zero
+//                   the query's histogram. The workspace's histogram region therefore only needs zeroing
+//                   once (csa_index_workspace_clear).
 // The chosen set is unique (score order plus index order is total), so the result does not depend
 // on how work is split or on the order of atomics.
 #include "csa_internal.h"
@@ -29,32 +30,29 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 
 struct Workspace {
-  uint32_t* keys;   // [n_q][max_elig]
-  uint32_t* hist;   // [n_q][kHistBins]
-  uint32_t* ctr;    // [n_q][4]: sure count, candidate count, arrivals, unused
-  uint2* sure;      // [n_q][k]        (key, index)
-  uint2* cand;      // [n_q][max_elig] (key, index)
+  uint32_t* hist;   // [n_q][kHistBins]: score histogram of key bits 31..20
+  uint32_t* keys;   // [n_q][max_elig]: order-preserving score keys
+  uint2* cand;      // [n_q][max_elig] (key, index): candidates beyond the LDS list
+  uint32_t* bits;   // [n_q][bits_stride]: chosen-entry bitmap of queries too long for LDS
+  int64_t bits_stride;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-__host__ __device__ inline size_t clean_bytes(int n_q) {
-  return align256(size_t(n_q) * kHistBins * 4) + align256(size_t(n_q) * 16);
-}
+__host__ __device__ inline size_t clean_bytes(int n_q) { return align256(size_t(n_q) * kHistBins * 4); }
 
-// Layout: [hist][ctr] (the region that must be zero between calls), then [keys][sure][cand].
-__host__ __device__ inline Workspace carve(void* base, int n_q, int64_t max_elig, int k) {
+// Layout: [hist] (the region that must be zero between calls), then [keys][cand][bits].
+__host__ __device__ inline Workspace carve(void* base, int n_q, int64_t max_elig) {
   char* p = static_cast<char*>(base);
   Workspace w;
   w.hist = reinterpret_cast<uint32_t*>(p);
-  p += align256(size_t(n_q) * kHistBins * 4);
-  w.ctr = reinterpret_cast<uint32_t*>(p);
-  p += align256(size_t(n_q) * 16);
+  p += clean_bytes(n_q);
   w.keys = reinterpret_cast<uint32_t*>(p);
   p += align256(size_t(n_q) * size_t(max_elig) * 4);
-  w.sure = reinterpret_cast<uint2*>(p);
-  p += align256(size_t(n_q) * size_t(k) * 8);
   w.cand = reinterpret_cast<uint2*>(p);
+  p += align256(size_t(n_q) * size_t(max_elig) * 8);
+  w.bits_stride = (max_elig + 31) / 32;
+  w.bits = reinterpret_cast<uint32_t*>(p);
   return w;
 }
 
@@ -68,12 +66,10 @@ __device__ __forceinline__ int64_t query_elig(const IndexArgs& a, int q, int* se
   return n;
 }
 
-__global__ void clear_kernel(uint32_t* hist, uint32_t* ctr, int n_q) {
+__global__ void clear_kernel(uint32_t* hist, int n_q) {
   const int64_t n_h = int64_t(n_q) * kHistBins;
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n_h + 4 * int64_t(n_q);
-       i += int64_t(gridDim.x) * blockDim.x) {
-    if (i < n_h) hist[i] = 0u; else ctr[i - n_h] = 0u;
-  }
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n_h; i += int64_t(gridDim.x) * blockDim.x)
+    hist[i] = 0u;
 }
 
 __device__ __forceinline__ void flush_hist(uint32_t* hist_s, uint32_t* hist_q) {
@@ -285,12 +281,13 @@ __global__ void __launch_bounds__(256) score_valu_kernel(IndexArgs a, Workspace 
 }
 
 // ------------------------------------------------------------------ select
-// One 1024-thread workgroup per query: boundary bin from the score histogram, one pass over the query's
-// keys that keeps keys above the bin ("sure", at most k) and keys inside it (candidates) in LDS, then the
-// exact refinement of the boundary bin, an index sort and the output -- no cross-workgroup hand-off.
+// One 1024-thread workgroup per query: boundary bin from the score histogram (key bits 31..20), one pass
+// over the query's keys that marks keys above the bin in a bitmap of chosen entries and lists the keys
+// inside it (candidates) with a histogram of their bits 19..8, a last 8-bit digit and, for exact ties,
+// the lowest indices first; the bitmap read in word order gives the chosen entries in ascending index.
 constexpr int kSelThreads = 1024;
 constexpr int kSelKeysPerThread = 16;
-constexpr int kCandLds = 8192;  // candidates held in LDS; more spill to the workspace list
+constexpr int kCandLds = 6144;  // candidates held in LDS; more spill to the workspace list
 
 __device__ __forceinline__ uint32_t dpp_sum16(uint32_t v) {
   v += uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
@@ -377,26 +374,6 @@ __device__ __forceinline__ void wave0_digit_asc(const uint32_t* dig, int nbins, 
   }
 }
 
-// Bitonic sort of n (power of two, <= 2048) (index, key) pairs in LDS by ascending index.
-__device__ void bitonic_by_index(uint32_t* idx, uint32_t* key, int n) {
-  for (int size = 2; size <= n; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      __syncthreads();
-      for (int t = threadIdx.x; t < n / 2; t += blockDim.x) {
-        const int lo = 2 * t - (t & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = ((lo & size) == 0);
-        const uint32_t a = idx[lo], b = idx[hi];
-        if ((a > b) == up) {
-          idx[lo] = b; idx[hi] = a;
-          const uint32_t ka = key[lo]; key[lo] = key[hi]; key[hi] = ka;
-        }
-      }
-    }
-  }
-  __syncthreads();
-}
-
 // Wave-aggregated append into an LDS list through an LDS counter; returns the slot of this lane's item.
 __device__ __forceinline__ uint32_t wave_slot(bool take, uint32_t* counter) {
   const uint64_t mask = __ballot(take);
@@ -410,13 +387,15 @@ __device__ __forceinline__ uint32_t wave_slot(bool take, uint32_t* counter) {
   return base + uint32_t(__popcll(mask & ((1ull << lane) - 1ull)));
 }
 
+constexpr int kBitmapLds = 8192;  // LDS bitmap words: queries with up to 262144 eligible entries
+
 __global__ void __launch_bounds__(kSelThreads) select_kernel(IndexArgs a, Workspace ws) {
   __shared__ uint32_t tmp[kSelThreads / 64];
+  __shared__ uint32_t hist2[kHistBins];      // key bits 19..8 of the candidates
   __shared__ uint32_t dig[256];
   __shared__ uint32_t res[4];
-  __shared__ uint32_t s_cnt[3];                 // sure count, candidate count, selected count
-  __shared__ uint32_t sel_idx[kMaxK];
-  __shared__ uint32_t sel_key[kMaxK];
+  __shared__ uint32_t s_cnt[2];              // sure count, candidate count
+  __shared__ uint32_t bitmap_s[kBitmapLds];  // chosen entries, one bit each
   __shared__ uint2 cand_s[kCandLds];
 
   const int q = blockIdx.x;
@@ -426,9 +405,14 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(IndexArgs a, Worksp
   const int tid = threadIdx.x;
   uint2* cand_g = ws.cand + int64_t(q) * a.max_elig;  // overflow of the candidate list
   const uint32_t* keys_q = ws.keys + int64_t(q) * a.max_elig;
-  if (tid < 3) s_cnt[tid] = 0u;
+  const int64_t n_words = (n_elig + 31) / 32;
+  // longer queries keep their bitmap in the workspace
+  uint32_t* bitmap = n_words <= kBitmapLds ? bitmap_s : reinterpret_cast<uint32_t*>(ws.bits + int64_t(q) * ws.bits_stride);
+  for (int64_t w = tid; w < n_words; w += kSelThreads) bitmap[w] = 0u;
+  for (int b = tid; b < kHistBins; b += kSelThreads) hist2[b] = 0u;
+  if (tid < 2) s_cnt[tid] = 0u;
 
-  // ---- boundary bin: largest b0 with count(bins >= b0) >= kk
+  // ---- boundary bin of the score histogram: largest b0 with count(bins >= b0) >= kk
   int b0 = -1;
   if (n_elig > a.k) {
     const uint32_t* hist = ws.hist + int64_t(q) * kHistBins;
@@ -439,7 +423,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(IndexArgs a, Worksp
     for (int j = 0; j < PER; ++j) { h[j] = hist[tid * PER + j]; local += h[j]; }
     uint32_t excl;
     const uint32_t total = block_excl_scan(local, tmp, &excl);
-    uint32_t run = total - excl - local;  // keys in bins above this thread's range
+    uint32_t run = total - excl - local;
     if (tid == 0) res[0] = 0xFFFFFFFFu;
     __syncthreads();
     for (int j = PER - 1; j >= 0; --j) {
@@ -449,9 +433,10 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(IndexArgs a, Worksp
     __syncthreads();
     b0 = int(res[0]);
   }
+  __threadfence_block();
   __syncthreads();
 
-  // ---- one pass over the keys: sure entries (above the bin) to LDS, candidates (in the bin) to LDS/workspace
+  // ---- one pass over the keys: mark keys above the bin, collect keys inside it (and their next 12 bits)
   for (int64_t base = 0; base < n_elig; base += int64_t(kSelThreads) * kSelKeysPerThread) {
     uint32_t key[kSelKeysPerThread];
 #pragma unroll
@@ -466,10 +451,14 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(IndexArgs a, Worksp
       const int bin = int(key[j] >> (32 - kHistBits));
       const bool is_sure = in && (b0 < 0 || bin > b0);
       const bool is_cand = in && b0 >= 0 && bin == b0;
-      const uint32_t ss = wave_slot(is_sure, &s_cnt[0]);
-      if (is_sure && ss < uint32_t(kMaxK)) { sel_idx[ss] = uint32_t(i); sel_key[ss] = key[j]; }
+      const uint64_t sm = __ballot(is_sure);
+      if (sm) {
+        if ((threadIdx.x & 63) == 0) atomicAdd(&s_cnt[0], uint32_t(__popcll(sm)));
+        if (is_sure) atomicOr(&bitmap[i >> 5], 1u << (i & 31));
+      }
       const uint32_t cs = wave_slot(is_cand, &s_cnt[1]);
       if (is_cand) {
+        atomicAdd(&hist2[(key[j] >> 8) & (kHistBins - 1)], 1u);
         const uint2 item = make_uint2(key[j], uint32_t(i));
         if (cs < uint32_t(kCandLds)) cand_s[cs] = item;
         else if (cs - kCandLds < uint32_t(a.max_elig)) cand_g[cs - kCandLds] = item;
@@ -479,35 +468,48 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(IndexArgs a, Worksp
   __threadfence_block();
   __syncthreads();
 
-  const uint32_t n_sure = min(s_cnt[0], uint32_t(min<int64_t>(kk, kMaxK)));
+  const uint32_t n_sure = s_cnt[0];
   const uint32_t n_cand = min<uint32_t>(s_cnt[1], uint32_t(min<int64_t>(int64_t(kCandLds) + a.max_elig, 0xFFFFFFFFll)));
-  auto cand_at = [&](uint32_t j) -> uint2 { return j < uint32_t(kCandLds) ? cand_s[j] : cand_g[j - kCandLds]; };
+  auto cand_at = [=](uint32_t j) -> uint2 { return j < uint32_t(kCandLds) ? cand_s[j] : cand_g[j - kCandLds]; };
   int64_t need = kk - int64_t(n_sure);
-  uint32_t prefix = uint32_t(b0 < 0 ? 0 : b0) << (32 - kHistBits);
-  uint32_t pmask = (b0 < 0) ? 0u : (0xFFFFFFFFu << (32 - kHistBits));
-  uint32_t idx_limit = 0xFFFFFFFFu;
   if (need > 0) {
-    uint32_t tie_count = 0;
-    const int shifts[3] = {12, 4, 0};
-    const uint32_t dmasks[3] = {0xFFu, 0xFFu, 0xFu};
-    for (int p = 0; p < 3; ++p) {
-      if (tid < 256) dig[tid] = 0u;
-      if (tid < 3) res[tid] = 0u;
-      __syncthreads();
-      for (uint32_t j = tid; j < n_cand; j += blockDim.x) {
-        const uint32_t k2 = cand_at(j).x;
-        if ((k2 & pmask) == prefix) atomicAdd(&dig[(k2 >> shifts[p]) & dmasks[p]], 1u);
-      }
-      __syncthreads();
-      wave0_digit_desc(dig, int(dmasks[p]) + 1, uint32_t(need), res);
-      __syncthreads();
-      need -= res[1];
-      prefix |= res[0] << shifts[p];
-      pmask |= dmasks[p] << shifts[p];
-      tie_count = res[2];
-      __syncthreads();
+    // sub-bin of key bits 19..8: largest b1 with count(candidates with bits >= b1) >= need
+    constexpr int PER = kHistBins / kSelThreads;
+    uint32_t h[PER];
+    uint32_t local = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) { h[j] = hist2[tid * PER + j]; local += h[j]; }
+    uint32_t excl;
+    const uint32_t total = block_excl_scan(local, tmp, &excl);
+    uint32_t run = total - excl - local;
+    if (tid == 0) { res[0] = 0u; res[1] = 0u; }
+    __syncthreads();
+    for (int j = PER - 1; j >= 0; --j) {
+      if (run < uint32_t(need) && run + h[j] >= uint32_t(need)) { res[0] = uint32_t(tid * PER + j); res[1] = run; }
+      run += h[j];
     }
+    __syncthreads();
+    uint32_t prefix = (uint32_t(b0) << 20) | (res[0] << 8);
+    const uint32_t pmask = 0xFFFFFF00u;
+    need -= res[1];
+    __syncthreads();
+    // last digit: key bits 7..0 among candidates matching the 24-bit prefix
+    if (tid < 256) dig[tid] = 0u;
+    if (tid < 3) res[tid] = 0u;
+    __syncthreads();
+    for (uint32_t j = tid; j < n_cand; j += blockDim.x) {
+      const uint32_t k2 = cand_at(j).x;
+      if ((k2 & pmask) == prefix) atomicAdd(&dig[k2 & 0xFFu], 1u);
+    }
+    __syncthreads();
+    wave0_digit_desc(dig, 256, uint32_t(need), res);
+    __syncthreads();
+    need -= res[1];
+    prefix |= res[0];
+    const uint32_t tie_count = res[2];
+    __syncthreads();
     // prefix is the exact threshold key; take `need` of its tie_count ties, lowest index first
+    uint32_t idx_limit = 0xFFFFFFFFu;
     if (uint32_t(need) < tie_count) {
       uint32_t ipre = 0, imask = 0;
       int64_t want = need;
@@ -529,27 +531,40 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(IndexArgs a, Worksp
       }
       idx_limit = ipre;
     }
-    // append the chosen candidates after the sure entries
     for (uint32_t j = tid; j < n_cand; j += blockDim.x) {
       const uint2 c = cand_at(j);
-      const bool take = (c.x > prefix) || (c.x == prefix && c.y <= idx_limit);
-      if (take) {
-        const uint32_t slot = n_sure + atomicAdd(&s_cnt[2], 1u);
-        if (slot < uint32_t(kMaxK)) { sel_idx[slot] = c.y; sel_key[slot] = c.x; }
-      }
+      if ((c.x > prefix) || (c.x == prefix && c.y <= idx_limit)) atomicOr(&bitmap[c.y >> 5], 1u << (c.y & 31));
     }
   }
+  __threadfence_block();
   __syncthreads();
-  const int n_sel = int(min<int64_t>(int64_t(n_sure) + s_cnt[2], kk));
-  int p2 = 1;
-  while (p2 < n_sel) p2 <<= 1;
-  for (int j = n_sel + tid; j < p2; j += blockDim.x) { sel_idx[j] = 0xFFFFFFFFu; sel_key[j] = 0u; }
-  if (p2 > 1) bitonic_by_index(sel_idx, sel_key, p2);
-  __syncthreads();
-  for (int j = tid; j < a.k; j += blockDim.x) {
-    const bool ok = j < n_sel;
-    a.out_idx[int64_t(q) * a.k + j] = ok ? int32_t(sel_idx[j]) : -1;
-    if (a.out_scores) a.out_scores[int64_t(q) * a.k + j] = ok ? key_score(sel_key[j]) : __uint_as_float(0x7FC00000u);
+
+  // ---- compaction of the bitmap in index order (each thread owns a run of consecutive words)
+  const int64_t per_t = (n_words + kSelThreads - 1) / kSelThreads;
+  const int64_t w0 = int64_t(tid) * per_t;
+  uint32_t mine = 0;
+  for (int64_t w = w0; w < w0 + per_t && w < n_words; ++w) mine += __popc(bitmap[w]);
+  uint32_t off;
+  const uint32_t n_sel_all = block_excl_scan(mine, tmp, &off);
+  const int n_sel = int(min<int64_t>(n_sel_all, kk));
+  int32_t* outq = a.out_idx + int64_t(q) * a.k;
+  float* outs = a.out_scores ? a.out_scores + int64_t(q) * a.k : nullptr;
+  for (int64_t w = w0; w < w0 + per_t && w < n_words; ++w) {
+    uint32_t bits = bitmap[w];
+    while (bits) {
+      const int b = __ffs(bits) - 1;
+      bits &= bits - 1;
+      const int32_t e = int32_t(w * 32 + b);
+      if (off < uint32_t(a.k)) {
+        outq[off] = e;
+        if (outs) outs[off] = key_score(keys_q[e]);
+      }
+      ++off;
+    }
+  }
+  for (int j = n_sel + tid; j < a.k; j += kSelThreads) {
+    outq[j] = -1;
+    if (outs) outs[j] = __uint_as_float(0x7FC00000u);
   }
   if (tid == 0 && a.out_count) a.out_count[q] = n_sel;
   // leave this query's histogram zeroed for the next score pass on this workspace
@@ -574,8 +589,9 @@ __global__ void empty_rows_kernel(IndexArgs a) {
 }  // namespace
 
 size_t index_workspace(int n_q, int64_t max_elig, int k) {
-  return clean_bytes(n_q) + align256(size_t(n_q) * size_t(max_elig) * 4) + align256(size_t(n_q) * size_t(k) * 8) +
-         align256(size_t(n_q) * size_t(max_elig) * 8);
+  (void)k;
+  return clean_bytes(n_q) + align256(size_t(n_q) * size_t(max_elig) * 4) + align256(size_t(n_q) * size_t(max_elig) * 8) +
+         align256(size_t(n_q) * size_t((max_elig + 31) / 32) * 4);
 }
 
 size_t index_clean_bytes(int n_q) { return clean_bytes(n_q); }
@@ -589,17 +605,17 @@ bool index_supported(const csa_cache_t& c, csa_dtype_t q_dtype, int n_heads, csa
 
 hipError_t launch_index_clear(void* ws_base, int n_q, hipStream_t stream) {
   if (n_q == 0) return hipSuccess;
-  Workspace ws = carve(ws_base, n_q, 0, 1);
-  const int64_t words = int64_t(n_q) * (kHistBins + 4);
+  Workspace ws = carve(ws_base, n_q, 0);
+  const int64_t words = int64_t(n_q) * kHistBins;
   const int64_t nb = (words + 255) / 256;
   const int blocks = int(nb < 4096 ? nb : 4096);
-  hipLaunchKernelGGL(clear_kernel, dim3(blocks), dim3(256), 0, stream, ws.hist, ws.ctr, n_q);
+  hipLaunchKernelGGL(clear_kernel, dim3(blocks), dim3(256), 0, stream, ws.hist, n_q);
   return hipGetLastError();
 }
 
 hipError_t launch_index_score(const IndexArgs& a, hipStream_t stream) {
   if (a.n_q == 0 || a.max_elig == 0) return hipSuccess;
-  Workspace ws = carve(a.ws, a.n_q, a.max_elig, a.k);
+  Workspace ws = carve(a.ws, a.n_q, a.max_elig);
   const bool mfma = a.cache.dtype != CSA_F32 && a.mode == CSA_SCORE_WRELU && a.cache.ratio == 4 &&
                     a.cache.dim == 128 && a.n_heads % 16 == 0 && a.n_heads <= 64;
   if (mfma) {
@@ -632,7 +648,7 @@ hipError_t launch_index_select(const IndexArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(empty_rows_kernel, dim3(a.n_q), dim3(256), 0, stream, a);
     return hipGetLastError();
   }
-  Workspace ws = carve(a.ws, a.n_q, a.max_elig, a.k);
+  Workspace ws = carve(a.ws, a.n_q, a.max_elig);
   hipLaunchKernelGGL(select_kernel, dim3(a.n_q), dim3(kSelThreads), 0, stream, a, ws);
   return hipGetLastError();
 }

@@ -136,6 +136,8 @@ INDEX_GRID_CASES = [
     ("f32", 1, 32, oi.DOT, 64, [1024, 900, 3]),
     ("bf16", 4, 64, oi.WRELU, 100, [3000, 1500]),
     ("fp8", 2, 32, oi.WRELU, 1, [4000, 10]),
+    # more than 2^18 eligible entries: the chosen-entry bitmap lives in the workspace, not in LDS
+    ("bf16", 16, 128, oi.WRELU, 512, [1200000, 40000]),
 ]
 
 
@@ -162,16 +164,22 @@ def test_index_topk_exact_grid_bit_exact(dtype, heads, dim, mode, k, positions):
     assert np.all(np.isnan(sc[~m]))
 
 
-def test_index_topk_all_ties_takes_lowest_indices():
-    _log("index all ties")
-    positions = [5000, 3000]
+@pytest.mark.parametrize("k", [512, 2048])
+def test_index_topk_all_ties_takes_lowest_indices(k):
+    """Every score equal: the lowest k indices win. 30000 tokens give 7498 tied candidates, more than
+    the select kernel's LDS list holds, so its workspace overflow list takes part."""
+    positions = [5000, 3000, 30000]
+    _log(f"index all ties k={k} pos={positions}")
     pc = si.paged_cache(3, 4, 128, "bf16", positions)
     pc.pages[:] = 0x3F80  # every key = 1.0
-    q = np.full((2, 64, 128), 0x3F80, np.uint16)
-    w = np.full((2, 64), 0.5, np.float32)
-    out, cnt, sc = _run_index(pc, positions, q, w, oi.WRELU, 512, "bf16")
-    assert np.array_equal(out[0], np.arange(512)) and np.array_equal(out[1], np.arange(512))
-    assert np.all(sc == 64 * 0.5 * 128.0)
+    q = np.full((3, 64, 128), 0x3F80, np.uint16)
+    w = np.full((3, 64), 0.5, np.float32)
+    out, cnt, sc = _run_index(pc, positions, q, w, oi.WRELU, k, "bf16")
+    for b, p in enumerate(positions):
+        n = min(k, paging.num_eligible(p, 4, 8))
+        assert cnt[b] == n
+        assert np.array_equal(out[b][:n], np.arange(n)) and np.all(out[b][n:] == -1)
+        assert np.all(sc[b][:n] == 64 * 0.5 * 128.0) and np.all(np.isnan(sc[b][n:]))
 
 
 @pytest.mark.parametrize("dtype,positions", [("bf16", [20000, 14011, 9001, 300, 7]), ("fp8", [30000, 2100])])
