@@ -17,6 +17,7 @@ Prints one JSON line (see README of the driver contract): value = queries/s of t
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -37,9 +38,22 @@ K_TOP, SWA = 512, 128
 LEN_LO, LEN_HI = 98304, 131072
 CONFIG_ID = 3
 
+# HBM bytes per launch of the index score kernel on this workload, from one FETCH_SIZE and one WRITE_SIZE
+# counter run (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0 as calibrated on a 1 GiB device copy). The figure holds only
+# for the kernel source it was measured on; for any other source the traffic is reported as unknown.
+SCORE_TRAFFIC = {"source": "long_context_compressed_compress_amd/csrc/index_topk.hip",
+                 "sha256": "e985d1858f777b718e6b0dd3ac17f1793bcf0650d2d7850a419904cfff0e9f6c",
+                 "bytes": 245996850}
+
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def score_traffic():
+    with open(os.path.join(ROOT, SCORE_TRAFFIC["source"]), "rb") as f:
+        same = hashlib.sha256(f.read()).hexdigest() == SCORE_TRAFFIC["sha256"]
+    return SCORE_TRAFFIC["bytes"] if same else None
 
 
 def workload_lengths():
@@ -286,7 +300,8 @@ def main():
                    "window": SWA, "layers_rotated": args.layers, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "kernel": "score_mfma_kernel (index score)",
                      "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(score_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(score_gbs / HBM_PEAK_GBS, 4), "traffic": score_traffic(),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated)",
                      "alg_bytes_per_launch": ab["score"], "avg_launch_us": round(stage_ms["score"] * 1e3, 2),
                      "frac_of_copy_bw": round(score_gbs / copy_gbs, 4)},
         "gathered_path": {"hbm_gbs": round(path_bytes / (path_ms * 1e-3) / 1e9, 1),

@@ -126,7 +126,8 @@ __global__ void __launch_bounds__(256) compress_insert_kernel(CompressArgs a) {
   for (int k = 0; k < CH; ++k) { m[k] = -INFINITY; s[k] = 0.f; acc[k] = 0.f; }
 
   constexpr int ROWS = (WINDOW + G - 1) / G;  // window rows per lane group
-#pragma unroll
+  constexpr int UNROLL = ROWS < 8 ? ROWS : 8;  // c4a windows unroll fully; c128a windows in steps of 8 rows
+#pragma unroll UNROLL
   for (int tt = 0; tt < ROWS; ++tt) {
     const int t = grp + tt * G;
     if (t >= WINDOW) break;
