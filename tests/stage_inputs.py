@@ -42,7 +42,7 @@ def paged_cache(config: int, ratio: int, dim: int, dtype: str, positions, grid: 
         elif dtype == codecs.BF16:
             pages = (vals.view(np.uint32) >> np.uint32(16)).astype(np.uint16)  # grid values are exact in bf16
         else:
-            pages = _grid_e4m3(vals)
+            pages = grid_e4m3(vals)
             scales = np.ones(rows, np.float32)
     else:
         if dtype == codecs.F32:
@@ -54,7 +54,7 @@ def paged_cache(config: int, ratio: int, dim: int, dtype: str, positions, grid: 
     return PagedCache(ratio, window, dim, dtype, bt, pages, scales)
 
 
-def _grid_e4m3(vals: np.ndarray) -> np.ndarray:
+def grid_e4m3(vals: np.ndarray) -> np.ndarray:
     """Codes of the exact-grid values {-2, -1.5, ..., 2} (all exactly representable in e4m3fn)."""
     table = {0.0: 0x00, 0.5: 0x30, 1.0: 0x38, 1.5: 0x3C, 2.0: 0x40}
     out = np.zeros(vals.shape, np.uint8)
@@ -83,3 +83,14 @@ def topk_lists(config: int, positions, ratio: int, k: int) -> np.ndarray:
         take = min(k, n)
         out[qi, :take] = np.sort(g.choice(n, size=take, replace=False))
     return out
+
+
+def grid_bf16(vals: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns of exact-grid values (every grid value is exact in bf16)."""
+    return (np.ascontiguousarray(vals, np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def grid_weights(g: np.random.Generator, shape) -> np.ndarray:
+    """Indexer head weights on the grid {0, 1/16, ..., 1}: with exact-grid keys and queries every partial
+    score is a multiple of 2^-6 below 2^15, so fp32 sums of them are exact in any order."""
+    return (np.rint(g.uniform(0, 16, shape)) / 16).astype(np.float32)
