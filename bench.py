@@ -143,6 +143,24 @@ def algorithmic_bytes(lens):
     return {"score": score, "select": sel, "attend": att, "compress": comp}
 
 
+def time_steps(torch, step, layers, steps, warmup, n_stages):
+    """Warm up, then time `steps` calls of step(layer, events) with HIP events on torch's current stream (the
+    stream every library call runs on). Returns (total ms, mean ms of each stage between consecutive events)."""
+    for i in range(warmup):
+        step(layers[i % len(layers)], None)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_stages + 1)] for _ in range(steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        step(layers[i % len(layers)], evs[i])
+    t1.record()
+    torch.cuda.synchronize()
+    stage = [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j in range(n_stages)]
+    return t0.elapsed_time(t1), stage
+
+
 def run_gpu(args, lens):
     import torch
     import long_context_compressed_compress_amd as csa
@@ -211,6 +229,314 @@ def run_gpu(args, lens):
     return total_ms, wall, stage_ms, copy_gbs
 
 
+# ------------------------------------------------------------------ side workloads, measured in the same run
+POOL_BYTES = 200 * 10 ** 9
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def _gen(torch, seed):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return g
+
+
+def _tail(torch, lens, bt_stride, first_rel, last_rel, cpu_gen):
+    """Table mapping only logical blocks L//256+first_rel .. L//256+last_rel of each sequence (window and
+    compressor-state pages) onto a pool of its own; returns (device table, pages)."""
+    per = last_rel - first_rel + 1
+    perm = torch.randperm(len(lens) * per, generator=cpu_gen).to(torch.int32)
+    t = torch.full((len(lens), bt_stride), -1, dtype=torch.int32)
+    for b, L in enumerate(lens):
+        for j, rel in enumerate(range(first_rel, last_rel + 1)):
+            t[b, int(L) // 256 + rel] = perm[b * per + j]
+    return t.to("cuda"), len(lens) * per
+
+
+def _fp8_rows(torch, gen, rows, dim):
+    """fp8 window rows: N(0,1) x 112 cast to e4m3fn by torch, one fp32 scale 4/448 per row (an N(0,1) row)."""
+    x = torch.randn((rows, dim), generator=gen, device="cuda") * 112.0
+    return x.to(torch.float8_e4m3fn).view(torch.uint8), torch.full((rows,), 4.0 / 448.0, device="cuda")
+
+
+def _build_prefix(torch, csa, cache, state, B, lens, dim, roles, gen, rope, per_call=1):
+    """Append tokens 0..L_b-1 of every sequence (N(0,1) bf16 raw rows and logits) with compress_insert."""
+    for c0 in range(0, B, per_call):
+        n = [int(lens[b]) if c0 <= b < c0 + per_call else 0 for b in range(B)]
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(n)]), dtype=torch.int32, device="cuda")
+        start = torch.zeros(B, dtype=torch.int32, device="cuda")
+        tot = int(sum(n))
+        kv = torch.randn((tot, dim), generator=gen, device="cuda", dtype=torch.bfloat16)
+        lg = torch.randn((tot, roles, dim), generator=gen, device="cuda", dtype=torch.bfloat16)
+        csa.compress_insert(cache, state, start, cu, kv, lg, torch.ones(dim, device="cuda"), 1e-6, rope, max(n))
+        del kv, lg
+
+
+def _decode_bytes(n_elig, p, e_main, e_idx, k, with_index):
+    """Algorithmic bytes of one decode query: (index score, top-k out, attention) -- eligible indexer keys once plus
+    q_idx and head weights; k indices; the selected entries and window rows once plus q and the fp32 output."""
+    sel = min(k, n_elig) if with_index else n_elig
+    score = n_elig * e_idx + H_IDX * D_IDX * 2 + 4 * H_IDX if with_index else 0
+    att = sel * e_main + min(SWA, p + 1) * e_main + (4 * k if with_index else 0) + H * D * 2 + 4 * H * D
+    return score, (4 * k if with_index else 0), att
+
+
+def run_c4(args, torch, csa):
+    """c4a decode at 1M: batch 4, query at 2^20, fp8 main / indexer / window caches with per-entry scales, pages of
+    every layer drawn uniformly from one 200 GB pool; top-512 + window 128."""
+    B, P = 4, 1 << 20
+    nb = P // 256 + 1
+    n_layers = args.layers_c4
+    per_page = 64 * D + 64 * D_IDX + 2 * 64 * 4
+    n_phys = POOL_BYTES // per_page
+    cpu_gen = torch.Generator()
+    cpu_gen.manual_seed(4007)
+    gen = _gen(torch, 4100)
+    pool_m = torch.empty((n_phys * 64, D), dtype=torch.uint8, device="cuda")
+    pool_ms = torch.empty((n_phys * 64,), dtype=torch.float32, device="cuda")
+    pool_i = torch.empty((n_phys * 64, D_IDX), dtype=torch.uint8, device="cuda")
+    pool_is = torch.empty((n_phys * 64,), dtype=torch.float32, device="cuda")
+    ids = torch.randperm(n_phys, generator=cpu_gen)[: n_layers * B * nb].to(torch.int32)
+    rope = csa.rope_table(P + 2, R)
+    lens = [P] * B
+    layers = []
+    for l in range(n_layers):
+        t0 = time.time()
+        ly = type("C4Layer", (), {})()
+        ly.bt = ids[l * B * nb:(l + 1) * B * nb].view(B, nb).contiguous().to("cuda")
+        ly.cache = csa.Cache(4, 8, D, R, pool_m, ly.bt, pool_ms)
+        ly.icache = csa.Cache(4, 8, D_IDX, R_IDX, pool_i, ly.bt, pool_is)
+        tail, n_tail = _tail(torch, [P - 1] * B, nb, -1, 1, cpu_gen)
+        ly.state = csa.Raw(D, 2, torch.zeros((n_tail * 256, D), dtype=torch.bfloat16, device="cuda"), tail,
+                           torch.zeros((n_tail * 256, 2, D), dtype=torch.bfloat16, device="cuda"))
+        ly.istate = csa.Raw(D_IDX, 2, torch.zeros((n_tail * 256, D_IDX), dtype=torch.bfloat16, device="cuda"), tail,
+                            torch.zeros((n_tail * 256, 2, D_IDX), dtype=torch.bfloat16, device="cuda"))
+        codes, sc = _fp8_rows(torch, gen, n_tail * 256, D)
+        ly.swa = csa.Raw(D, 0, codes, tail, None, sc)
+        _build_prefix(torch, csa, ly.cache, ly.state, B, lens, D, 2, gen, rope)
+        _build_prefix(torch, csa, ly.icache, ly.istate, B, lens, D_IDX, 2, gen, rope)
+        ly.pos = torch.full((B,), P, dtype=torch.int32, device="cuda")
+        ly.seq = torch.arange(B, dtype=torch.int32, device="cuda")
+        ly.cu1 = torch.arange(B + 1, dtype=torch.int32, device="cuda")
+        ly.kv1 = torch.randn((B, D), generator=gen, device="cuda").to(torch.bfloat16)
+        ly.lg1 = torch.randn((B, 2, D), generator=gen, device="cuda").to(torch.bfloat16)
+        ly.ikv1 = torch.randn((B, D_IDX), generator=gen, device="cuda").to(torch.bfloat16)
+        ly.ilg1 = torch.randn((B, 2, D_IDX), generator=gen, device="cuda").to(torch.bfloat16)
+        ly.q = torch.randn((B, H, D), generator=gen, device="cuda").to(torch.bfloat16)
+        ly.q_idx = torch.randn((B, H_IDX, D_IDX), generator=gen, device="cuda").to(torch.bfloat16)
+        ly.head_w = torch.rand((B, H_IDX), generator=gen, device="cuda")
+        ly.gamma, ly.igamma = torch.ones(D, device="cuda"), torch.ones(D_IDX, device="cuda")
+        layers.append(ly)
+        torch.cuda.synchronize()
+        log(f"c4 layer {l} built in {time.time() - t0:.1f}s")
+    max_elig = csa.num_eligible(P, 4, 8)
+    ws = csa.index_workspace(B, max_elig, K_TOP, H_IDX)
+    topk = torch.empty((B, K_TOP), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
+    att_ws = torch.empty(max(csa.attend_workspace(B, H, D, K_TOP + SWA), 1), dtype=torch.uint8, device="cuda")
+
+    def step(ly, ev):
+        if ev: ev[0].record()
+        csa.compress_insert(ly.cache, ly.state, ly.pos, ly.cu1, ly.kv1, ly.lg1, ly.gamma, 1e-6, rope, 1)
+        csa.compress_insert(ly.icache, ly.istate, ly.pos, ly.cu1, ly.ikv1, ly.ilg1, ly.igamma, 1e-6, rope, 1)
+        if ev: ev[1].record()
+        csa.index_score(ly.icache, ly.seq, ly.pos, max_elig, ly.q_idx, ly.head_w, csa.SCORE_WRELU, K_TOP, ws)
+        if ev: ev[2].record()
+        csa.index_select(ly.icache, ly.seq, ly.pos, max_elig, K_TOP, topk, ws)
+        if ev: ev[3].record()
+        csa.attend(ly.cache, ly.swa, SWA, ly.seq, ly.pos, ly.q, topk, max_elig, 1.0 / math.sqrt(D), True, rope, out,
+                   workspace=att_ws)
+        if ev: ev[4].record()
+
+    log(f"c4: timing {args.steps} steps")
+    total_ms, st = time_steps(torch, step, layers, args.steps, args.warmup, 4)
+    stage = dict(zip(["compress", "score", "select", "attend"], st))
+    sb, kb, ab = (B * x for x in _decode_bytes(max_elig, P, D + 4, D_IDX + 4, K_TOP, True))
+    del layers, pool_m, pool_ms, pool_i, pool_is, ws
+    torch.cuda.empty_cache()
+    path_ms = stage["score"] + stage["select"] + stage["attend"]
+    score_gbs = sb / (stage["score"] * 1e-3) / 1e9
+    return {
+        "workload": f"c4a fp8 decode, batch {B}, context 2^20 (262143 compressed entries), query at 2^20, 64 heads x "
+                    "K=V 512 fp8 e4m3 + per-entry fp32 scale, indexer 64 heads x 128 fp8 WRELU, top-512 + window 128, "
+                    f"pages uniform over a 200 GB pool ({n_phys} 256-position pages), {n_layers} layers rotated",
+        "value": round(B * args.steps / (total_ms * 1e-3), 1), "unit": "queries/s",
+        "ms_per_step": round(total_ms / args.steps, 5), "dtype": "fp8 e4m3 caches, bf16 queries, fp32 accumulate",
+        "stages_us": {k: round(v * 1e3, 2) for k, v in stage.items()},
+        "roofline": {"bound": "hbm", "kernel": "score_mfma_kernel<fp8> (index score)", "achieved": round(score_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(score_gbs / HBM_PEAK_GBS, 4),
+                     "alg_bytes_per_launch": sb, "avg_launch_us": round(stage["score"] * 1e3, 2)},
+        "gathered_path": {"hbm_gbs": round((sb + kb + ab) / (path_ms * 1e-3) / 1e9, 1),
+                          "frac_peak": round((sb + kb + ab) / (path_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "alg_bytes": sb + kb + ab, "us": round(path_ms * 1e3, 2)},
+    }
+
+
+def run_c2(args, torch, csa):
+    """c128a bf16 decode, batch 16 at position 65536: dense attention over all 512 eligible entries + window 128."""
+    B, P = 16, 65536
+    nb = P // 256 + 1
+    n_layers = args.layers_c2
+    cpu_gen = torch.Generator()
+    cpu_gen.manual_seed(2007)
+    gen = _gen(torch, 2100)
+    rope = csa.rope_table(P + 2, R)
+    layers = []
+    t0 = time.time()
+    for l in range(n_layers):
+        ly = type("C2Layer", (), {})()
+        n_phys = 2 * B * nb
+        ly.bt = torch.randperm(n_phys, generator=cpu_gen)[: B * nb].to(torch.int32).view(B, nb).contiguous().to("cuda")
+        ly.cache = csa.Cache(128, 128, D, R, torch.empty((n_phys * 2, D), dtype=torch.bfloat16, device="cuda"), ly.bt)
+        tail, n_tail = _tail(torch, [P] * B, nb, -1, 0, cpu_gen)
+        ly.state = csa.Raw(D, 1, torch.zeros((n_tail * 256, D), dtype=torch.bfloat16, device="cuda"), tail,
+                           torch.zeros((n_tail * 256, 1, D), dtype=torch.bfloat16, device="cuda"))
+        ly.swa = csa.Raw(D, 0, torch.randn((n_tail * 256, D), generator=gen, device="cuda", dtype=torch.bfloat16), tail)
+        _build_prefix(torch, csa, ly.cache, ly.state, B, [P] * B, D, 1, gen, rope, per_call=B)
+        ly.pos = torch.full((B,), P, dtype=torch.int32, device="cuda")
+        ly.seq = torch.arange(B, dtype=torch.int32, device="cuda")
+        ly.cu1 = torch.arange(B + 1, dtype=torch.int32, device="cuda")
+        ly.kv1 = torch.randn((B, D), generator=gen, device="cuda", dtype=torch.bfloat16)
+        ly.lg1 = torch.randn((B, 1, D), generator=gen, device="cuda", dtype=torch.bfloat16)
+        ly.q = torch.randn((B, H, D), generator=gen, device="cuda", dtype=torch.bfloat16)
+        layers.append(ly)
+    gamma = torch.ones(D, device="cuda")
+    torch.cuda.synchronize()
+    log(f"c2: {n_layers} layers built in {time.time() - t0:.1f}s")
+    n_elig = csa.num_eligible(P, 128, 128)
+    out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
+    att_ws = torch.empty(max(csa.attend_workspace(B, H, D, n_elig + SWA), 1), dtype=torch.uint8, device="cuda")
+
+    def step(ly, ev):
+        if ev: ev[0].record()
+        csa.compress_insert(ly.cache, ly.state, ly.pos, ly.cu1, ly.kv1, ly.lg1, gamma, 1e-6, rope, 1)
+        if ev: ev[1].record()
+        csa.attend(ly.cache, ly.swa, SWA, ly.seq, ly.pos, ly.q, None, n_elig, 1.0 / math.sqrt(D), True, rope, out,
+                   workspace=att_ws)
+        if ev: ev[2].record()
+
+    log(f"c2: timing {args.steps} steps")
+    total_ms, st = time_steps(torch, step, layers, args.steps, args.warmup, 2)
+    stage = dict(zip(["compress", "attend"], st))
+    _, _, ab = (B * x for x in _decode_bytes(n_elig, P, 2 * D, 0, 0, False))
+    del layers
+    torch.cuda.empty_cache()
+    gbs = ab / (stage["attend"] * 1e-3) / 1e9
+    return {
+        "workload": f"c128a bf16 decode, batch {B}, context 65536 (512 compressed entries), query at 65536, 64 heads x "
+                    f"K=V 512, dense over every eligible entry + window 128, {n_layers} layers rotated",
+        "value": round(B * args.steps / (total_ms * 1e-3), 1), "unit": "queries/s",
+        "ms_per_step": round(total_ms / args.steps, 5), "dtype": "bf16",
+        "stages_us": {k: round(v * 1e3, 2) for k, v in stage.items()},
+        "roofline": {"bound": "hbm", "kernel": "attend_split_kernel + attend_combine_kernel (dense)",
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": ab,
+                     "avg_launch_us": round(stage["attend"] * 1e3, 2)},
+    }
+
+
+def run_c5(args, torch, csa):
+    """Prefill chunk on one c4a + c128a layer pair: 2 sequences x 2048 new tokens at context 262144. compress_insert of
+    the chunk into the c4a main, indexer and c128a caches, index + top-512 for all 4096 queries, causal top-512 +
+    window attention (c4a), dense attention over the 2048-2064 eligible c128a entries + window."""
+    B, CTX, CH = 2, 262144, 2048
+    nb = (CTX + CH - 1) // 256 + 1
+    n_layers = args.layers_c5
+    cpu_gen = torch.Generator()
+    cpu_gen.manual_seed(5007)
+    gen = _gen(torch, 5100)
+    rows = CTX + CH + 1
+    rope = csa.rope_table(rows, R)
+    n_q = B * CH
+    q_pos = torch.arange(CTX, CTX + CH, dtype=torch.int32).repeat(B).to("cuda")
+    q_seq = torch.arange(B, dtype=torch.int32).repeat_interleave(CH).to("cuda")
+    start = torch.full((B,), CTX, dtype=torch.int32, device="cuda")
+    cu = (torch.arange(B + 1, dtype=torch.int32) * CH).to("cuda")
+    layers = []
+    t0 = time.time()
+    for l in range(n_layers):
+        ly = type("C5Layer", (), {})()
+        n_phys = B * nb + 8
+        ly.bt = torch.randperm(n_phys, generator=cpu_gen)[: B * nb].to(torch.int32).view(B, nb).contiguous().to("cuda")
+        bf = torch.bfloat16
+        ly.cache = csa.Cache(4, 8, D, R, torch.empty((n_phys * 64, D), dtype=bf, device="cuda"), ly.bt)
+        ly.icache = csa.Cache(4, 8, D_IDX, R_IDX, torch.empty((n_phys * 64, D_IDX), dtype=bf, device="cuda"), ly.bt)
+        ly.hcache = csa.Cache(128, 128, D, R, torch.empty((n_phys * 2, D), dtype=bf, device="cuda"), ly.bt)
+        tail, n_tail = _tail(torch, [CTX] * B, nb, -1, (CH - 1) // 256, cpu_gen)
+        z = lambda *shape: torch.zeros(shape, dtype=bf, device="cuda")
+        ly.state = csa.Raw(D, 2, z(n_tail * 256, D), tail, z(n_tail * 256, 2, D))
+        ly.istate = csa.Raw(D_IDX, 2, z(n_tail * 256, D_IDX), tail, z(n_tail * 256, 2, D_IDX))
+        ly.hstate = csa.Raw(D, 1, z(n_tail * 256, D), tail, z(n_tail * 256, 1, D))
+        ly.swa = csa.Raw(D, 0, torch.randn((n_tail * 256, D), generator=gen, device="cuda", dtype=bf), tail)
+        _build_prefix(torch, csa, ly.cache, ly.state, B, [CTX] * B, D, 2, gen, rope, per_call=B)
+        _build_prefix(torch, csa, ly.icache, ly.istate, B, [CTX] * B, D_IDX, 2, gen, rope, per_call=B)
+        _build_prefix(torch, csa, ly.hcache, ly.hstate, B, [CTX] * B, D, 1, gen, rope, per_call=B)
+        r = lambda *shape: torch.randn(shape, generator=gen, device="cuda", dtype=bf)
+        ly.kv, ly.lg, ly.ikv, ly.ilg = r(n_q, D), r(n_q, 2, D), r(n_q, D_IDX), r(n_q, 2, D_IDX)
+        ly.hkv, ly.hlg = r(n_q, D), r(n_q, 1, D)
+        ly.q, ly.q_idx = r(n_q, H, D), r(n_q, H_IDX, D_IDX)
+        ly.head_w = torch.rand((n_q, H_IDX), generator=gen, device="cuda")
+        layers.append(ly)
+    g1, gi = torch.ones(D, device="cuda"), torch.ones(D_IDX, device="cuda")
+    torch.cuda.synchronize()
+    log(f"c5: {n_layers} layers built in {time.time() - t0:.1f}s")
+    max_elig = csa.num_eligible(CTX + CH - 1, 4, 8)
+    max_elig_h = csa.num_eligible(CTX + CH - 1, 128, 128)
+    ws = csa.index_workspace(n_q, max_elig, K_TOP, H_IDX)
+    topk = torch.empty((n_q, K_TOP), dtype=torch.int32, device="cuda")
+    out = torch.empty((n_q, H, D), dtype=torch.float32, device="cuda")
+    out_h = torch.empty((n_q, H, D), dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(D)
+
+    def step(ly, ev):
+        if ev: ev[0].record()
+        csa.compress_insert(ly.cache, ly.state, start, cu, ly.kv, ly.lg, g1, 1e-6, rope, CH)
+        csa.compress_insert(ly.icache, ly.istate, start, cu, ly.ikv, ly.ilg, gi, 1e-6, rope, CH)
+        csa.compress_insert(ly.hcache, ly.hstate, start, cu, ly.hkv, ly.hlg, g1, 1e-6, rope, CH)
+        if ev: ev[1].record()
+        csa.index_score(ly.icache, q_seq, q_pos, max_elig, ly.q_idx, ly.head_w, csa.SCORE_WRELU, K_TOP, ws)
+        if ev: ev[2].record()
+        csa.index_select(ly.icache, q_seq, q_pos, max_elig, K_TOP, topk, ws)
+        if ev: ev[3].record()
+        csa.attend(ly.cache, ly.swa, SWA, q_seq, q_pos, ly.q, topk, max_elig, scale, True, rope, out)
+        if ev: ev[4].record()
+        csa.attend(ly.hcache, ly.swa, SWA, q_seq, q_pos, ly.q, None, max_elig_h, scale, True, rope, out_h)
+        if ev: ev[5].record()
+
+    steps = max(1, min(args.steps, args.steps_c5))
+    log(f"c5: timing {steps} steps")
+    total_ms, st = time_steps(torch, step, layers, steps, min(args.warmup, 2), 5)
+    stage = dict(zip(["compress", "score", "select", "attend_c4a", "attend_c128a"], st))
+    del layers, ws
+    torch.cuda.empty_cache()
+    pos = np.arange(CTX, CTX + CH)
+    ne = np.array([(p + 1 - 8) // 4 + 1 for p in pos], np.int64)        # eligible c4a entries at each position
+    ne_h = np.array([(p + 1 - 128) // 128 + 1 for p in pos], np.int64)   # eligible c128a entries
+    score_fl = B * int(np.sum(2 * H_IDX * D_IDX * ne))
+    att_fl = B * int(np.sum(4 * H * D * (np.minimum(K_TOP, ne) + SWA)))
+    atth_fl = B * int(np.sum(4 * H * D * (ne_h + SWA)))
+    tf = lambda fl, ms: fl / (ms * 1e-3) / 1e12
+    mf = {"score": (score_fl, stage["score"]), "attend_c4a": (att_fl, stage["attend_c4a"]),
+          "attend_c128a": (atth_fl, stage["attend_c128a"])}
+    return {
+        "workload": f"prefill chunk, batch {B} x {CH} new tokens at context {CTX}: compress_insert (c4a main + indexer, "
+                    "c128a), index + top-512 for every new query, causal top-512 + window 128 attention (c4a), dense "
+                    "c128a attention over 2048-2064 entries + window 128; 64 heads x K=V 512 bf16, indexer 64 x 128 "
+                    f"WRELU, one shared block table, {n_layers} layers rotated",
+        "value": round(n_q * steps / (total_ms * 1e-3), 1), "unit": "tokens/s",
+        "ms_per_step": round(total_ms / steps, 4), "steps": steps, "dtype": "bf16",
+        "stages_us": {k: round(v * 1e3, 1) for k, v in stage.items()},
+        "mfma": {k: {"flop": fl, "tflops": round(tf(fl, ms), 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "frac": round(tf(fl, ms) / MFMA_BF16_PEAK_TFLOPS, 4)} for k, (fl, ms) in mf.items()},
+        "roofline": {"bound": "mfma", "kernel": "score_mfma_kernel (index score, 4096 queries)",
+                     "achieved": round(tf(score_fl, stage["score"]), 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf(score_fl, stage["score"]) / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "avg_launch_us": round(stage["score"] * 1e3, 1)},
+    }
+
+
+SIDE = {"c4": ("c4a_fp8_1m", run_c4), "c2": ("c128a_dense_64k", run_c2), "c5": ("prefill_chunk_256k", run_c5)}
+
+
 # ------------------------------------------------------------------ CPU baseline: the oracle, untuned
 def cpu_baseline(lens, min_seconds=10.0, n_seq=8):
     import synth
@@ -266,6 +592,13 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layers", type=int, default=5)
+    ap.add_argument("--workloads", default="c3,c4,c2,c5",
+                    help="c3 = the headline 128K bf16 decode (always run); side workloads c4 = 1M fp8 decode, "
+                         "c2 = c128a dense 64K decode, c5 = 2048-token prefill chunk at 256K")
+    ap.add_argument("--layers-c4", type=int, default=4)
+    ap.add_argument("--layers-c2", type=int, default=32)
+    ap.add_argument("--layers-c5", type=int, default=2)
+    ap.add_argument("--steps-c5", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
@@ -311,6 +644,22 @@ def main():
         "copy_gbs": round(copy_gbs, 1),
         "wall_s_timed": round(wall, 3),
     }
+    side = [w for w in args.workloads.split(",") if w and w != "c3"]
+    if side:
+        import torch
+        import long_context_compressed_compress_amd as csa
+        torch.cuda.empty_cache()
+        res["workloads"] = {}
+        for w in side:
+            name, fn = SIDE[w]
+            log(f"side workload {name}")
+            t0 = time.time()
+            try:
+                res["workloads"][name] = fn(args, torch, csa)
+            except torch.cuda.OutOfMemoryError as e:  # a device without room for the 200 GB pool; any other error
+                res["workloads"][name] = {"error": f"{type(e).__name__}: {e}"}  # (a device fault above all) propagates
+            torch.cuda.empty_cache()
+            log(f"side workload {name} done in {time.time() - t0:.1f}s")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         res["cpu_baseline"] = cpu_baseline(lens, args.cpu_seconds)

@@ -161,15 +161,16 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a) {
   const float scale = a.scale;
   // descriptor fields as locals: selecting between struct fields per lane would turn into vector loads
   // from the kernel-argument block, each followed by a full wait
-  const int32_t* bt_c = a.cache.block_table + int64_t(seq) * a.cache.bt_stride;
-  const int32_t* bt_w = a.swa.block_table + int64_t(seq) * a.swa.bt_stride;
+  // rows of an out-of-range sequence id are never used (seq_c / seq_w mask them); point at row 0 so that the
+  // unconditional table loads stay inside the table
+  const int32_t* bt_c = a.cache.block_table + int64_t(seq >= 0 && seq < a.cache.batch ? seq : 0) * a.cache.bt_stride;
+  const int32_t* bt_w = a.swa.block_table + int64_t(seq >= 0 && seq < a.swa.batch ? seq : 0) * a.swa.bt_stride;
   const int bts_c = a.cache.bt_stride, bts_w = a.swa.bt_stride;
   const int nph_c = a.cache.n_phys, nph_w = a.swa.n_phys;
   const bool seq_c = seq >= 0 && seq < a.cache.batch;
   const bool seq_w = seq >= 0 && seq < a.swa.batch;
   const int per_block = kBlock / a.cache.ratio;
   const int32_t* topk_q = a.topk ? a.topk + int64_t(q) * a.k : nullptr;
-  const int32_t* idx_src = topk_q ? topk_q : a.q_pos;  // any readable int32 when there is no top-k list
   // The window pool is addressed as an integer offset from the cache pool so that choosing a pool per lane
   // is a register select (a per-lane choice between two pointers otherwise becomes an indexed stack load).
   const char* pages_c = static_cast<const char*>(a.cache.pages);
@@ -186,7 +187,8 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a) {
 #pragma unroll
       for (int j = 0; j < kPerThread; ++j) {
         const int64_t t = pass0 + tid + 256 * j;
-        const int32_t v = idx_src[t < n_c ? t : 0];  // unconditional load
+        // top-k mode: unconditional load (clamped index); dense mode reads no index list at all
+        const int32_t v = topk_q ? topk_q[t < n_c ? t : 0] : 0;
         int64_t e = topk_q ? int64_t(v) : t;
         if (t >= n_c) e = (t < n_keys) ? lo + (t - n_c) : -1;
         ent[j] = int32_t(e);
@@ -465,15 +467,16 @@ __global__ void __launch_bounds__(512) attend_split_kernel(AttendArgs a, SplitPl
   const int64_t k_begin = int64_t(split) * sp.split_keys;
   const int64_t k_end = min<int64_t>(n_keys, k_begin + sp.split_keys);
 
-  const int32_t* bt_c = a.cache.block_table + int64_t(seq) * a.cache.bt_stride;
-  const int32_t* bt_w = a.swa.block_table + int64_t(seq) * a.swa.bt_stride;
+  // rows of an out-of-range sequence id are never used (seq_c / seq_w mask them); point at row 0 so that the
+  // unconditional table loads stay inside the table
+  const int32_t* bt_c = a.cache.block_table + int64_t(seq >= 0 && seq < a.cache.batch ? seq : 0) * a.cache.bt_stride;
+  const int32_t* bt_w = a.swa.block_table + int64_t(seq >= 0 && seq < a.swa.batch ? seq : 0) * a.swa.bt_stride;
   const int bts_c = a.cache.bt_stride, bts_w = a.swa.bt_stride;
   const int nph_c = a.cache.n_phys, nph_w = a.swa.n_phys;
   const bool seq_c = seq >= 0 && seq < a.cache.batch;
   const bool seq_w = seq >= 0 && seq < a.swa.batch;
   const int per_block = kBlock / a.cache.ratio;
   const int32_t* topk_q = a.topk ? a.topk + int64_t(q) * a.k : nullptr;
-  const int32_t* idx_src = topk_q ? topk_q : a.q_pos;
   const char* pages_c = static_cast<const char*>(a.cache.pages);
   const int64_t pages_dw = int64_t(reinterpret_cast<uintptr_t>(a.swa.kv_pages)) - int64_t(reinterpret_cast<uintptr_t>(pages_c));
   const float* scales_c = a.cache.scales;
@@ -502,7 +505,7 @@ __global__ void __launch_bounds__(512) attend_split_kernel(AttendArgs a, SplitPl
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
         const int64_t t = pass0 + tid + 512 * j;
-        const int32_t v = idx_src[t < n_c ? t : 0];
+        const int32_t v = topk_q ? topk_q[t < n_c ? t : 0] : 0;  // dense mode reads no index list
         int64_t e = topk_q ? int64_t(v) : t;
         if (t >= n_c) e = (t < n_keys) ? lo + (t - n_c) : -1;
         ent[j] = int32_t(e);
