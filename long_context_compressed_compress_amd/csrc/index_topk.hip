@@ -31,22 +31,30 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 struct Workspace {
   uint32_t* hist;   // [n_q][kHistBins]: score histogram of key bits 31..20
+  uint32_t* hist2;  // [n_q][kHistBins]: bits 19..8 of the boundary-bin candidates (pre-marked selects)
+  uint32_t* ncand;  // [n_q]: candidates listed by the mark pass (pre-marked selects)
   uint32_t* keys;   // [n_q][max_elig]: order-preserving score keys
   uint2* cand;      // [n_q][max_elig] (key, index): candidates beyond the LDS list
-  uint32_t* bits;   // [n_q][bits_stride]: chosen-entry bitmap of queries too long for LDS
+  uint32_t* bits;   // [n_q][bits_stride]: chosen-entry bitmap (long queries, pre-marked selects)
   int64_t bits_stride;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-__host__ __device__ inline size_t clean_bytes(int n_q) { return align256(size_t(n_q) * kHistBins * 4); }
+__host__ __device__ inline size_t clean_bytes(int n_q) {
+  return 2 * align256(size_t(n_q) * kHistBins * 4) + align256(size_t(n_q) * 4);
+}
 
-// Layout: [hist] (the region that must be zero between calls), then [keys][cand][bits].
+// Layout: [hist][hist2][ncand] (the region that must be zero between calls), then [keys][cand][bits].
 __host__ __device__ inline Workspace carve(void* base, int n_q, int64_t max_elig) {
   char* p = static_cast<char*>(base);
   Workspace w;
   w.hist = reinterpret_cast<uint32_t*>(p);
-  p += clean_bytes(n_q);
+  p += align256(size_t(n_q) * kHistBins * 4);
+  w.hist2 = reinterpret_cast<uint32_t*>(p);
+  p += align256(size_t(n_q) * kHistBins * 4);
+  w.ncand = reinterpret_cast<uint32_t*>(p);
+  p += align256(size_t(n_q) * 4);
   w.keys = reinterpret_cast<uint32_t*>(p);
   p += align256(size_t(n_q) * size_t(max_elig) * 4);
   w.cand = reinterpret_cast<uint2*>(p);
@@ -66,10 +74,9 @@ __device__ __forceinline__ int64_t query_elig(const IndexArgs& a, int q, int* se
   return n;
 }
 
-__global__ void clear_kernel(uint32_t* hist, int n_q) {
-  const int64_t n_h = int64_t(n_q) * kHistBins;
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n_h; i += int64_t(gridDim.x) * blockDim.x)
-    hist[i] = 0u;
+__global__ void clear_kernel(uint32_t* clean, int64_t n_words) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n_words; i += int64_t(gridDim.x) * blockDim.x)
+    clean[i] = 0u;
 }
 
 __device__ __forceinline__ void flush_hist(uint32_t* hist_s, uint32_t* hist_q) {
@@ -297,10 +304,11 @@ __device__ __forceinline__ uint32_t dpp_sum16(uint32_t v) {
   return v;
 }
 
-// Block-wide (kSelThreads) exclusive prefix sum of one value per thread; returns the block total.
+// Block-wide (NT threads) exclusive prefix sum of one value per thread; returns the block total.
+template <int NT = kSelThreads>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, uint32_t* excl) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr int NW = kSelThreads / 64;
+  constexpr int NW = NT / 64;
   uint32_t incl = v;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -389,6 +397,93 @@ __device__ __forceinline__ uint32_t wave_slot(bool take, uint32_t* counter) {
 
 constexpr int kBitmapLds = 8192;  // LDS bitmap words: queries with up to 262144 eligible entries
 
+// ------------------------------------------------------------------ mark pass (few queries with many entries)
+// One workgroup per query cannot scan a long key list quickly, so for few long queries the key pass runs
+// first as its own launch, split into chunks of kMarkChunk keys: each workgroup finds the boundary bin from
+// the query's histogram, writes the chosen-entry bitmap words of its chunk (a set bit = a key above the
+// bin; every word of the chunk is written, so the bitmap needs no clearing), lists the keys inside the bin
+// as candidates and counts their bits 19..8 in hist2. The select pass then only resolves the boundary bin.
+constexpr int kMarkThreads = 256;
+constexpr int kMarkKeysPerThread = 32;
+constexpr int kMarkChunk = kMarkThreads * kMarkKeysPerThread;  // 8192 keys = 256 bitmap words
+constexpr int kPremarkMaxQueries = 64;
+constexpr int64_t kPremarkMinElig = 65536;
+
+__global__ void __launch_bounds__(kMarkThreads) select_mark_kernel(IndexArgs a, Workspace ws) {
+  __shared__ uint32_t tmp[kMarkThreads / 64];
+  __shared__ uint32_t res[2];
+  __shared__ uint32_t h2_s[kHistBins];
+  __shared__ uint2 cand_s[kMarkChunk];  // this chunk's candidates; one global reservation per workgroup
+  const int q = blockIdx.y;
+  int seq;
+  const int64_t n_elig = query_elig(a, q, &seq);
+  if (n_elig <= a.k) return;  // every entry is chosen: the select pass handles the query alone
+  const int64_t c0 = int64_t(blockIdx.x) * kMarkChunk;
+  if (c0 >= n_elig) return;  // uniform per block
+  const int64_t c1 = min<int64_t>(n_elig, c0 + kMarkChunk);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const uint32_t* keys_q = ws.keys + int64_t(q) * a.max_elig;
+  uint32_t key[kMarkKeysPerThread];
+#pragma unroll
+  for (int j = 0; j < kMarkKeysPerThread; ++j) {
+    const int64_t i = c0 + tid + int64_t(kMarkThreads) * j;
+    key[j] = keys_q[i < c1 ? i : c0];  // clamped, unconditional load
+  }
+  for (int b = tid; b < kHistBins; b += kMarkThreads) h2_s[b] = 0u;
+  // boundary bin: the largest b0 with count(bins >= b0) >= k
+  constexpr int PER = kHistBins / kMarkThreads;
+  const uint32_t* hist = ws.hist + int64_t(q) * kHistBins;
+  uint32_t h[PER];
+  uint32_t local = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) { h[j] = hist[tid * PER + j]; local += h[j]; }
+  uint32_t excl;
+  const uint32_t total = block_excl_scan<kMarkThreads>(local, tmp, &excl);
+  uint32_t run = total - excl - local;
+  if (tid == 0) { res[0] = 0xFFFFFFFFu; res[1] = 0u; }
+  __syncthreads();
+  const uint32_t kk = uint32_t(a.k);
+  for (int j = PER - 1; j >= 0; --j) {
+    if (run < kk && run + h[j] >= kk) res[0] = uint32_t(tid * PER + j);
+    run += h[j];
+  }
+  __syncthreads();
+  const uint32_t b0 = res[0];  // 0xFFFFFFFF only for an inconsistent histogram: nothing is marked then
+
+  uint32_t* bits_q = ws.bits + int64_t(q) * ws.bits_stride;
+  uint2* cand_q = ws.cand + int64_t(q) * a.max_elig;
+  const int64_t n_words = (n_elig + 31) / 32;
+#pragma unroll
+  for (int j = 0; j < kMarkKeysPerThread; ++j) {
+    const int64_t i = c0 + tid + int64_t(kMarkThreads) * j;
+    const bool in = i < c1;
+    const uint32_t bin = key[j] >> (32 - kHistBits);
+    const bool is_sure = in && bin > b0 && b0 != 0xFFFFFFFFu;
+    const bool is_cand = in && bin == b0;
+    // a wave's 64 keys are consecutive and start on a 64-key boundary: it owns two whole bitmap words
+    const uint64_t sm = __ballot(is_sure);
+    const int64_t w0 = (c0 + (tid & ~63) + int64_t(kMarkThreads) * j) >> 5;
+    if (lane < 2 && w0 + lane < n_words) bits_q[w0 + lane] = lane == 0 ? uint32_t(sm) : uint32_t(sm >> 32);
+    // candidates go to an LDS list (a returning device-scope atomic per wave would serialise on the
+    // query's counter across XCDs)
+    const uint32_t cs = wave_slot(is_cand, &res[1]);
+    if (is_cand) {
+      cand_s[cs] = make_uint2(key[j], uint32_t(i));
+      atomicAdd(&h2_s[(key[j] >> 8) & (kHistBins - 1)], 1u);
+    }
+  }
+  __syncthreads();
+  const uint32_t n_local = res[1];  // <= kMarkChunk
+  if (tid == 0) tmp[0] = n_local ? atomicAdd(ws.ncand + q, n_local) : 0u;
+  __syncthreads();
+  const uint32_t base = tmp[0];
+  for (uint32_t j = tid; j < n_local; j += kMarkThreads)
+    if (base + j < uint32_t(a.max_elig)) cand_q[base + j] = cand_s[j];
+  flush_hist(h2_s, ws.hist2 + int64_t(q) * kHistBins);
+}
+
+template <bool PRE>
 __global__ void __launch_bounds__(kSelThreads) select_kernel(IndexArgs a, Workspace ws) {
   __shared__ uint32_t tmp[kSelThreads / 64];
   __shared__ uint32_t hist2[kHistBins];      // key bits 19..8 of the candidates
@@ -406,11 +501,29 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(IndexArgs a, Worksp
   uint2* cand_g = ws.cand + int64_t(q) * a.max_elig;  // overflow of the candidate list
   const uint32_t* keys_q = ws.keys + int64_t(q) * a.max_elig;
   const int64_t n_words = (n_elig + 31) / 32;
+  // the mark pass has already scanned this query's keys (bitmap words of keys above the boundary bin,
+  // candidate list and hist2 in the workspace)
+  const bool pre = PRE && n_elig > a.k;
+  uint32_t* bits_g = ws.bits + int64_t(q) * ws.bits_stride;
   // longer queries keep their bitmap in the workspace
-  uint32_t* bitmap = n_words <= kBitmapLds ? bitmap_s : reinterpret_cast<uint32_t*>(ws.bits + int64_t(q) * ws.bits_stride);
-  for (int64_t w = tid; w < n_words; w += kSelThreads) bitmap[w] = 0u;
-  for (int b = tid; b < kHistBins; b += kSelThreads) hist2[b] = 0u;
-  if (tid < 2) s_cnt[tid] = 0u;
+  uint32_t* bitmap = n_words <= kBitmapLds ? bitmap_s : bits_g;
+  uint32_t* hist2_g = ws.hist2 + int64_t(q) * kHistBins;
+  if (pre) {
+    if (bitmap != bits_g)
+      for (int64_t w = tid; w < n_words; w += kSelThreads) bitmap[w] = bits_g[w];
+    for (int b = tid; b < kHistBins; b += kSelThreads) {
+      hist2[b] = hist2_g[b];
+      hist2_g[b] = 0u;  // left zero for the next mark pass
+    }
+    if (tid == 0) {
+      s_cnt[1] = ws.ncand[q];
+      ws.ncand[q] = 0u;
+    }
+  } else {
+    for (int64_t w = tid; w < n_words; w += kSelThreads) bitmap[w] = 0u;
+    for (int b = tid; b < kHistBins; b += kSelThreads) hist2[b] = 0u;
+    if (tid < 2) s_cnt[tid] = 0u;
+  }
 
   // ---- boundary bin of the score histogram: largest b0 with count(bins >= b0) >= kk
   int b0 = -1;
@@ -424,20 +537,21 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(IndexArgs a, Worksp
     uint32_t excl;
     const uint32_t total = block_excl_scan(local, tmp, &excl);
     uint32_t run = total - excl - local;
-    if (tid == 0) res[0] = 0xFFFFFFFFu;
+    if (tid == 0) { res[0] = 0xFFFFFFFFu; res[1] = 0u; }
     __syncthreads();
     for (int j = PER - 1; j >= 0; --j) {
-      if (run < uint32_t(kk) && run + h[j] >= uint32_t(kk)) res[0] = uint32_t(tid * PER + j);
+      if (run < uint32_t(kk) && run + h[j] >= uint32_t(kk)) { res[0] = uint32_t(tid * PER + j); res[1] = run; }
       run += h[j];
     }
     __syncthreads();
     b0 = int(res[0]);
+    if (pre && tid == 0) s_cnt[0] = res[1];  // keys above the bin, all marked by the mark pass
   }
   __threadfence_block();
   __syncthreads();
 
   // ---- one pass over the keys: mark keys above the bin, collect keys inside it (and their next 12 bits)
-  for (int64_t base = 0; base < n_elig; base += int64_t(kSelThreads) * kSelKeysPerThread) {
+  for (int64_t base = 0; base < (pre ? 0 : n_elig); base += int64_t(kSelThreads) * kSelKeysPerThread) {
     uint32_t key[kSelKeysPerThread];
 #pragma unroll
     for (int j = 0; j < kSelKeysPerThread; ++j) {
@@ -469,8 +583,9 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(IndexArgs a, Worksp
   __syncthreads();
 
   const uint32_t n_sure = s_cnt[0];
-  const uint32_t n_cand = min<uint32_t>(s_cnt[1], uint32_t(min<int64_t>(int64_t(kCandLds) + a.max_elig, 0xFFFFFFFFll)));
-  auto cand_at = [=](uint32_t j) -> uint2 { return j < uint32_t(kCandLds) ? cand_s[j] : cand_g[j - kCandLds]; };
+  const uint32_t lds_n = pre ? 0u : uint32_t(kCandLds);  // the mark pass lists every candidate in the workspace
+  const uint32_t n_cand = min<uint32_t>(s_cnt[1], uint32_t(min<int64_t>(int64_t(lds_n) + a.max_elig, 0xFFFFFFFFll)));
+  auto cand_at = [=](uint32_t j) -> uint2 { return j < lds_n ? cand_s[j] : cand_g[j - lds_n]; };
   int64_t need = kk - int64_t(n_sure);
   if (need > 0) {
     // sub-bin of key bits 19..8: largest b1 with count(candidates with bits >= b1) >= need
@@ -605,11 +720,10 @@ bool index_supported(const csa_cache_t& c, csa_dtype_t q_dtype, int n_heads, csa
 
 hipError_t launch_index_clear(void* ws_base, int n_q, hipStream_t stream) {
   if (n_q == 0) return hipSuccess;
-  Workspace ws = carve(ws_base, n_q, 0);
-  const int64_t words = int64_t(n_q) * kHistBins;
+  const int64_t words = int64_t(clean_bytes(n_q) / 4);
   const int64_t nb = (words + 255) / 256;
   const int blocks = int(nb < 4096 ? nb : 4096);
-  hipLaunchKernelGGL(clear_kernel, dim3(blocks), dim3(256), 0, stream, ws.hist, n_q);
+  hipLaunchKernelGGL(clear_kernel, dim3(blocks), dim3(256), 0, stream, static_cast<uint32_t*>(ws_base), words);
   return hipGetLastError();
 }
 
@@ -649,7 +763,13 @@ hipError_t launch_index_select(const IndexArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   Workspace ws = carve(a.ws, a.n_q, a.max_elig);
-  hipLaunchKernelGGL(select_kernel, dim3(a.n_q), dim3(kSelThreads), 0, stream, a, ws);
+  if (a.n_q <= kPremarkMaxQueries && a.max_elig >= kPremarkMinElig) {
+    const dim3 grid(unsigned((a.max_elig + kMarkChunk - 1) / kMarkChunk), unsigned(a.n_q));
+    hipLaunchKernelGGL(select_mark_kernel, grid, dim3(kMarkThreads), 0, stream, a, ws);
+    hipLaunchKernelGGL(select_kernel<true>, dim3(a.n_q), dim3(kSelThreads), 0, stream, a, ws);
+  } else {
+    hipLaunchKernelGGL(select_kernel<false>, dim3(a.n_q), dim3(kSelThreads), 0, stream, a, ws);
+  }
   return hipGetLastError();
 }
 

@@ -164,11 +164,13 @@ def test_index_topk_exact_grid_bit_exact(dtype, heads, dim, mode, k, positions):
     assert np.all(np.isnan(sc[~m]))
 
 
-@pytest.mark.parametrize("k", [512, 2048])
-def test_index_topk_all_ties_takes_lowest_indices(k):
+@pytest.mark.parametrize("k,positions", [(512, [5000, 3000, 30000]), (2048, [5000, 3000, 30000]),
+                                         (512, [300000, 70000, 2000]), (2048, [1100000, 2000])])
+def test_index_topk_all_ties_takes_lowest_indices(k, positions):
     """Every score equal: the lowest k indices win. 30000 tokens give 7498 tied candidates, more than
-    the select kernel's LDS list holds, so its workspace overflow list takes part."""
-    positions = [5000, 3000, 30000]
+    the select kernel's LDS list holds, so its workspace overflow list takes part. With few queries of more
+    than 2^16 entries the keys are scanned by the separate mark pass (every key a candidate), and one query
+    there has fewer entries than k."""
     _log(f"index all ties k={k} pos={positions}")
     pc = si.paged_cache(3, 4, 128, "bf16", positions)
     pc.pages[:] = 0x3F80  # every key = 1.0
@@ -182,7 +184,8 @@ def test_index_topk_all_ties_takes_lowest_indices(k):
         assert np.all(sc[b][:n] == 64 * 0.5 * 128.0) and np.all(np.isnan(sc[b][n:]))
 
 
-@pytest.mark.parametrize("dtype,positions", [("bf16", [20000, 14011, 9001, 300, 7]), ("fp8", [30000, 2100])])
+@pytest.mark.parametrize("dtype,positions", [("bf16", [20000, 14011, 9001, 300, 7]), ("fp8", [30000, 2100]),
+                                             ("bf16", [400000, 90001, 1500]), ("fp8", [1100000, 300])])
 def test_index_topk_continuous_near_ties(dtype, positions):
     """N(0,1) keys and queries: the GPU set equals the oracle set up to swaps certified as fp32 near-ties."""
     _log(f"index continuous {dtype} {positions}")
