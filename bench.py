@@ -38,22 +38,23 @@ K_TOP, SWA = 512, 128
 LEN_LO, LEN_HI = 98304, 131072
 CONFIG_ID = 3
 
-# HBM bytes per launch of the index score kernel on this workload, from one FETCH_SIZE and one WRITE_SIZE
-# counter run (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0 as calibrated on a 1 GiB device copy). The figure holds only
-# for the kernel source it was measured on; for any other source the traffic is reported as unknown.
+# HBM bytes per launch of the index score kernel on the 128K bf16 (c3) and 1M fp8 (c4) decode workloads, from one
+# FETCH_SIZE and one WRITE_SIZE counter run (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0 as calibrated on a 1 GiB device
+# copy). The figures hold only for the kernel source they were measured on; for any other source the traffic is
+# reported as unknown.
 SCORE_TRAFFIC = {"source": "long_context_compressed_compress_amd/csrc/index_topk.hip",
-                 "sha256": "e985d1858f777b718e6b0dd3ac17f1793bcf0650d2d7850a419904cfff0e9f6c",
-                 "bytes": 245996850}
+                 "sha256": "52dfe8230fefc1b1cd768f93fb5154d5828248b9e0cea4e1ebe50104f741c5df",
+                 "bytes": {"c3": 245913600, "c4": 143575347}}
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def score_traffic():
+def score_traffic(workload):
     with open(os.path.join(ROOT, SCORE_TRAFFIC["source"]), "rb") as f:
         same = hashlib.sha256(f.read()).hexdigest() == SCORE_TRAFFIC["sha256"]
-    return SCORE_TRAFFIC["bytes"] if same else None
+    return SCORE_TRAFFIC["bytes"][workload] if same else None
 
 
 def workload_lengths():
@@ -161,6 +162,72 @@ def time_steps(torch, step, layers, steps, warmup, n_stages):
     return t0.elapsed_time(t1), stage
 
 
+EAGER_ONLY = False
+STEP_MODES = {"eager": "eager launches on one stream with an event between stages",
+              "graph": "one HIP graph per layer, every call on one stream",
+              "graph_2stream": "one HIP graph per layer, main-cache compress_insert on a second stream beside the "
+                               "indexer pipeline"}
+
+
+def capture_graphs(torch, layers, fn):
+    """One HIP graph per layer holding one whole step (fn(layer) issued on the capturing stream)."""
+    graphs = []
+    for ly in layers:
+        fn(ly)  # eager warm-up of exactly the captured work
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn(ly)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def time_graphs(torch, graphs, steps, warmup):
+    """Replay the per-layer step graphs in rotation; ms for `steps` replays between two events."""
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1)
+
+
+def best_graph_mode(torch, layers, steps, warmup, sequential, two_stream):
+    """Time the step as one HIP graph per layer, issued on one stream and with the main-cache compress on a second
+    stream; returns (ms of the faster mode, its name, ms of each mode). With --eager-only (profiler runs) no graph
+    is built and (None, "eager", {}) comes back."""
+    if EAGER_ONLY:
+        return None, "eager", {}
+    modes = {}
+    for name, fn in (("graph", sequential), ("graph_2stream", two_stream)):
+        if fn is None:
+            continue
+        graphs = capture_graphs(torch, layers, fn)
+        modes[name] = time_graphs(torch, graphs, steps, warmup)
+        del graphs
+    best = min(modes, key=modes.get)
+    return modes[best], best, modes
+
+
+def overlapped(torch, side, main_compress, index_path, attend):
+    """The decode step with the main-cache compress on a second stream beside the indexer pipeline: only the
+    attention needs the main cache, so it joins there (both streams at the default priority)."""
+    def fn(ly):
+        cur = torch.cuda.current_stream()
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            main_compress(ly)
+        index_path(ly)
+        cur.wait_stream(side)
+        attend(ly)
+    return fn
+
+
 def run_gpu(args, lens):
     import torch
     import long_context_compressed_compress_amd as csa
@@ -223,10 +290,26 @@ def run_gpu(args, lens):
     t_end.record()
     torch.cuda.synchronize()
     wall = time.time() - wall0
-    total_ms = t_start.elapsed_time(t_end)
+    eager_ms = t_start.elapsed_time(t_end)
     names = ["compress", "score", "select", "attend"]
     stage_ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
-    return total_ms, wall, stage_ms, copy_gbs
+
+    # the step as deployed: one HIP graph per layer, main-cache compress overlapped with the indexer pipeline
+    side = torch.cuda.Stream()
+    fn = overlapped(
+        torch, side,
+        lambda ly: csa.compress_insert(ly.cache, ly.state, ly.pos, ly.cu1, ly.kv1, ly.lg1, ly.gamma, 1e-6, rope_main, 1),
+        lambda ly: (csa.compress_insert(ly.icache, ly.istate, ly.pos, ly.cu1, ly.ikv1, ly.ilg1, ly.igamma, 1e-6,
+                                        rope_idx, 1),
+                    csa.index_score(ly.icache, ly.seq, ly.pos, max_elig, ly.q_idx, ly.head_w, csa.SCORE_WRELU, K_TOP,
+                                    ws),
+                    csa.index_select(ly.icache, ly.seq, ly.pos, max_elig, K_TOP, topk, ws)),
+        lambda ly: csa.attend(ly.cache, ly.swa, SWA, ly.seq, ly.pos, ly.q, topk, max_elig, scale, True, rope_main, out,
+                              workspace=att_ws))
+    wall0 = time.time()
+    total_ms, mode, modes = best_graph_mode(torch, layers, args.steps, args.warmup, lambda ly: step(ly, None), fn)
+    wall = time.time() - wall0
+    return total_ms, eager_ms, wall, stage_ms, copy_gbs, mode, modes
 
 
 # ------------------------------------------------------------------ side workloads, measured in the same run
@@ -253,8 +336,8 @@ def _tail(torch, lens, bt_stride, first_rel, last_rel, cpu_gen):
 
 
 def _fp8_rows(torch, gen, rows, dim):
-    """fp8 window rows: N(0,1) x 112 cast to e4m3fn by torch, one fp32 scale 4/448 per row (an N(0,1) row)."""
-    x = torch.randn((rows, dim), generator=gen, device="cuda") * 112.0
+    """fp8 window rows: N(0,1) x 112 clamped to the e4m3fn range and cast by torch, one fp32 scale 4/448 per row."""
+    x = (torch.randn((rows, dim), generator=gen, device="cuda") * 112.0).clamp_(-448.0, 448.0)  # e4m3fn has no inf
     return x.to(torch.float8_e4m3fn).view(torch.uint8), torch.full((rows,), 4.0 / 448.0, device="cuda")
 
 
@@ -348,8 +431,20 @@ def run_c4(args, torch, csa):
         if ev: ev[4].record()
 
     log(f"c4: timing {args.steps} steps")
-    total_ms, st = time_steps(torch, step, layers, args.steps, args.warmup, 4)
+    eager_ms, st = time_steps(torch, step, layers, args.steps, args.warmup, 4)
     stage = dict(zip(["compress", "score", "select", "attend"], st))
+    side = torch.cuda.Stream()
+    fn = overlapped(
+        torch, side,
+        lambda ly: csa.compress_insert(ly.cache, ly.state, ly.pos, ly.cu1, ly.kv1, ly.lg1, ly.gamma, 1e-6, rope, 1),
+        lambda ly: (csa.compress_insert(ly.icache, ly.istate, ly.pos, ly.cu1, ly.ikv1, ly.ilg1, ly.igamma, 1e-6, rope, 1),
+                    csa.index_score(ly.icache, ly.seq, ly.pos, max_elig, ly.q_idx, ly.head_w, csa.SCORE_WRELU, K_TOP,
+                                    ws),
+                    csa.index_select(ly.icache, ly.seq, ly.pos, max_elig, K_TOP, topk, ws)),
+        lambda ly: csa.attend(ly.cache, ly.swa, SWA, ly.seq, ly.pos, ly.q, topk, max_elig, 1.0 / math.sqrt(D), True,
+                              rope, out, workspace=att_ws))
+    total_ms, mode, modes = best_graph_mode(torch, layers, args.steps, args.warmup, lambda ly: step(ly, None), fn)
+    total_ms = eager_ms if total_ms is None else total_ms
     sb, kb, ab = (B * x for x in _decode_bytes(max_elig, P, D + 4, D_IDX + 4, K_TOP, True))
     del layers, pool_m, pool_ms, pool_i, pool_is, ws
     torch.cuda.empty_cache()
@@ -360,10 +455,15 @@ def run_c4(args, torch, csa):
                     "K=V 512 fp8 e4m3 + per-entry fp32 scale, indexer 64 heads x 128 fp8 WRELU, top-512 + window 128, "
                     f"pages uniform over a 200 GB pool ({n_phys} 256-position pages), {n_layers} layers rotated",
         "value": round(B * args.steps / (total_ms * 1e-3), 1), "unit": "queries/s",
-        "ms_per_step": round(total_ms / args.steps, 5), "dtype": "fp8 e4m3 caches, bf16 queries, fp32 accumulate",
+        "ms_per_step": round(total_ms / args.steps, 5), "step_mode": STEP_MODES[mode],
+        "modes_ms_per_step": {"eager_with_stage_events": round(eager_ms / args.steps, 5),
+                              **{k: round(v / args.steps, 5) for k, v in modes.items()}},
+        "dtype": "fp8 e4m3 caches, bf16 queries, fp32 accumulate",
         "stages_us": {k: round(v * 1e3, 2) for k, v in stage.items()},
         "roofline": {"bound": "hbm", "kernel": "score_mfma_kernel<fp8> (index score)", "achieved": round(score_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(score_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": score_traffic("c4"),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated)",
                      "alg_bytes_per_launch": sb, "avg_launch_us": round(stage["score"] * 1e3, 2)},
         "gathered_path": {"hbm_gbs": round((sb + kb + ab) / (path_ms * 1e-3) / 1e9, 1),
                           "frac_peak": round((sb + kb + ab) / (path_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -415,8 +515,10 @@ def run_c2(args, torch, csa):
         if ev: ev[2].record()
 
     log(f"c2: timing {args.steps} steps")
-    total_ms, st = time_steps(torch, step, layers, args.steps, args.warmup, 2)
+    eager_ms, st = time_steps(torch, step, layers, args.steps, args.warmup, 2)
     stage = dict(zip(["compress", "attend"], st))
+    total_ms, mode, modes = best_graph_mode(torch, layers, args.steps, args.warmup, lambda ly: step(ly, None), None)
+    total_ms = eager_ms if total_ms is None else total_ms
     _, _, ab = (B * x for x in _decode_bytes(n_elig, P, 2 * D, 0, 0, False))
     del layers
     torch.cuda.empty_cache()
@@ -425,7 +527,10 @@ def run_c2(args, torch, csa):
         "workload": f"c128a bf16 decode, batch {B}, context 65536 (512 compressed entries), query at 65536, 64 heads x "
                     f"K=V 512, dense over every eligible entry + window 128, {n_layers} layers rotated",
         "value": round(B * args.steps / (total_ms * 1e-3), 1), "unit": "queries/s",
-        "ms_per_step": round(total_ms / args.steps, 5), "dtype": "bf16",
+        "ms_per_step": round(total_ms / args.steps, 5), "step_mode": STEP_MODES[mode],
+        "modes_ms_per_step": {"eager_with_stage_events": round(eager_ms / args.steps, 5),
+                              **{k: round(v / args.steps, 5) for k, v in modes.items()}},
+        "dtype": "bf16",
         "stages_us": {k: round(v * 1e3, 2) for k, v in stage.items()},
         "roofline": {"bound": "hbm", "kernel": "attend_split_kernel + attend_combine_kernel (dense)",
                      "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -600,14 +705,19 @@ def main():
     ap.add_argument("--layers-c5", type=int, default=2)
     ap.add_argument("--steps-c5", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager-only", action="store_true", help="no HIP graphs (for profiler counter runs)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this path runs per GPU with no exchange (sequences shard by data "
               f"parallelism), and multi-GPU runs are not part of this build; got --gpus {args.gpus}.", file=sys.stderr)
         sys.exit(2)
+    global EAGER_ONLY
+    EAGER_ONLY = args.eager_only
     lens = workload_lengths()
-    total_ms, wall, stage_ms, copy_gbs = run_gpu(args, lens)
+    total_ms, eager_ms, wall, stage_ms, copy_gbs, mode, modes = run_gpu(args, lens)
+    if total_ms is None:
+        total_ms = eager_ms
     ms_step = total_ms / args.steps
     qps = B * args.steps / (total_ms / 1e3)
     ab = algorithmic_bytes(lens)
@@ -622,6 +732,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "step_mode": STEP_MODES[mode] + " (stage times below come from an eager pass with an event between stages)",
+        "modes_ms_per_step": {"eager_with_stage_events": round(eager_ms / args.steps, 5),
+                              **{k: round(v / args.steps, 5) for k, v in modes.items()}},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -633,7 +746,7 @@ def main():
                    "window": SWA, "layers_rotated": args.layers, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "kernel": "score_mfma_kernel (index score)",
                      "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(score_gbs / HBM_PEAK_GBS, 4), "traffic": score_traffic(),
+                     "frac": round(score_gbs / HBM_PEAK_GBS, 4), "traffic": score_traffic("c3"),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated)",
                      "alg_bytes_per_launch": ab["score"], "avg_launch_us": round(stage_ms["score"] * 1e3, 2),
                      "frac_of_copy_bw": round(score_gbs / copy_gbs, 4)},
