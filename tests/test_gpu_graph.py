@@ -1,0 +1,134 @@
+"""The decode step captured in a HIP graph, with the main-cache compress_insert on a second stream beside the
+indexer pipeline (the way the benchmark runs it), replays to the eager result.
+
+Shapes are the real ones (64 heads x K=V 512 bf16, indexer 64 heads x 128 WRELU, top-512 + window 128) at a few
+short contexts. Each replay runs after eager work of its own and a synchronisation; every replay's top-k lists,
+attention output and written cache rows must equal the eager step's bit for bit (every kernel is
+deterministic), and the eager step itself is checked against the oracle by the parity tests.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_compressed_compress_amd as csa
+import synth
+
+pytestmark = pytest.mark.gpu
+
+B, H, D, R = 6, 64, 512, 64
+H_IDX, D_IDX = 64, 128
+K_TOP, SWA = 512, 128
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+class _Layer:
+    def __init__(self, seed):
+        dev = "cuda"
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        self.lens = [int(x) for x in synth.lengths_uniform(synth.rng(seed, synth.STREAM_LEN), B, 9000, 20000)]
+        nb = [L // 256 + 1 for L in self.lens]
+        stride = max(nb)
+        n_phys = sum(nb) + 5
+        perm = torch.randperm(n_phys, generator=torch.Generator().manual_seed(seed))[: sum(nb)].to(torch.int32)
+        bt = torch.full((B, stride), -1, dtype=torch.int32)
+        o = 0
+        for b, n in enumerate(nb):
+            bt[b, :n] = perm[o:o + n]
+            o += n
+        self.bt = bt.to(dev)
+        tail = torch.full((B, stride), -1, dtype=torch.int32)
+        for b, L in enumerate(self.lens):
+            tail[b, L // 256 - 1], tail[b, L // 256] = 2 * b, 2 * b + 1
+        self.tail = tail.to(dev)
+        bf = torch.bfloat16
+        self.cache = csa.Cache(4, 8, D, R, torch.zeros((n_phys * 64, D), dtype=bf, device=dev), self.bt)
+        self.icache = csa.Cache(4, 8, D_IDX, R, torch.zeros((n_phys * 64, D_IDX), dtype=bf, device=dev), self.bt)
+        z = lambda *s: torch.zeros(s, dtype=bf, device=dev)
+        self.state = csa.Raw(D, 2, z(2 * B * 256, D), self.tail, z(2 * B * 256, 2, D))
+        self.istate = csa.Raw(D_IDX, 2, z(2 * B * 256, D_IDX), self.tail, z(2 * B * 256, 2, D_IDX))
+        self.swa = csa.Raw(D, 0, torch.randn((2 * B * 256, D), generator=g, device=dev, dtype=bf), self.tail)
+        self.rope = csa.rope_table(max(self.lens) + 2, R)
+        self.gamma, self.igamma = torch.ones(D, device=dev), torch.ones(D_IDX, device=dev)
+        r = lambda *s: torch.randn(s, generator=g, device=dev, dtype=bf)
+        n = self.lens
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(n)]), dtype=torch.int32, device=dev)
+        start = torch.zeros(B, dtype=torch.int32, device=dev)
+        csa.compress_insert(self.cache, self.state, start, cu, r(sum(n), D), r(sum(n), 2, D), self.gamma, 1e-6,
+                            self.rope, max(n))
+        csa.compress_insert(self.icache, self.istate, start, cu, r(sum(n), D_IDX), r(sum(n), 2, D_IDX), self.igamma,
+                            1e-6, self.rope, max(n))
+        self.pos = torch.tensor(self.lens, dtype=torch.int32, device=dev)
+        self.seq = torch.arange(B, dtype=torch.int32, device=dev)
+        self.cu1 = torch.arange(B + 1, dtype=torch.int32, device=dev)
+        self.kv1, self.lg1, self.ikv1, self.ilg1 = r(B, D), r(B, 2, D), r(B, D_IDX), r(B, 2, D_IDX)
+        self.q, self.q_idx = r(B, H, D), r(B, H_IDX, D_IDX)
+        self.head_w = torch.rand((B, H_IDX), generator=g, device=dev)
+        self.max_elig = max(csa.num_eligible(L, 4, 8) for L in self.lens)
+        self.ws = csa.index_workspace(B, self.max_elig, K_TOP, H_IDX)
+        self.att_ws = torch.empty(max(csa.attend_workspace(B, H, D, K_TOP + SWA), 1), dtype=torch.uint8, device=dev)
+        self.topk = torch.full((B, K_TOP), -7, dtype=torch.int32, device=dev)
+        self.out = torch.full((B, H, D), -7.0, device=dev)
+        self.lse = torch.full((B, H), -7.0, device=dev)
+        torch.cuda.synchronize()
+
+    def step(self, side):
+        cur = torch.cuda.current_stream()
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            csa.compress_insert(self.cache, self.state, self.pos, self.cu1, self.kv1, self.lg1, self.gamma, 1e-6,
+                                self.rope, 1)
+        csa.compress_insert(self.icache, self.istate, self.pos, self.cu1, self.ikv1, self.ilg1, self.igamma, 1e-6,
+                            self.rope, 1)
+        csa.index_score(self.icache, self.seq, self.pos, self.max_elig, self.q_idx, self.head_w, csa.SCORE_WRELU,
+                        K_TOP, self.ws)
+        csa.index_select(self.icache, self.seq, self.pos, self.max_elig, K_TOP, self.topk, self.ws)
+        cur.wait_stream(side)
+        csa.attend(self.cache, self.swa, SWA, self.seq, self.pos, self.q, self.topk, self.max_elig,
+                   1.0 / math.sqrt(D), True, self.rope, self.out, self.lse, workspace=self.att_ws)
+
+    def results(self):
+        torch.cuda.synchronize()
+        return [t.clone() for t in (self.topk, self.out, self.lse, self.cache.pages, self.icache.pages,
+                                    self.state.kv_pages, self.istate.kv_pages)]
+
+    def poison(self):
+        """Overwrite every output and every slot the step writes, so a replay that skips work shows."""
+        self.topk.fill_(-7)
+        self.out.fill_(-7.0)
+        self.lse.fill_(-7.0)
+        for L, b in zip(self.lens, range(B)):
+            if L % 4 == 3:  # the decode token completes entry (L - 7) / 4
+                i = (L - 7) // 4
+                for c in (self.cache, self.icache):
+                    c.pages[int(self.bt[b, i // 64]) * 64 + i % 64].fill_(float("nan"))
+
+
+def test_graph_replay_matches_eager():
+    torch.cuda.synchronize()
+    ly = _Layer(81)
+    other = _Layer(82)
+    side = torch.cuda.Stream()
+    _log(f"graph replay: contexts {ly.lens}")
+    ly.step(side)
+    ref = ly.results()
+    assert int((ref[0] >= 0).sum()) == B * K_TOP
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ly.step(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        other.step(side)          # eager work of the program between replays, on other buffers
+        ly.poison()
+        torch.cuda.synchronize()
+        g.replay()
+        got = ly.results()
+        for name, a, b in zip(["topk", "out", "lse", "pages", "idx pages", "state", "idx state"], got, ref):
+            assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
+                               b.view(torch.uint8) if b.dtype == torch.bfloat16 else b), f"replay {rep}: {name} differs"
+        _log(f"replay {rep}: identical to the eager step")
