@@ -94,6 +94,7 @@ __device__ __forceinline__ void flush_hist(uint32_t* hist_s, uint32_t* hist_q) {
 // groups hold the 16 scores of a tile, and lane l keeps the score of entry l of the page, so each page ends
 // in one coalesced 256-byte key store.
 constexpr int kPagesPerBlock = 32;
+constexpr int kQueryFastMin = 256;  // queries per launch from which the grid walks queries first
 
 template <bool FP8>
 struct PageBuf;
@@ -168,17 +169,20 @@ __device__ __forceinline__ uint32_t score_page(const PageBuf<FP8>& b, const bf16
   return mine;
 }
 
+// Grid order: with few queries (decode) blockIdx.x walks the page runs of one query; with many queries per
+// sequence (a prefill chunk) blockIdx.x walks the queries (query_fast), so the workgroups running at the same
+// time read the same run of pages and an XCD's L2 serves its queries' repeated reads of them.
 template <bool FP8, int HT>
-__global__ void __launch_bounds__(256, 2) score_mfma_kernel(IndexArgs a, Workspace ws) {
+__global__ void __launch_bounds__(256, 2) score_mfma_kernel(IndexArgs a, Workspace ws, int query_fast) {
   constexpr int DIM = 128;
   constexpr int E = 64;
   __shared__ uint32_t hist_s[kHistBins];
   __shared__ int32_t pg_phys[kPagesPerBlock];  // physical page of each page of this block, -1 if unmapped
-  const int q = blockIdx.y;
+  const int q = query_fast ? blockIdx.x : blockIdx.y;
   int seq;
   const int64_t n_elig = query_elig(a, q, &seq);
   const int64_t n_pages = (n_elig + E - 1) / E;
-  const int64_t pg_begin = int64_t(blockIdx.x) * kPagesPerBlock;
+  const int64_t pg_begin = int64_t(query_fast ? blockIdx.y : blockIdx.x) * kPagesPerBlock;
   if (pg_begin >= n_pages) return;  // uniform per block
   const int64_t pg_end = min(n_pages, pg_begin + kPagesPerBlock);
   for (int b = threadIdx.x; b < kHistBins; b += blockDim.x) hist_s[b] = 0u;
@@ -734,17 +738,19 @@ hipError_t launch_index_score(const IndexArgs& a, hipStream_t stream) {
                     a.cache.dim == 128 && a.n_heads % 16 == 0 && a.n_heads <= 64;
   if (mfma) {
     const int64_t max_pages = (a.max_elig + 63) / 64;
-    const dim3 grid(unsigned((max_pages + kPagesPerBlock - 1) / kPagesPerBlock), unsigned(a.n_q));
+    const int64_t runs = (max_pages + kPagesPerBlock - 1) / kPagesPerBlock;
+    const int qf = (a.n_q >= kQueryFastMin && runs <= 65535) ? 1 : 0;
+    const dim3 grid = qf ? dim3(unsigned(a.n_q), unsigned(runs)) : dim3(unsigned(runs), unsigned(a.n_q));
     const bool fp8 = a.cache.dtype == CSA_FP8_E4M3;
     switch (a.n_heads / 16) {
-      case 1: if (fp8) hipLaunchKernelGGL((score_mfma_kernel<true, 1>), grid, dim3(256), 0, stream, a, ws);
-              else hipLaunchKernelGGL((score_mfma_kernel<false, 1>), grid, dim3(256), 0, stream, a, ws); break;
-      case 2: if (fp8) hipLaunchKernelGGL((score_mfma_kernel<true, 2>), grid, dim3(256), 0, stream, a, ws);
-              else hipLaunchKernelGGL((score_mfma_kernel<false, 2>), grid, dim3(256), 0, stream, a, ws); break;
-      case 3: if (fp8) hipLaunchKernelGGL((score_mfma_kernel<true, 3>), grid, dim3(256), 0, stream, a, ws);
-              else hipLaunchKernelGGL((score_mfma_kernel<false, 3>), grid, dim3(256), 0, stream, a, ws); break;
-      default: if (fp8) hipLaunchKernelGGL((score_mfma_kernel<true, 4>), grid, dim3(256), 0, stream, a, ws);
-               else hipLaunchKernelGGL((score_mfma_kernel<false, 4>), grid, dim3(256), 0, stream, a, ws); break;
+      case 1: if (fp8) hipLaunchKernelGGL((score_mfma_kernel<true, 1>), grid, dim3(256), 0, stream, a, ws, qf);
+              else hipLaunchKernelGGL((score_mfma_kernel<false, 1>), grid, dim3(256), 0, stream, a, ws, qf); break;
+      case 2: if (fp8) hipLaunchKernelGGL((score_mfma_kernel<true, 2>), grid, dim3(256), 0, stream, a, ws, qf);
+              else hipLaunchKernelGGL((score_mfma_kernel<false, 2>), grid, dim3(256), 0, stream, a, ws, qf); break;
+      case 3: if (fp8) hipLaunchKernelGGL((score_mfma_kernel<true, 3>), grid, dim3(256), 0, stream, a, ws, qf);
+              else hipLaunchKernelGGL((score_mfma_kernel<false, 3>), grid, dim3(256), 0, stream, a, ws, qf); break;
+      default: if (fp8) hipLaunchKernelGGL((score_mfma_kernel<true, 4>), grid, dim3(256), 0, stream, a, ws, qf);
+               else hipLaunchKernelGGL((score_mfma_kernel<false, 4>), grid, dim3(256), 0, stream, a, ws, qf); break;
     }
   } else {
     const dim3 grid(unsigned((a.max_elig + 255) / 256), unsigned(a.n_q));

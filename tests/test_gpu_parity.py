@@ -138,6 +138,8 @@ INDEX_GRID_CASES = [
     ("fp8", 2, 32, oi.WRELU, 1, [4000, 10]),
     # more than 2^18 eligible entries: the chosen-entry bitmap lives in the workspace, not in LDS
     ("bf16", 16, 128, oi.WRELU, 512, [1200000, 40000]),
+    # many queries in one launch: the score grid walks queries first
+    ("bf16", 64, 128, oi.WRELU, 512, [300 + 13 * i for i in range(300)]),
 ]
 
 
