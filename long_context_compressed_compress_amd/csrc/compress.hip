@@ -48,13 +48,19 @@ __device__ __forceinline__ void zero_vec(float (&v)[N]) {
   for (int k = 0; k < N; ++k) v[k] = 0.f;
 }
 
+// Largest b < batch with cu[b] <= row (cu non-decreasing, cu[0] = 0 <= row). The whole wave calls it for one row:
+// each lane tests one offset, so a batch of up to 64 sequences costs one memory round trip (a binary search
+// would cost one per step).
 __device__ __forceinline__ int find_seq(const int32_t* cu, int batch, int row) {
-  int lo = 0, hi = batch - 1;  // largest b with cu[b] <= row
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (cu[mid] <= row) lo = mid; else hi = mid - 1;
+  const int lane = threadIdx.x & 63;
+  int found = 0;
+  for (int base = 0; base < batch; base += 64) {
+    const int b = base + lane;
+    const uint64_t le = __ballot(b < batch && cu[b] <= row);
+    if (le) found = base + 63 - __clzll((unsigned long long)le);
+    if (le != ~0ull) break;  // a lane of this chunk is past the row: later chunks are too
   }
-  return lo;
+  return found;
 }
 
 template <typename TIn, int OUT, int D, int RATIO, int WINDOW>
@@ -120,6 +126,28 @@ __global__ void __launch_bounds__(256) compress_insert_kernel(CompressArgs a) {
   const int ch0 = ch_lane * CH;
   const int cu_b = a.cu_new[b];
   const int32_t* st_bt = (b < a.state.batch) ? a.state.block_table + int64_t(b) * a.state.bt_stride : nullptr;
+  // everything the epilogue reads that does not depend on the window (the output slot, gamma, the anchor's
+  // cos/sin) is loaded now, so its round trip overlaps the window loads
+  const int64_t slot = entry_row(a.cache.block_table + int64_t(b) * a.cache.bt_stride, a.cache.bt_stride,
+                                 a.cache.n_phys, i, E);
+  float gam[CH];
+#pragma unroll
+  for (int k = 0; k < CH; ++k) gam[k] = a.gamma[ch0 + k];
+  const int R = a.cache.rope_dims;
+  const int base = D - R;
+  const bool rot = R > 0 && first < a.rope_rows;
+  float rc[CH / 2], rsn[CH / 2];
+#pragma unroll
+  for (int k = 0; k < CH; k += 2) {
+    const int c = ch0 + k;
+    rc[k / 2] = 1.f;
+    rsn[k / 2] = 0.f;
+    if (rot && c >= base) {
+      const float* cs = a.rope_cs + first * int64_t(R) + (c - base);  // pair j = (c - base) / 2 at 2j
+      rc[k / 2] = cs[0];
+      rsn[k / 2] = cs[1];
+    }
+  }
 
   float m[CH], s[CH], acc[CH];
 #pragma unroll
@@ -184,28 +212,21 @@ __global__ void __launch_bounds__(256) compress_insert_kernel(CompressArgs a) {
   for (int off = 1; off < NLC; off <<= 1) ss += __shfl_xor(ss, off);
   const float rms = sqrtf(ss / float(D) + a.eps);
 #pragma unroll
-  for (int k = 0; k < CH; ++k) y[k] = y[k] / rms * a.gamma[ch0 + k];
+  for (int k = 0; k < CH; ++k) y[k] = y[k] / rms * gam[k];
 
   // RoPE at the anchor on dims [D-R, D), interleaved pairs (each lane owns whole pairs)
-  const int R = a.cache.rope_dims;
-  const int base = D - R;
-  if (R > 0 && first < a.rope_rows) {
-    const float* cs = a.rope_cs + first * int64_t(R);  // row stride R/2 pairs * 2 floats
+  if (rot) {
 #pragma unroll
     for (int k = 0; k < CH; k += 2) {
       const int c = ch0 + k;
       if (c >= base) {
-        const int j = (c - base) >> 1;
-        const float co = cs[2 * j], si = cs[2 * j + 1];
+        const float co = rc[k / 2], si = rsn[k / 2];
         const float u = y[k], v = y[k + 1];
         y[k] = u * co - v * si;
         y[k + 1] = u * si + v * co;
       }
     }
   }
-
-  const int64_t slot = entry_row(a.cache.block_table + int64_t(b) * a.cache.bt_stride, a.cache.bt_stride,
-                                 a.cache.n_phys, i, E);
   const bool in_table = b < a.cache.batch && slot >= 0;
   if (OUT == 2) {
     float amax = 0.f;
