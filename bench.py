@@ -309,7 +309,33 @@ def run_gpu(args, lens):
     wall0 = time.time()
     total_ms, mode, modes = best_graph_mode(torch, layers, args.steps, args.warmup, lambda ly: step(ly, None), fn)
     wall = time.time() - wall0
-    return total_ms, eager_ms, wall, stage_ms, copy_gbs, mode, modes
+    epilogue = time_output_epilogue(torch, csa, layers, step, out, topk, max_elig, scale, rope_main, att_ws)
+    return total_ms, eager_ms, wall, stage_ms, copy_gbs, mode, modes, epilogue
+
+
+def time_output_epilogue(torch, csa, layers, step, out, topk, max_elig, scale, rope, att_ws, group=128, iters=100):
+    """The fused inverse RoPE + fp8 quantisation of the attention output (the step after this path, in front of an
+    fp8 output projection) on this workload's real outputs: attention without its fused rotation, then the
+    epilogue kernel timed alone. Algorithmic bytes: the fp32 output read once, codes and group scales written."""
+    ly = layers[0]
+    step(ly, None)
+    raw = torch.empty_like(out)
+    csa.attend(ly.cache, ly.swa, SWA, ly.seq, ly.pos, ly.q, topk, max_elig, scale, False, rope, raw, workspace=att_ws)
+    codes = torch.empty(raw.shape, dtype=torch.uint8, device="cuda")
+    scales = torch.empty((B, H, D // group), dtype=torch.float32, device="cuda")
+    for _ in range(5):
+        csa.inv_rope_quant_fp8(raw, ly.pos, R, rope, group, codes, scales)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        csa.inv_rope_quant_fp8(raw, ly.pos, R, rope, group, codes, scales)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / iters
+    alg = raw.numel() * 4 + codes.numel() + scales.numel() * 4
+    return {"kernel": "inv_rope_quant_kernel", "group": group, "us": round(us, 2), "alg_bytes": alg,
+            "gbs": round(alg / (us * 1e-6) / 1e9, 1), "frac_peak": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 # ------------------------------------------------------------------ side workloads, measured in the same run
@@ -715,7 +741,7 @@ def main():
     global EAGER_ONLY
     EAGER_ONLY = args.eager_only
     lens = workload_lengths()
-    total_ms, eager_ms, wall, stage_ms, copy_gbs, mode, modes = run_gpu(args, lens)
+    total_ms, eager_ms, wall, stage_ms, copy_gbs, mode, modes, epilogue = run_gpu(args, lens)
     if total_ms is None:
         total_ms = eager_ms
     ms_step = total_ms / args.steps
@@ -754,6 +780,7 @@ def main():
                           "frac_peak": round(path_bytes / (path_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                           "alg_bytes": path_bytes, "us": round(path_ms * 1e3, 2)},
         "stages_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
+        "fp8_output_epilogue": epilogue,
         "copy_gbs": round(copy_gbs, 1),
         "wall_s_timed": round(wall, 3),
     }

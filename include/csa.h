@@ -12,6 +12,7 @@
  *   csa_index_topk       (c4a only)
  *   csa_attend           (top-k entries + raw sliding window, or dense for c128a; optional fused inverse RoPE)
  *   csa_inv_rope         (standalone inverse RoPE, when not fused)
+ *   csa_inv_rope_quant_fp8 (inverse RoPE fused with fp8 quantisation of the output, for an fp8 projection)
  *
  * Conventions
  *   - Every pointer is DEVICE memory unless marked [host]. Every call is asynchronous on
@@ -200,6 +201,26 @@ csa_status_t csa_attend(const csa_cache_t* kv_cache, const csa_raw_t* swa, int32
 csa_status_t csa_inv_rope(int32_t n_q, int32_t n_heads, int32_t dim, int32_t rope_dims,
                           const int32_t* q_pos, const float* rope_cs, int32_t rope_rows, float* io,
                           hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * csa_inv_rope_quant_fp8 -- inverse RoPE fused with fp8 quantisation of the attention output.
+ * [P1] "GPU Compute Saturation" (kernel fusions) / [P2] "3.2 內核": the main attention output goes
+ * through the inverse RoPE and into the fp8 batched matmul of the o_lora projection; fusing the two
+ * saves one HBM round trip of the output. The pages give no quantisation granularity; here every
+ * (query, head) row is cut into groups of `group` consecutive channels, each stored as OCP e4m3fn
+ * codes with one fp32 scale by the rule of the fp8 caches, computed in fp32 after the rotation:
+ * amax = max|y|, code = e4m3_rne(y * (448 / amax)), scale = amax / 448 (zero codes and scale 1 for an
+ * all-zero group).
+ *   in          [n_q][n_heads][dim] fp32, the output of csa_attend with fuse_inv_rope = 0 (16-byte aligned)
+ *   out_codes   [n_q][n_heads][dim] uint8 (8-byte aligned); out_scales [n_q][n_heads][dim / group] fp32
+ *   dim in {32, 64, 128, 256, 512}; rope_dims even, <= dim (the rotated dims are the last rope_dims);
+ *   group a power of two in [8, 512] dividing dim; n_heads in [1, 128]; positions q_pos[q] < rope_rows
+ *   (a position outside the table leaves that query unrotated). Caller-owned buffers; nothing is allocated.
+ * ------------------------------------------------------------------------------------------- */
+csa_status_t csa_inv_rope_quant_fp8(int32_t n_q, int32_t n_heads, int32_t dim, int32_t rope_dims,
+                                    const int32_t* q_pos, const float* rope_cs, int32_t rope_rows,
+                                    const float* in, int32_t group, uint8_t* out_codes, float* out_scales,
+                                    hipStream_t stream);
 
 /* csa_rope_table -- fill rope_cs [rows][rope_dims/2][2] with (cos, sin) of p * theta^(-2j/R),
  * evaluated in fp64 and rounded to the nearest fp32. */

@@ -69,6 +69,7 @@ def lib() -> ctypes.CDLL:
             "csa_attend": (I32, [CP, RP, I32, I32, P, P, P, I32, I32, P, I32, I64, F, I32, P, I32, P, P, P, SZ, P]),
             "csa_inv_rope": (I32, [I32, I32, I32, I32, P, P, I32, P, P]),
             "csa_rope_table": (I32, [I32, I32, D, P, P]),
+            "csa_inv_rope_quant_fp8": (I32, [I32, I32, I32, I32, P, P, I32, P, I32, P, P, P]),
             "csa_num_entries": (I64, [I64, I32, I32]),
             "csa_num_eligible": (I64, [I64, I32, I32]),
             "csa_entry_slot": (I64, [P, I64, I32]),
@@ -234,6 +235,22 @@ def inv_rope(io: torch.Tensor, q_pos: torch.Tensor, rope_dims: int, rope_cs: tor
     n_q, n_heads, dim = io.shape
     _check("csa_inv_rope", lib().csa_inv_rope(n_q, n_heads, dim, rope_dims, _ptr(q_pos), _ptr(rope_cs),
                                               rope_cs.shape[0], _ptr(io), _stream(stream)))
+
+
+def inv_rope_quant_fp8(x: torch.Tensor, q_pos: torch.Tensor, rope_dims: int, rope_cs: torch.Tensor, group: int,
+                       out_codes: Optional[torch.Tensor] = None, out_scales: Optional[torch.Tensor] = None,
+                       stream=None):
+    """Inverse RoPE + fp8 quantisation of an attention output x [n_q][H][D] fp32 (not inverse-rotated yet).
+    Returns (codes uint8 [n_q][H][D], scales fp32 [n_q][H][D // group])."""
+    n_q, n_heads, dim = x.shape
+    if out_codes is None:
+        out_codes = torch.empty((n_q, n_heads, dim), dtype=torch.uint8, device=x.device)
+    if out_scales is None:
+        out_scales = torch.empty((n_q, n_heads, dim // group), dtype=torch.float32, device=x.device)
+    _check("csa_inv_rope_quant_fp8", lib().csa_inv_rope_quant_fp8(
+        n_q, n_heads, dim, rope_dims, _ptr(q_pos), _ptr(rope_cs), rope_cs.shape[0], _ptr(x), group,
+        _ptr(out_codes), _ptr(out_scales), _stream(stream)))
+    return out_codes, out_scales
 
 
 def rope_table(rows: int, rope_dims: int, theta: float = 10000.0, device="cuda", stream=None) -> torch.Tensor:

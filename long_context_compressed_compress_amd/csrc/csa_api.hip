@@ -222,6 +222,20 @@ csa_status_t csa_inv_rope(int32_t n_q, int32_t n_heads, int32_t dim, int32_t rop
   return hip_status(csa::launch_inv_rope(n_q, n_heads, dim, rope_dims, q_pos, rope_cs, rope_rows, io, stream));
 }
 
+csa_status_t csa_inv_rope_quant_fp8(int32_t n_q, int32_t n_heads, int32_t dim, int32_t rope_dims,
+                                    const int32_t* q_pos, const float* rope_cs, int32_t rope_rows, const float* in,
+                                    int32_t group, uint8_t* out_codes, float* out_scales, hipStream_t stream) {
+  if (n_q < 0 || n_heads < 1 || n_heads > 128 || !valid_dim(dim)) return CSA_ERR_INVALID_ARG;
+  if (rope_dims < 0 || rope_dims > dim || (rope_dims & 1)) return CSA_ERR_INVALID_ARG;
+  if (group < 8 || group > 512 || (group & (group - 1)) || dim % group) return CSA_ERR_INVALID_ARG;
+  if (n_q == 0) return CSA_OK;
+  if (!q_pos || !in || !out_codes || !out_scales || !aligned(in, 16) || !aligned(out_codes, 8) || !aligned(out_scales, 4))
+    return CSA_ERR_INVALID_ARG;
+  if (rope_dims > 0 && (!rope_cs || rope_rows < 1)) return CSA_ERR_INVALID_ARG;
+  return hip_status(csa::launch_inv_rope_quant(n_q, n_heads, dim, rope_dims, q_pos, rope_cs, rope_rows, in, group,
+                                               out_codes, out_scales, stream));
+}
+
 csa_status_t csa_rope_table(int32_t rows, int32_t rope_dims, double theta, float* rope_cs, hipStream_t stream) {
   if (rows < 0 || rope_dims < 2 || (rope_dims & 1) || !(theta > 0.0) || !isfinite(theta)) return CSA_ERR_INVALID_ARG;
   if (rows > 0 && !rope_cs) return CSA_ERR_INVALID_ARG;

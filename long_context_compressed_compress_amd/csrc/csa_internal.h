@@ -170,5 +170,8 @@ hipError_t launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStre
 hipError_t launch_inv_rope(int n_q, int n_heads, int dim, int rope_dims, const int32_t* q_pos, const float* rope_cs,
                            int rope_rows, float* io, hipStream_t stream);
 hipError_t launch_rope_table(int rows, int rope_dims, double theta, float* out, hipStream_t stream);
+hipError_t launch_inv_rope_quant(int n_q, int n_heads, int dim, int rope_dims, const int32_t* q_pos,
+                                 const float* rope_cs, int rope_rows, const float* in, int group, uint8_t* codes,
+                                 float* scales, hipStream_t stream);
 
 }  // namespace csa

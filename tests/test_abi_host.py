@@ -29,10 +29,11 @@ def L():
 def test_exports_every_declared_symbol(L):
     with open(os.path.join(ROOT, "include", "csa.h")) as f:
         text = f.read()
-    names = set(re.findall(r"^\s*(?:[A-Za-z_][A-Za-z0-9_ ]*[\s*])?(csa_[a-z_]+)\(", text, flags=re.M))
-    names |= set(re.findall(r"\b(csa_[a-z_]+)\s*\(", text))
+    names = set(re.findall(r"^\s*(?:[A-Za-z_][A-Za-z0-9_ ]*[\s*])?(csa_[a-z0-9_]+)\(", text, flags=re.M))
+    names |= set(re.findall(r"\b(csa_[a-z0-9_]+)\s*\(", text))
     names = {n for n in names if not n.endswith("_t")}
-    assert {"csa_compress_insert", "csa_index_topk", "csa_attend", "csa_inv_rope", "csa_rope_table"} <= names
+    assert {"csa_compress_insert", "csa_index_topk", "csa_attend", "csa_inv_rope", "csa_rope_table",
+            "csa_inv_rope_quant_fp8"} <= names
     for n in sorted(names):
         assert hasattr(L, n), n
 
@@ -170,3 +171,19 @@ def test_inv_rope_and_table_validation(L):
     assert L.csa_rope_table(10, 64, -1.0, FAKE, None) == INVALID
     assert L.csa_rope_table(10, 64, 10000.0, None, None) == INVALID
     assert L.csa_rope_table(0, 64, 10000.0, None, None) == OK
+
+
+def test_inv_rope_quant_fp8_validation(L):
+    f = L.csa_inv_rope_quant_fp8
+    good = dict(n_q=2, h=4, dim=512, r=64, pos=FAKE, cs=FAKE, rows=10, x=FAKE, g=128, codes=FAKE, sc=FAKE)
+
+    def call(**kw):
+        a = {**good, **kw}
+        return f(a["n_q"], a["h"], a["dim"], a["r"], a["pos"], a["cs"], a["rows"], a["x"], a["g"], a["codes"],
+                 a["sc"], None)
+    for bad in (dict(dim=100), dict(dim=1024), dict(r=3), dict(r=1024), dict(g=4), dict(g=96), dict(g=1024),
+                dict(h=0), dict(h=129), dict(n_q=-1), dict(pos=None), dict(x=None), dict(codes=None), dict(sc=None),
+                dict(x=FAKE + 8), dict(codes=FAKE + 4), dict(rows=0), dict(cs=None)):
+        assert call(**bad) == INVALID, bad
+    assert call(dim=64, g=128) == INVALID          # group larger than the row
+    assert call(n_q=0, pos=None, x=None, codes=None, sc=None) == OK

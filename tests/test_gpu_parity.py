@@ -311,6 +311,31 @@ def test_inv_rope_parity():
     assert gu.rowwise_rel_err(t.cpu().numpy(), ref) <= 1e-6
 
 
+@pytest.mark.parametrize("heads,dim,rope,group", [(64, 512, 64, 128), (8, 128, 64, 32), (16, 512, 64, 512),
+                                                  (4, 256, 0, 64), (3, 64, 32, 8)])
+def test_inv_rope_quant_fp8_parity(heads, dim, rope, group):
+    """Inverse RoPE + fp8 output quantisation against the oracle: scales within 2^-14, each dequantised element
+    within one e4m3 step; an all-zero row stores zero codes with scale 1."""
+    _log(f"inv_rope_quant_fp8 H={heads} D={dim} R={rope} G={group}")
+    import synth
+    from oracle import output_quant as oq
+    pos = np.array([0, 1, 1000, 65536, 1 << 20, 7, 4095], np.int32)
+    g = synth.rng(91, dim + group)
+    x = synth.normal_f32(g, (len(pos), heads, dim)) * synth.uniform_f32(g, (len(pos), heads, 1), 0.01, 40.0)
+    x[5, 0] = 0.0
+    rows = (1 << 20) + 1
+    table = orope.rope_table(rows, rope if rope else 64)
+    ref_codes, ref_scales = oq.inv_rope_quant(x.astype(np.float64), pos, table, rope, group)
+    codes, scales = csa.inv_rope_quant_fp8(gu.dev_f32(x), gu.dev_i32(pos), rope, csa.rope_table(rows, rope if rope else 64),
+                                           group)
+    torch.cuda.synchronize()
+    codes, scales = codes.cpu().numpy(), scales.cpu().numpy()
+    frac = gu.assert_fp8_rows(codes.reshape(-1, group), scales.reshape(-1), ref_codes.reshape(-1, group),
+                              ref_scales.reshape(-1))
+    assert np.all(codes[5, 0] == 0) and np.all(scales[5, 0] == 1.0)
+    _log(f"identical codes {frac:.5f}")
+
+
 def test_attend_deterministic():
     _log("attend determinism")
     cfg = StepConfig(seed=51, ratio=4, lens=[5000, 3000], dim=512, rope_dims=64, heads=64, cache_dtype="bf16",
