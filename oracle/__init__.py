@@ -20,7 +20,7 @@ three source pages:
   (attention pruning), "工程实现" (engineering).
 
 Where the pages are silent the oracle takes the readings listed in the module
-docstrings (R1..R23 of the design notes); the GPU path takes the same ones.
+docstrings (R1..R24 of the design notes); the GPU path takes the same ones.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against closed forms, library routines (torch CPU casts, torch SDPA), brute
@@ -28,4 +28,4 @@ force in pure Python and invariants. Fidelity to the real DeepSeek-V4 model
 (logit semantics, RMSNorm epsilon, RoPE pairing, joint softmax, softmax scale)
 is a convention the pages do not fix: parity unpinned against the real model.
 """
-from . import codecs, paging, rope, compress, index, attend, memory_model, output_quant  # noqa: F401
+from . import codecs, paging, rope, compress, index, attend, memory_model, output_quant, prepare  # noqa: F401
