@@ -310,7 +310,29 @@ def run_gpu(args, lens):
     total_ms, mode, modes = best_graph_mode(torch, layers, args.steps, args.warmup, lambda ly: step(ly, None), fn)
     wall = time.time() - wall0
     epilogue = time_output_epilogue(torch, csa, layers, step, out, topk, max_elig, scale, rope_main, att_ws)
+    epilogue["upstream_prepare"] = time_prepare(torch, csa, layers[-1], rope_main)
     return total_ms, eager_ms, wall, stage_ms, copy_gbs, mode, modes, epilogue
+
+
+def time_prepare(torch, csa, ly, rope, iters=100):
+    """The fused step in front of this path (query RMSNorm + RoPE for 64 heads, window-key RoPE + insert) for the
+    batch's 32 decode tokens, timed alone (it rewrites the window row of each query position of this layer).
+    Algorithmic bytes: q read and written once (bf16), the key row read and its window row written."""
+    q_out = torch.empty_like(ly.q)
+    gamma = torch.ones(D, device="cuda")
+    for _ in range(5):
+        csa.prepare_qk(ly.q, ly.kv1, ly.seq, ly.pos, gamma, 1e-6, ly.swa, R, rope, q_out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        csa.prepare_qk(ly.q, ly.kv1, ly.seq, ly.pos, gamma, 1e-6, ly.swa, R, rope, q_out)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / iters
+    alg = 2 * ly.q.numel() * 2 + 2 * ly.kv1.numel() * 2 + D * 4
+    return {"kernel": "prepare_qk_kernel", "us": round(us, 2), "alg_bytes": alg, "gbs": round(alg / (us * 1e-6) / 1e9, 1),
+            "frac_peak": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def time_output_epilogue(torch, csa, layers, step, out, topk, max_elig, scale, rope, att_ws, group=128, iters=100):
@@ -780,6 +802,7 @@ def main():
                           "frac_peak": round(path_bytes / (path_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                           "alg_bytes": path_bytes, "us": round(path_ms * 1e3, 2)},
         "stages_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
+        "upstream_prepare": epilogue.pop("upstream_prepare"),
         "fp8_output_epilogue": epilogue,
         "copy_gbs": round(copy_gbs, 1),
         "wall_s_timed": round(wall, 3),

@@ -13,6 +13,7 @@
  *   csa_attend           (top-k entries + raw sliding window, or dense for c128a; optional fused inverse RoPE)
  *   csa_inv_rope         (standalone inverse RoPE, when not fused)
  *   csa_inv_rope_quant_fp8 (inverse RoPE fused with fp8 quantisation of the output, for an fp8 projection)
+ * and, upstream of the step, csa_prepare_qk (query norm + RoPE, window-key RoPE + insert).
  *
  * Conventions
  *   - Every pointer is DEVICE memory unless marked [host]. Every call is asynchronous on
@@ -201,6 +202,26 @@ csa_status_t csa_attend(const csa_cache_t* kv_cache, const csa_raw_t* swa, int32
 csa_status_t csa_inv_rope(int32_t n_q, int32_t n_heads, int32_t dim, int32_t rope_dims,
                           const int32_t* q_pos, const float* rope_cs, int32_t rope_rows, float* io,
                           hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * csa_prepare_qk -- query norm + query RoPE and window-key RoPE + window-key insert, fused.
+ * [P1] "GPU Compute Saturation" (kernel fusions) / [P2] "3.2 內核": the elementwise work on the query
+ * heads and on the uncompressed sliding-window key in front of the main attention runs as one
+ * horizontally fused kernel, each wavefront statically assigned to a query head or to the key.
+ * For every new token t (position tok_pos[t] < rope_rows of sequence tok_seq[t]):
+ *   q_out[t][h] = RoPE_p(RMSNorm(q_in[t][h]) * q_gamma), RMSNorm over the D channels of each head with
+ *     eps rms_eps and one weight vector q_gamma [D] for all heads, rounded once to q_dtype;
+ *   the window row of position p in `swa` (roles 0) = RoPE_p(kv_in[t]), rounded to the window pages'
+ *     type (fp8: code = e4m3_rne(y * 448/amax), scale = amax/448 per row, zeros and scale 1 for a zero row);
+ *     a position whose block is unmapped is skipped.
+ *   q_in, q_out [n_tok][n_heads][D] and kv_in [n_tok][D] in q_dtype; D = swa->dim. Type pairs:
+ *   (CSA_F32 q, CSA_F32 window) or (CSA_BF16 q, CSA_BF16 or CSA_FP8_E4M3 window). n_heads in [1, 128].
+ *   q_out must not alias q_in. Caller-owned buffers; nothing is allocated.
+ * ------------------------------------------------------------------------------------------- */
+csa_status_t csa_prepare_qk(int32_t n_tok, int32_t n_heads, const int32_t* tok_seq, const int32_t* tok_pos,
+                            const void* q_in, csa_dtype_t q_dtype, const float* q_gamma, float rms_eps,
+                            const void* kv_in, const csa_raw_t* swa, int32_t rope_dims,
+                            const float* rope_cs, int32_t rope_rows, void* q_out, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * csa_inv_rope_quant_fp8 -- inverse RoPE fused with fp8 quantisation of the attention output.

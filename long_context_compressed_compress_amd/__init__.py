@@ -70,6 +70,7 @@ def lib() -> ctypes.CDLL:
             "csa_inv_rope": (I32, [I32, I32, I32, I32, P, P, I32, P, P]),
             "csa_rope_table": (I32, [I32, I32, D, P, P]),
             "csa_inv_rope_quant_fp8": (I32, [I32, I32, I32, I32, P, P, I32, P, I32, P, P, P]),
+            "csa_prepare_qk": (I32, [I32, I32, P, P, P, I32, P, F, P, RP, I32, P, I32, P, P]),
             "csa_num_entries": (I64, [I64, I32, I32]),
             "csa_num_eligible": (I64, [I64, I32, I32]),
             "csa_entry_slot": (I64, [P, I64, I32]),
@@ -235,6 +236,21 @@ def inv_rope(io: torch.Tensor, q_pos: torch.Tensor, rope_dims: int, rope_cs: tor
     n_q, n_heads, dim = io.shape
     _check("csa_inv_rope", lib().csa_inv_rope(n_q, n_heads, dim, rope_dims, _ptr(q_pos), _ptr(rope_cs),
                                               rope_cs.shape[0], _ptr(io), _stream(stream)))
+
+
+def prepare_qk(q: torch.Tensor, kv: torch.Tensor, tok_seq: torch.Tensor, tok_pos: torch.Tensor, q_gamma: torch.Tensor,
+               rms_eps: float, swa: Raw, rope_dims: int, rope_cs: torch.Tensor, q_out: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    """Query norm + RoPE into q_out (same shape and dtype as q [n][H][D]); the window key of every token (kv [n][D],
+    RoPE'd at its position) is written into swa's pages. Returns q_out."""
+    n_tok, n_heads, _ = q.shape
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    sd = swa.desc()
+    _check("csa_prepare_qk", lib().csa_prepare_qk(
+        n_tok, n_heads, _ptr(tok_seq), _ptr(tok_pos), _ptr(q), dtype_code(q), _ptr(q_gamma), rms_eps, _ptr(kv),
+        ctypes.byref(sd), rope_dims, _ptr(rope_cs), rope_cs.shape[0], _ptr(q_out), _stream(stream)))
+    return q_out
 
 
 def inv_rope_quant_fp8(x: torch.Tensor, q_pos: torch.Tensor, rope_dims: int, rope_cs: torch.Tensor, group: int,

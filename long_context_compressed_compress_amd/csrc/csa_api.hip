@@ -236,6 +236,26 @@ csa_status_t csa_inv_rope_quant_fp8(int32_t n_q, int32_t n_heads, int32_t dim, i
                                                out_codes, out_scales, stream));
 }
 
+csa_status_t csa_prepare_qk(int32_t n_tok, int32_t n_heads, const int32_t* tok_seq, const int32_t* tok_pos,
+                            const void* q_in, csa_dtype_t q_dtype, const float* q_gamma, float rms_eps,
+                            const void* kv_in, const csa_raw_t* swa, int32_t rope_dims, const float* rope_cs,
+                            int32_t rope_rows, void* q_out, hipStream_t stream) {
+  if (n_tok < 0 || n_heads < 1 || n_heads > 128 || !swa || !valid_dim(swa->dim)) return CSA_ERR_INVALID_ARG;
+  if (!valid_raw_common(swa, swa->dim) || swa->roles != 0) return CSA_ERR_INVALID_ARG;
+  const bool combo = (q_dtype == CSA_F32 && swa->dtype == CSA_F32) ||
+                     (q_dtype == CSA_BF16 && (swa->dtype == CSA_BF16 || swa->dtype == CSA_FP8_E4M3));
+  if (!combo) return CSA_ERR_INVALID_ARG;
+  if (swa->dtype == CSA_FP8_E4M3 && !swa->scales) return CSA_ERR_INVALID_ARG;
+  if (rope_dims < 0 || rope_dims > swa->dim || (rope_dims & 1)) return CSA_ERR_INVALID_ARG;
+  if (rope_dims > 0 && (!rope_cs || rope_rows < 1)) return CSA_ERR_INVALID_ARG;
+  if (!(rms_eps >= 0.f) || !isfinite(rms_eps)) return CSA_ERR_INVALID_ARG;
+  if (n_tok == 0) return CSA_OK;
+  if (!tok_seq || !tok_pos || !q_in || !q_out || !q_gamma || !kv_in) return CSA_ERR_INVALID_ARG;
+  csa::PrepareArgs a{n_tok, n_heads, tok_seq, tok_pos, q_in, q_out, q_gamma, rms_eps, kv_in, *swa, rope_dims,
+                     rope_cs, rope_rows};
+  return hip_status(csa::launch_prepare_qk(a, q_dtype, stream));
+}
+
 csa_status_t csa_rope_table(int32_t rows, int32_t rope_dims, double theta, float* rope_cs, hipStream_t stream) {
   if (rows < 0 || rope_dims < 2 || (rope_dims & 1) || !(theta > 0.0) || !isfinite(theta)) return CSA_ERR_INVALID_ARG;
   if (rows > 0 && !rope_cs) return CSA_ERR_INVALID_ARG;

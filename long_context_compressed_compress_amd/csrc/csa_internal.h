@@ -170,6 +170,21 @@ hipError_t launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStre
 hipError_t launch_inv_rope(int n_q, int n_heads, int dim, int rope_dims, const int32_t* q_pos, const float* rope_cs,
                            int rope_rows, float* io, hipStream_t stream);
 hipError_t launch_rope_table(int rows, int rope_dims, double theta, float* out, hipStream_t stream);
+struct PrepareArgs {
+  int n_tok, n_heads;
+  const int32_t* tok_seq;
+  const int32_t* tok_pos;
+  const void* q_in;
+  void* q_out;
+  const float* gamma;
+  float eps;
+  const void* kv_in;
+  csa_raw_t swa;
+  int rope_dims;
+  const float* rope_cs;
+  int rope_rows;
+};
+hipError_t launch_prepare_qk(const PrepareArgs& a, csa_dtype_t q_dtype, hipStream_t stream);
 hipError_t launch_inv_rope_quant(int n_q, int n_heads, int dim, int rope_dims, const int32_t* q_pos,
                                  const float* rope_cs, int rope_rows, const float* in, int group, uint8_t* codes,
                                  float* scales, hipStream_t stream);

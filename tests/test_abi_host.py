@@ -187,3 +187,21 @@ def test_inv_rope_quant_fp8_validation(L):
         assert call(**bad) == INVALID, bad
     assert call(dim=64, g=128) == INVALID          # group larger than the row
     assert call(n_q=0, pos=None, x=None, codes=None, sc=None) == OK
+
+
+def test_prepare_qk_validation(L):
+    raw = _raw(dim=512, roles=0, dtype=csa.BF16)
+    f = L.csa_prepare_qk
+
+    def call(n=2, h=8, seq=FAKE, pos=FAKE, q=FAKE, qd=csa.BF16, g=FAKE, eps=1e-6, kv=FAKE, swa=raw, r=64, cs=FAKE,
+             rows=10, out=FAKE):
+        return f(n, h, seq, pos, q, qd, g, eps, kv, ctypes.byref(swa) if swa is not None else None, r, cs, rows, out,
+                 None)
+    for bad in (dict(h=0), dict(h=129), dict(n=-1), dict(seq=None), dict(q=None), dict(g=None), dict(kv=None),
+                dict(out=None), dict(swa=None), dict(qd=csa.F32), dict(r=3), dict(r=1024), dict(cs=None),
+                dict(rows=0), dict(eps=-1.0), dict(eps=float("nan"))):
+        assert call(**bad) == INVALID, bad
+    assert call(swa=_raw(dim=512, roles=2, dtype=csa.BF16)) == INVALID       # a state descriptor, not a window
+    assert call(swa=_raw(dim=100, roles=0, dtype=csa.BF16)) == INVALID
+    assert call(qd=csa.BF16, swa=_raw(dim=512, roles=0, dtype=csa.F32)) == INVALID
+    assert call(n=0, seq=None, pos=None, q=None, g=None, kv=None, out=None) == OK

@@ -336,6 +336,62 @@ def test_inv_rope_quant_fp8_parity(heads, dim, rope, group):
     _log(f"identical codes {frac:.5f}")
 
 
+@pytest.mark.parametrize("q_dtype,win_dtype,heads,dim,rope", [("bf16", "bf16", 64, 512, 64), ("bf16", "fp8", 64, 512, 64),
+                                                                ("f32", "f32", 8, 128, 64), ("bf16", "bf16", 4, 32, 16)])
+def test_prepare_qk_parity(q_dtype, win_dtype, heads, dim, rope):
+    """Query norm + RoPE and window-key RoPE + insert against the oracle: queries within one bf16 ulp (fp32: 1e-6
+    rowwise), written window rows within one storage step, every other row (and an unmapped block) untouched."""
+    _log(f"prepare_qk q={q_dtype} window={win_dtype} H={heads} D={dim} R={rope}")
+    import synth
+    from oracle import prepare as op
+    g = synth.rng(95, dim + heads)
+    positions = np.array([0, 255, 256, 131071, 131072, 77, 5000, 300], np.int32)
+    seqs = np.array([0, 0, 3, 2, 2, 3, 3, 1], np.int32)
+    nb = 131072 // 256 + 1
+    n_phys = 4 * nb
+    bt = synth.random_block_table(synth.rng(95, synth.STREAM_BT), 4, nb, n_phys)
+    bt[1, 300 // 256] = -1  # the last token's block is unmapped: it must be skipped
+    n = len(positions)
+    q = synth.normal_f32(g, (n, heads, dim)) * 3.0 if q_dtype == "f32" else synth.normal_bf16_bits(g, (n, heads, dim))
+    kv = synth.normal_f32(g, (n, dim)) if q_dtype == "f32" else synth.normal_bf16_bits(g, (n, dim))
+    gamma = synth.uniform_f32(g, (dim,), 0.5, 1.5)
+    pages = gu.canary((n_phys * 256, dim), win_dtype)
+    scales = np.full(n_phys * 256, np.nan, np.float32) if win_dtype == "fp8" else None
+    rows = 131073
+    table = orope.rope_table(rows, rope)
+    oswa = oc.Raw(win_dtype, dim, 0, pages.copy(), None, None if scales is None else scales.copy(), bt)
+    ref_q = op.prepare_qk(codecs.load_rows(q, q_dtype), q_dtype, codecs.load_rows(kv, q_dtype), seqs, positions, gamma,
+                          1e-6, table, rope, oswa)
+    gswa = csa.Raw(dim, 0, gu.dev_store(pages, win_dtype), gu.dev_i32(bt), None,
+                   gu.dev_f32(scales) if scales is not None else None)
+    qd = gu.dev_f32(q) if q_dtype == "f32" else gu.dev_bf16(q)
+    kd = gu.dev_f32(kv) if q_dtype == "f32" else gu.dev_bf16(kv)
+    out = csa.prepare_qk(qd, kd, gu.dev_i32(seqs), gu.dev_i32(positions), gu.dev_f32(gamma), 1e-6, gswa, rope,
+                         csa.rope_table(rows, rope))
+    torch.cuda.synchronize()
+    got_q = gu.host_store(out)
+    if q_dtype == "f32":
+        assert gu.rowwise_rel_err(got_q, ref_q) <= 1e-6
+    else:
+        gu.assert_bf16_rows(got_q.reshape(-1, dim), ref_q.reshape(-1, dim))
+    gp = gu.host_store(gswa.kv_pages)
+    written = np.zeros(gp.shape[0], bool)
+    for s_, p_ in zip(seqs, positions):
+        if bt[s_, p_ // 256] >= 0:
+            written[paging.raw_slot(bt[s_], int(p_))] = True
+    assert written.sum() == n - 1
+    if win_dtype == "fp8":
+        gs = gswa.scales.cpu().numpy()
+        gu.assert_fp8_rows(gp[written], gs[written], oswa.kv_pages[written], oswa.scales[written])
+        assert np.array_equal(gp[~written], pages[~written]) and np.all(np.isnan(gs[~written]))
+    elif win_dtype == "bf16":
+        gu.assert_bf16_rows(gp[written], oswa.kv_pages[written])
+        assert np.array_equal(gp[~written], pages[~written])
+    else:
+        assert gu.rowwise_rel_err(gp[written], oswa.kv_pages[written]) <= 1e-6
+        assert np.all(np.isnan(gp[~written]))
+
+
 def test_attend_deterministic():
     _log("attend determinism")
     cfg = StepConfig(seed=51, ratio=4, lens=[5000, 3000], dim=512, rope_dims=64, heads=64, cache_dtype="bf16",
