@@ -245,6 +245,167 @@ __global__ void __launch_bounds__(256, 2) score_mfma_kernel(IndexArgs a, Workspa
   flush_hist(hist_s, ws.hist + int64_t(q) * kHistBins);
 }
 
+// ------------------------------------------------------------------ MFMA score, pages shared by queries (prefill)
+// A prefill chunk has thousands of queries per sequence that all read the same pages, so a workgroup of
+// kShareQ waves takes kShareQ consecutive queries (one per wave) and stages every page of its run once
+// through LDS for all of them; kShareAhead pages stay in flight in registers while one is scored. Each wave
+// scores the page for its own query with score_page (the same arithmetic as score_mfma_kernel, so the
+// scores are identical). Queries of a workgroup that belong to different sequences are processed in
+// successive rounds, one sequence per round.
+constexpr int kShareQ = 8;
+constexpr int kShareThreads = 64 * kShareQ;
+constexpr int kShareAhead = 4;
+
+template <bool FP8>
+struct SharedPage {
+  static constexpr int ROW = FP8 ? 144 : 272;        // LDS bytes per page row (padded: rows start 4 banks apart)
+  static constexpr int CHUNKS = FP8 ? 512 : 1024;    // 16-byte chunks of one page in HBM
+  static constexpr int PER_T = CHUNKS / kShareThreads;  // chunks each thread copies
+  static constexpr int RAW_ROW = FP8 ? 128 : 256;    // bytes per page row in HBM
+};
+
+template <bool FP8, int HT>
+__global__ void __launch_bounds__(kShareThreads, 1) score_shared_kernel(IndexArgs a, Workspace ws) {
+  using L = SharedPage<FP8>;
+  constexpr int DIM = 128;
+  constexpr int E = 64;
+  // per-query histograms with two 16-bit bins per word (a workgroup counts at most kPagesPerBlock * 64 keys
+  // per query)
+  __shared__ uint32_t hist_s[kShareQ][kHistBins / 2];
+  __shared__ __attribute__((aligned(16))) char page_s[2][E * L::ROW];
+  __shared__ float scale_s[2][E];
+  __shared__ int32_t pg_phys[kPagesPerBlock];
+  __shared__ int32_t w_seq[kShareQ];
+  __shared__ int32_t w_npages[kShareQ];
+  __shared__ int32_t round_seq;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 15;
+  const int kg = lane >> 4;
+  const int H = HT * 16;
+  const int q = blockIdx.x * kShareQ + wave;
+  const bool q_ok = q < a.n_q;
+  int seq = -1;
+  const int64_t n_elig = q_ok ? query_elig(a, q, &seq) : 0;
+  const int64_t pg_begin = int64_t(blockIdx.y) * kPagesPerBlock;
+  const int64_t n_pages = (n_elig + E - 1) / E;
+  for (int b = tid; b < kShareQ * kHistBins / 2; b += kShareThreads) (&hist_s[0][0])[b] = 0u;
+  if (lane == 0) {
+    w_seq[wave] = (n_pages > pg_begin) ? seq : -1;  // -1: nothing of this run to score
+    w_npages[wave] = int32_t(min<int64_t>(n_pages, pg_begin + kPagesPerBlock));
+  }
+  // this wave's query operands and head weights (registers for the whole kernel)
+  bf16x8 qa[HT][4];
+  float wv[HT][4];
+  {
+    const int qq = q_ok ? q : 0;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + int64_t(qq) * H * DIM;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        qa[ht][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + (ht * 16 + col) * DIM + ks * 32 + kg * 8));
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wv[ht][i] = a.head_w[int64_t(qq) * H + ht * 16 + kg * 4 + i];
+  }
+  uint32_t* keys_q = ws.keys + int64_t(q_ok ? q : 0) * a.max_elig;
+  __syncthreads();
+
+  bool done = w_seq[wave] < 0;  // per wave; the round bookkeeping below is uniform over the workgroup
+  for (int round = 0; round < kShareQ; ++round) {
+    if (tid == 0) {
+      int rs = -1;
+      for (int w = kShareQ - 1; w >= 0; --w)
+        if (w_seq[w] >= 0) rs = w_seq[w];  // the first wave's sequence not done yet
+      round_seq = rs;
+    }
+    __syncthreads();
+    const int rseq = round_seq;
+    if (rseq < 0) break;  // uniform
+    const bool active = !done && w_seq[wave] == rseq;
+    int64_t run_end = pg_begin;
+    for (int w = 0; w < kShareQ; ++w)
+      if (w_seq[w] == rseq) run_end = max<int64_t>(run_end, w_npages[w]);
+    const int n_pg = int(run_end - pg_begin);
+    if (tid < kPagesPerBlock) {
+      const int64_t pg = pg_begin + tid;
+      const int32_t* bt = a.cache.block_table + int64_t(rseq) * a.cache.bt_stride;
+      const int32_t phys = (pg < run_end && pg < a.cache.bt_stride) ? bt[pg] : -1;
+      pg_phys[tid] = (phys >= 0 && phys < a.cache.n_phys) ? phys : -1;
+    }
+    __syncthreads();
+    // page i of the run -> registers: each thread copies PER_T 16-byte chunks (and fp8 threads < 64 one scale)
+    uint4 pre[kShareAhead][L::PER_T];
+    float pre_sc[kShareAhead];
+    auto fetch = [&](int i, uint4 (&dst)[L::PER_T], float& sc) {
+      const int ii = i < n_pg ? i : n_pg - 1;
+      const int32_t phys = pg_phys[ii];
+      const char* src = static_cast<const char*>(a.cache.pages) + int64_t(phys >= 0 ? phys : 0) * E * L::RAW_ROW;
+#pragma unroll
+      for (int c = 0; c < L::PER_T; ++c) dst[c] = *reinterpret_cast<const uint4*>(src + (tid + kShareThreads * c) * 16);
+      if (FP8) sc = tid < E ? a.cache.scales[int64_t(phys >= 0 ? phys : 0) * E + tid] : 0.f;
+    };
+#pragma unroll
+    for (int s = 0; s < kShareAhead; ++s) fetch(s, pre[s], pre_sc[s]);
+    for (int i0 = 0; i0 < n_pg; i0 += kShareAhead) {
+#pragma unroll
+      for (int s = 0; s < kShareAhead; ++s) {
+        const int i = i0 + s;
+        if (i < n_pg) {  // uniform
+          char* buf = page_s[i & 1];
+#pragma unroll
+          for (int c = 0; c < L::PER_T; ++c) {
+            const int chunk = tid + kShareThreads * c;
+            const int row = chunk / (L::RAW_ROW / 16), off = (chunk % (L::RAW_ROW / 16)) * 16;
+            *reinterpret_cast<uint4*>(buf + row * L::ROW + off) = pre[s][c];
+          }
+          if (FP8 && tid < E) scale_s[i & 1][tid] = pre_sc[s];
+          fetch(i + kShareAhead, pre[s], pre_sc[s]);
+          lds_barrier();
+          const int64_t pg = pg_begin + i;
+          if (active && pg < w_npages[wave]) {
+            PageBuf<FP8> b;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const char* rowp = buf + (u * 16 + col) * L::ROW;
+#pragma unroll
+              for (int ks = 0; ks < 4; ++ks) {
+                if (FP8) reinterpret_cast<PageBuf<true>&>(b).v[u][ks] = *reinterpret_cast<const uint2*>(rowp + ks * 32 + kg * 8);
+                else reinterpret_cast<PageBuf<false>&>(b).v[u][ks] = *reinterpret_cast<const uint4*>(rowp + ks * 64 + kg * 16);
+              }
+              if (FP8) reinterpret_cast<PageBuf<true>&>(b).sc[u] = scale_s[i & 1][u * 16 + col];
+            }
+            const uint32_t key = score_page<FP8, HT>(b, qa, wv, kg);
+            const int64_t e = pg * E + lane;
+            if (e < n_elig) {
+              const uint32_t k2 = pg_phys[i] >= 0 ? key : 0u;
+              keys_q[e] = k2;
+              const uint32_t bin = k2 >> (32 - kHistBits);
+              atomicAdd(&hist_s[wave][bin >> 1], 1u << ((bin & 1u) * 16));
+            }
+          }
+        }
+      }
+    }
+    if (active) done = true;
+    __syncthreads();
+    if (lane == 0 && active) w_seq[wave] = -1;
+    __syncthreads();
+  }
+  if (q_ok) {
+    uint32_t* hq = ws.hist + int64_t(q) * kHistBins;
+    for (int b = lane; b < kHistBins / 2; b += 64) {
+      const uint32_t v = hist_s[wave][b];
+      if (v & 0xFFFFu) atomicAdd(hq + 2 * b, v & 0xFFFFu);
+      if (v >> 16) atomicAdd(hq + 2 * b + 1, v >> 16);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ VALU score (any head count / dim / dtype)
 template <int DT>  // 0 f32, 1 bf16, 2 fp8
 __global__ void __launch_bounds__(256) score_valu_kernel(IndexArgs a, Workspace ws) {
@@ -739,6 +900,21 @@ hipError_t launch_index_score(const IndexArgs& a, hipStream_t stream) {
   if (mfma) {
     const int64_t max_pages = (a.max_elig + 63) / 64;
     const int64_t runs = (max_pages + kPagesPerBlock - 1) / kPagesPerBlock;
+    const bool fp8s = a.cache.dtype == CSA_FP8_E4M3;
+    if (a.n_q >= kQueryFastMin && runs <= 65535) {  // many queries per launch: pages shared through LDS
+      const dim3 g2(unsigned((a.n_q + kShareQ - 1) / kShareQ), unsigned(runs));
+      switch (a.n_heads / 16) {
+        case 1: if (fp8s) hipLaunchKernelGGL((score_shared_kernel<true, 1>), g2, dim3(kShareThreads), 0, stream, a, ws);
+                else hipLaunchKernelGGL((score_shared_kernel<false, 1>), g2, dim3(kShareThreads), 0, stream, a, ws); break;
+        case 2: if (fp8s) hipLaunchKernelGGL((score_shared_kernel<true, 2>), g2, dim3(kShareThreads), 0, stream, a, ws);
+                else hipLaunchKernelGGL((score_shared_kernel<false, 2>), g2, dim3(kShareThreads), 0, stream, a, ws); break;
+        case 3: if (fp8s) hipLaunchKernelGGL((score_shared_kernel<true, 3>), g2, dim3(kShareThreads), 0, stream, a, ws);
+                else hipLaunchKernelGGL((score_shared_kernel<false, 3>), g2, dim3(kShareThreads), 0, stream, a, ws); break;
+        default: if (fp8s) hipLaunchKernelGGL((score_shared_kernel<true, 4>), g2, dim3(kShareThreads), 0, stream, a, ws);
+                 else hipLaunchKernelGGL((score_shared_kernel<false, 4>), g2, dim3(kShareThreads), 0, stream, a, ws); break;
+      }
+      return hipGetLastError();
+    }
     const int qf = (a.n_q >= kQueryFastMin && runs <= 65535) ? 1 : 0;
     const dim3 grid = qf ? dim3(unsigned(a.n_q), unsigned(runs)) : dim3(unsigned(runs), unsigned(a.n_q));
     const bool fp8 = a.cache.dtype == CSA_FP8_E4M3;
