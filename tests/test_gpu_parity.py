@@ -138,8 +138,11 @@ INDEX_GRID_CASES = [
     ("fp8", 2, 32, oi.WRELU, 1, [4000, 10]),
     # more than 2^18 eligible entries: the chosen-entry bitmap lives in the workspace, not in LDS
     ("bf16", 16, 128, oi.WRELU, 512, [1200000, 40000]),
-    # many queries in one launch: the score grid walks queries first
+    # many queries in one launch: pages shared by the queries of a workgroup (one sequence per query here, so
+    # every workgroup runs one round per query), bf16 and fp8 pages, 64 and 16 heads
     ("bf16", 64, 128, oi.WRELU, 512, [300 + 13 * i for i in range(300)]),
+    ("fp8", 64, 128, oi.WRELU, 512, [700 + 29 * i for i in range(288)]),
+    ("bf16", 16, 128, oi.WRELU, 100, [5000 - 17 * i for i in range(260)]),
 ]
 
 
