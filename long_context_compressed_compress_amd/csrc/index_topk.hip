@@ -264,6 +264,23 @@ struct SharedPage {
   static constexpr int RAW_ROW = FP8 ? 128 : 256;    // bytes per page row in HBM
 };
 
+// Page i of the run (clamped to the last one) -> this thread's 16-byte chunks (and, fp8, scale `tid` of the page).
+// A forced-inline function, so the caller's register arrays are never address-taken (a lambda called this way
+// was left out of line and its arrays went to scratch memory).
+template <bool FP8>
+__device__ __forceinline__ void fetch_shared_page(const IndexArgs& a, const int32_t* pg_phys, int i, int n_pg, int tid,
+                                                  uint4& c0, uint4& c1, float& sc) {
+  using L = SharedPage<FP8>;
+  static_assert(L::PER_T == 1 || L::PER_T == 2, "one or two chunks per thread");
+  const int ii = i < n_pg ? i : n_pg - 1;
+  const int32_t phys = pg_phys[ii];
+  const int64_t page = phys >= 0 ? phys : 0;
+  const char* src = static_cast<const char*>(a.cache.pages) + page * 64 * L::RAW_ROW;
+  c0 = *reinterpret_cast<const uint4*>(src + tid * 16);
+  if (L::PER_T == 2) c1 = *reinterpret_cast<const uint4*>(src + (tid + kShareThreads) * 16);
+  if (FP8) sc = tid < 64 ? a.cache.scales[page * 64 + tid] : 0.f;
+}
+
 template <bool FP8, int HT>
 __global__ void __launch_bounds__(kShareThreads, 1) score_shared_kernel(IndexArgs a, Workspace ws) {
   using L = SharedPage<FP8>;
@@ -339,18 +356,10 @@ __global__ void __launch_bounds__(kShareThreads, 1) score_shared_kernel(IndexArg
     }
     __syncthreads();
     // page i of the run -> registers: each thread copies PER_T 16-byte chunks (and fp8 threads < 64 one scale)
-    uint4 pre[kShareAhead][L::PER_T];
-    float pre_sc[kShareAhead];
-    auto fetch = [&](int i, uint4 (&dst)[L::PER_T], float& sc) {
-      const int ii = i < n_pg ? i : n_pg - 1;
-      const int32_t phys = pg_phys[ii];
-      const char* src = static_cast<const char*>(a.cache.pages) + int64_t(phys >= 0 ? phys : 0) * E * L::RAW_ROW;
+    uint4 pre0[kShareAhead], pre1[kShareAhead];  // this thread's first and second chunk of each page in flight
+    float pre_sc[kShareAhead] = {};
 #pragma unroll
-      for (int c = 0; c < L::PER_T; ++c) dst[c] = *reinterpret_cast<const uint4*>(src + (tid + kShareThreads * c) * 16);
-      if (FP8) sc = tid < E ? a.cache.scales[int64_t(phys >= 0 ? phys : 0) * E + tid] : 0.f;
-    };
-#pragma unroll
-    for (int s = 0; s < kShareAhead; ++s) fetch(s, pre[s], pre_sc[s]);
+    for (int s = 0; s < kShareAhead; ++s) fetch_shared_page<FP8>(a, pg_phys, s, n_pg, tid, pre0[s], pre1[s], pre_sc[s]);
     for (int i0 = 0; i0 < n_pg; i0 += kShareAhead) {
 #pragma unroll
       for (int s = 0; s < kShareAhead; ++s) {
@@ -361,10 +370,10 @@ __global__ void __launch_bounds__(kShareThreads, 1) score_shared_kernel(IndexArg
           for (int c = 0; c < L::PER_T; ++c) {
             const int chunk = tid + kShareThreads * c;
             const int row = chunk / (L::RAW_ROW / 16), off = (chunk % (L::RAW_ROW / 16)) * 16;
-            *reinterpret_cast<uint4*>(buf + row * L::ROW + off) = pre[s][c];
+            *reinterpret_cast<uint4*>(buf + row * L::ROW + off) = c == 0 ? pre0[s] : pre1[s];
           }
           if (FP8 && tid < E) scale_s[i & 1][tid] = pre_sc[s];
-          fetch(i + kShareAhead, pre[s], pre_sc[s]);
+          fetch_shared_page<FP8>(a, pg_phys, i + kShareAhead, n_pg, tid, pre0[s], pre1[s], pre_sc[s]);
           lds_barrier();
           const int64_t pg = pg_begin + i;
           if (active && pg < w_npages[wave]) {
