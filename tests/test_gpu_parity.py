@@ -303,6 +303,44 @@ def test_attend_parity(ratio, dim, heads, dtype, k, positions):
     assert gu.rowwise_rel_err(out2.cpu().numpy(), out.cpu().numpy()) <= 1e-6
 
 
+@pytest.mark.parametrize("heads,k,window,dtype,positions", [(128, 512, 128, "bf16", [9000, 3001, 700]),
+                                                             (64, 2048, 1024, "bf16", [12000, 9500]),
+                                                             (64, 2048, 1024, "fp8", [12000]),
+                                                             (128, 0, 1024, "bf16", [70000, 1100])])
+def test_attend_maximum_sizes(heads, k, window, dtype, positions):
+    """The largest shapes the ABI takes: 128 heads (two 64-head chunks per query), top-2048 plus a 1024-row window
+    (the key-row table exactly full), and dense c128a with a 1024-row window."""
+    _log(f"attend max heads={heads} k={k} window={window} dtype={dtype} pos={positions}")
+    import synth
+    ratio = 4 if k else 128
+    dim, R = 512, 64
+    cfg = 77 + heads + k + window
+    pc = si.paged_cache(cfg, ratio, dim, dtype, positions)
+    n_phys = pc.bt.max() + 1 + 3
+    swa_pages, swa_sc = si.window_rows(cfg, dim, dtype, n_phys)
+    q = synth.normal_bf16_bits(synth.rng(cfg, synth.STREAM_Q), (len(positions), heads, dim))
+    tk = si.topk_lists(cfg, positions, ratio, k) if k else None
+    rows = max(positions) + 1
+    scale = float(1.0 / np.sqrt(dim))
+    o_out, o_lse = oa.attend(pc.oracle(R), oc.Raw(dtype, dim, 0, swa_pages, None, swa_sc, pc.bt), window,
+                             np.arange(len(positions)), positions, codecs.load_rows(q, "bf16"), tk, scale, True,
+                             orope.rope_table(rows, R))
+    gcache = csa.Cache(ratio, pc.window, dim, R, gu.dev_store(pc.pages, dtype), gu.dev_i32(pc.bt),
+                       gu.dev_f32(pc.scales) if pc.scales is not None else None)
+    gswa = csa.Raw(dim, 0, gu.dev_store(swa_pages, dtype), gu.dev_i32(pc.bt), None,
+                   gu.dev_f32(swa_sc) if swa_sc is not None else None)
+    max_elig = max(paging.num_eligible(p, ratio, pc.window) for p in positions)
+    out = torch.full((len(positions), heads, dim), -7.0, device="cuda")
+    lse = torch.full((len(positions), heads), -7.0, device="cuda")
+    csa.attend(gcache, gswa, window, gu.dev_i32(np.arange(len(positions))), gu.dev_i32(positions), gu.dev_bf16(q),
+               gu.dev_i32(tk) if tk is not None else None, max_elig, scale, True, csa.rope_table(rows, R), out, lse)
+    torch.cuda.synchronize()
+    err = gu.rowwise_rel_err(out.cpu().numpy(), o_out)
+    _log(f"rowwise rel err {err:.3e}")
+    assert err <= TOL[dtype]
+    assert np.allclose(lse.cpu().numpy(), o_lse, rtol=0, atol=1e-4)
+
+
 def test_inv_rope_parity():
     _log("inv_rope")
     import synth
