@@ -131,7 +131,9 @@ class Layer:
 
 
 def algorithmic_bytes(lens):
-    """Bytes the method must move per step (SURVEY-style accounting)."""
+    """Bytes the method must move per step: every eligible indexer key once, q_idx and head weights per query; the
+    top-k indices; the selected entries and window rows once, q and the fp32 output per query; the decode-step
+    compression's raw rows and new entries."""
     from long_context_compressed_compress_amd import num_eligible
     score = sel = att = comp = 0
     for L in lens:
@@ -758,7 +760,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this path runs per GPU with no exchange (sequences shard by data "
-              f"parallelism), and multi-GPU runs are not part of this build; got --gpus {args.gpus}.", file=sys.stderr)
+              f"parallelism), and multi-GPU runs are not measured here; got --gpus {args.gpus}.", file=sys.stderr)
         sys.exit(2)
     global EAGER_ONLY
     EAGER_ONLY = args.eager_only

@@ -20,7 +20,7 @@ three source pages:
   (attention pruning), "工程实现" (engineering).
 
 Where the pages are silent the oracle takes the readings listed in the module
-docstrings (R1..R24 of the design notes); the GPU path takes the same ones.
+docstrings (labelled R1..R24); the GPU path takes the same ones.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against closed forms, library routines (torch CPU casts, torch SDPA), brute

@@ -3,7 +3,7 @@
 Cache element types come from the pages: bf16 caches for prefill and a
 token-wise fp8 attention cache for decode ([P2] "二、注意力機制為什么這么麻煩";
 [P1] "Deployment and Hardware Support" names the fp8 KV cache). The per-entry
-fp8 scale rule is the reading O7 of the design notes (amax / 448 per entry).
+fp8 scale rule is a reading (R20): amax / 448 per entry.
 
 bf16 and e4m3fn are written from their format definitions:
 * bf16: 1 sign, 8 exponent (bias 127), 7 mantissa bits -> the top half of fp32.
@@ -92,7 +92,7 @@ def f64_to_e4m3(x) -> np.ndarray:
     return code.astype(np.uint8)
 
 
-# ---------------------------------------------------------------- entry store (reading O7)
+# ---------------------------------------------------------------- entry store (reading R20)
 def store_row(y: np.ndarray, dtype: str):
     """Round one fp64 row to the cache element type.
 

@@ -4,7 +4,7 @@ Source: [P1] "GPU Compute Saturation" (kernel fusions) and [P2] "3.2 內核": af
 output goes through the inverse RoPE and then into the fp8 batched matmul of the o_lora projection; the
 two steps are fused so the output makes one trip through HBM instead of two.
 
-The pages do not say how the output is quantised for that matmul. Reading (R23 of the design notes): each
+The pages do not say how the output is quantised for that matmul. Reading R23: each
 (query, head) output row of D channels is cut into consecutive groups of G channels; every group is stored
 as OCP e4m3fn codes with one fp32 scale, by the same per-row rule as the fp8 caches (reading R20):
 y32 = fl32(y), amax = max|y32|, code = e4m3(fl32(y32 * fl32(448 / amax))), scale = fl32(amax / 448); an

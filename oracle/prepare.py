@@ -4,7 +4,7 @@ Source: [P1] "GPU Compute Saturation" and [P2] "3.2 內核": the elementwise wor
 uncompressed sliding-window key in front of the main attention is one horizontally fused step (some waves
 take query heads, others the key; no communication between them).
 
-Readings (the pages name the steps, not their formulas) -- R24 of the design notes:
+Readings (the pages name the steps, not their formulas), labelled R24:
 * query norm is an RMSNorm of each head's D channels with one weight vector gamma_q [D] shared by the heads and
   eps an input (the compressor's RMSNorm rule, R6), then RoPE at the token's position on the last R dims
   (R7/R8), rounded once to the query's element type;
