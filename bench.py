@@ -8,7 +8,7 @@ score = sum_h w_h ReLU(q_h . k); top-512 compressed entries + 128-token raw wind
 256-position blocks at random physical pages. Inputs are synthetic (seeded), resident in HBM.
 
 A step is one pass of the whole path for the batch: compress_insert of the decode token into the main
-and the indexer cache, index score, top-k select, attention with fused inverse RoPE. Steps rotate over
+and the indexer cache (one paired call), index score, top-k select, attention with fused inverse RoPE. Steps rotate over
 --layers independently built layer caches (placed at random in their own pools) so repeated steps do
 not run out of the 256 MB Infinity Cache.
 
@@ -253,8 +253,8 @@ def run_gpu(args, lens):
 
     def step(ly, ev=None):
         if ev: ev[0].record()
-        csa.compress_insert(ly.cache, ly.state, ly.pos, ly.cu1, ly.kv1, ly.lg1, ly.gamma, 1e-6, rope_main, 1)
-        csa.compress_insert(ly.icache, ly.istate, ly.pos, ly.cu1, ly.ikv1, ly.ilg1, ly.igamma, 1e-6, rope_idx, 1)
+        csa.compress_insert_pair(ly.cache, ly.state, ly.kv1, ly.lg1, ly.gamma, rope_main, ly.icache, ly.istate, ly.ikv1,
+                                 ly.ilg1, ly.igamma, rope_idx, ly.pos, ly.cu1, 1e-6, 1)
         if ev: ev[1].record()
         csa.index_score(ly.icache, ly.seq, ly.pos, max_elig, ly.q_idx, ly.head_w, csa.SCORE_WRELU, K_TOP, ws)
         if ev: ev[2].record()
@@ -469,8 +469,8 @@ def run_c4(args, torch, csa):
 
     def step(ly, ev):
         if ev: ev[0].record()
-        csa.compress_insert(ly.cache, ly.state, ly.pos, ly.cu1, ly.kv1, ly.lg1, ly.gamma, 1e-6, rope, 1)
-        csa.compress_insert(ly.icache, ly.istate, ly.pos, ly.cu1, ly.ikv1, ly.ilg1, ly.igamma, 1e-6, rope, 1)
+        csa.compress_insert_pair(ly.cache, ly.state, ly.kv1, ly.lg1, ly.gamma, rope, ly.icache, ly.istate, ly.ikv1,
+                                 ly.ilg1, ly.igamma, rope, ly.pos, ly.cu1, 1e-6, 1)
         if ev: ev[1].record()
         csa.index_score(ly.icache, ly.seq, ly.pos, max_elig, ly.q_idx, ly.head_w, csa.SCORE_WRELU, K_TOP, ws)
         if ev: ev[2].record()
@@ -644,8 +644,8 @@ def run_c5(args, torch, csa):
 
     def step(ly, ev):
         if ev: ev[0].record()
-        csa.compress_insert(ly.cache, ly.state, start, cu, ly.kv, ly.lg, g1, 1e-6, rope, CH)
-        csa.compress_insert(ly.icache, ly.istate, start, cu, ly.ikv, ly.ilg, gi, 1e-6, rope, CH)
+        csa.compress_insert_pair(ly.cache, ly.state, ly.kv, ly.lg, g1, rope, ly.icache, ly.istate, ly.ikv, ly.ilg, gi,
+                                 rope, start, cu, 1e-6, CH)
         csa.compress_insert(ly.hcache, ly.hstate, start, cu, ly.hkv, ly.hlg, g1, 1e-6, rope, CH)
         if ev: ev[1].record()
         csa.index_score(ly.icache, q_seq, q_pos, max_elig, ly.q_idx, ly.head_w, csa.SCORE_WRELU, K_TOP, ws)

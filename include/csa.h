@@ -123,6 +123,24 @@ csa_status_t csa_compress_insert(const csa_cache_t* cache, const csa_raw_t* stat
                                  int32_t* out_new_entries, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * csa_compress_insert_pair -- csa_compress_insert of two caches that take the same new tokens (a c4a
+ * layer's main cache a and indexer cache b: [P2] "3.2 內核" keeps one compressor instance per cache) in one
+ * call. Each cache's arguments mean what they mean for csa_compress_insert (kv_a / logit_a / gamma_a /
+ * rope_cs_a belong to cache_a, and so on); batch, start_pos, cu_new, total_new, max_new_per_seq and rms_eps
+ * are shared; no slot or count outputs. Results are those of the two separate calls. A c4a bf16 / fp8 main
+ * cache of dim 512 with an indexer cache of dim 128 and bf16 inputs runs as one kernel launch whose blocks
+ * each work for one of the two caches (each with its own per-dim code); any other pair runs as two launches.
+ * Validation: both argument sets as for csa_compress_insert, before any HIP call.
+ * ------------------------------------------------------------------------------------------- */
+csa_status_t csa_compress_insert_pair(const csa_cache_t* cache_a, const csa_raw_t* state_a, const void* kv_a,
+                                      const void* logit_a, const float* gamma_a, const float* rope_cs_a,
+                                      int32_t rope_rows_a, const csa_cache_t* cache_b, const csa_raw_t* state_b,
+                                      const void* kv_b, const void* logit_b, const float* gamma_b,
+                                      const float* rope_cs_b, int32_t rope_rows_b, int32_t batch,
+                                      const int32_t* start_pos, const int32_t* cu_new, int32_t total_new,
+                                      int32_t max_new_per_seq, float rms_eps, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * csa_index_topk -- indexer score over eligible entries and top-k selection (c4a layers).
  * [P1] architecture section / [P2] "二、注意力機制為什么這么麻煩": DeepSeek Sparse Attention keeps the
  * top-k compressed entries (k = 512 on c4a). [P2] "3.2 內核": the indexer pipeline has its own

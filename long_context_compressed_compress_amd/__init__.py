@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
         CP, RP = ctypes.POINTER(CacheDesc), ctypes.POINTER(RawDesc)
         sig = {
             "csa_compress_insert": (I32, [CP, RP, I32, P, P, I32, I32, P, P, P, F, P, I32, P, I32, P, P]),
+            "csa_compress_insert_pair": (I32, [CP, RP, P, P, P, P, I32, CP, RP, P, P, P, P, I32, I32, P, P, I32, I32, F,
+                                               P]),
             "csa_index_topk_workspace": (SZ, [I32, I64, I32, I32]),
             "csa_index_topk": (I32, [CP, I32, P, P, I64, P, I32, I32, P, I32, I32, P, P, P, P, SZ, P]),
             "csa_index_workspace_clear": (I32, [P, SZ, I32, P]),
@@ -164,6 +166,19 @@ def compress_insert(cache: Cache, state: Raw, start_pos: torch.Tensor, cu_new: t
         ctypes.byref(cd), ctypes.byref(sd), batch, _ptr(start_pos), _ptr(cu_new), kv_new.shape[0], max_new_per_seq,
         _ptr(kv_new), _ptr(logit_new), _ptr(gamma), rms_eps, _ptr(rope_cs), rope_cs.shape[0],
         _ptr(out_slots), 0 if out_slots is None else out_slots.shape[1], _ptr(out_new_entries), _stream(stream)))
+
+
+def compress_insert_pair(cache_a: Cache, state_a: Raw, kv_a: torch.Tensor, logit_a: torch.Tensor,
+                         gamma_a: torch.Tensor, rope_a: torch.Tensor, cache_b: Cache, state_b: Raw,
+                         kv_b: torch.Tensor, logit_b: torch.Tensor, gamma_b: torch.Tensor, rope_b: torch.Tensor,
+                         start_pos: torch.Tensor, cu_new: torch.Tensor, rms_eps: float, max_new_per_seq: int,
+                         stream=None) -> None:
+    """compress_insert of two caches taking the same new tokens (main + indexer of a c4a layer) in one call."""
+    ca, sa, cb, sb = cache_a.desc(), state_a.desc(), cache_b.desc(), state_b.desc()
+    _check("csa_compress_insert_pair", lib().csa_compress_insert_pair(
+        ctypes.byref(ca), ctypes.byref(sa), _ptr(kv_a), _ptr(logit_a), _ptr(gamma_a), _ptr(rope_a), rope_a.shape[0],
+        ctypes.byref(cb), ctypes.byref(sb), _ptr(kv_b), _ptr(logit_b), _ptr(gamma_b), _ptr(rope_b), rope_b.shape[0],
+        start_pos.shape[0], _ptr(start_pos), _ptr(cu_new), kv_a.shape[0], max_new_per_seq, rms_eps, _stream(stream)))
 
 
 def index_topk_workspace(n_q: int, max_elig: int, k: int, n_heads: int) -> int:

@@ -63,8 +63,9 @@ __device__ __forceinline__ int find_seq(const int32_t* cu, int batch, int row) {
   return found;
 }
 
+// The work of one 256-thread block of a compress_insert grid (block = its index within that grid).
 template <typename TIn, int OUT, int D, int RATIO, int WINDOW>
-__global__ void __launch_bounds__(256) compress_insert_kernel(CompressArgs a) {
+__device__ __forceinline__ void compress_insert_body(const CompressArgs& a, int64_t block) {
   constexpr int ROLES = WINDOW / RATIO;
   constexpr int VEC = 16 / int(sizeof(TIn));
   constexpr int CH = (D / 64 > VEC) ? D / 64 : VEC;
@@ -74,7 +75,7 @@ __global__ void __launch_bounds__(256) compress_insert_kernel(CompressArgs a) {
   static_assert(D % CH == 0 && NLC <= 64 && (NLC & (NLC - 1)) == 0, "channel split");
 
   const int lane = threadIdx.x & 63;
-  const int64_t gw = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t gw = block * 4 + (threadIdx.x >> 6);
   const int64_t n_append = a.total_new;
   const TIn* kv_new = reinterpret_cast<const TIn*>(a.kv_new);
   const TIn* lg_new = reinterpret_cast<const TIn*>(a.logit_new);
@@ -274,6 +275,24 @@ __global__ void __launch_bounds__(256) compress_insert_kernel(CompressArgs a) {
     a.out_slots[int64_t(b) * a.max_entries_out + c_idx] = in_table ? int32_t(slot) : -1;
 }
 
+template <typename TIn, int OUT, int D, int RATIO, int WINDOW>
+__global__ void __launch_bounds__(256) compress_insert_kernel(CompressArgs a) {
+  compress_insert_body<TIn, OUT, D, RATIO, WINDOW>(a, blockIdx.x);
+}
+
+// Two c4a caches' compress_insert in one grid (a decode step's main and indexer caches): blocks [0, blocks_a)
+// run cache a's code for head dim DA, the rest cache b's for DB. Each cache keeps its own per-dim code, the
+// step saves one launch.
+template <typename TIn, int OUT, int DA, int DB>
+__global__ void __launch_bounds__(256) compress_pair_kernel(CompressArgs a, CompressArgs b, int64_t blocks_a) {
+  if (int64_t(blockIdx.x) < blocks_a) compress_insert_body<TIn, OUT, DA, 4, 8>(a, blockIdx.x);
+  else compress_insert_body<TIn, OUT, DB, 4, 8>(b, int64_t(blockIdx.x) - blocks_a);
+}
+
+inline int64_t compress_blocks(const CompressArgs& a) {
+  return (int64_t(a.total_new) + int64_t(a.batch) * a.max_entries_bound + 3) / 4;
+}
+
 template <typename TIn, int OUT, int D>
 hipError_t dispatch_ratio(const CompressArgs& a, hipStream_t stream) {
   const int64_t units = int64_t(a.total_new) + int64_t(a.batch) * a.max_entries_bound;
@@ -314,6 +333,26 @@ hipError_t dispatch_out(const CompressArgs& a, hipStream_t stream) {
 hipError_t launch_compress(const CompressArgs& a, hipStream_t stream) {
   if (a.state.dtype == CSA_F32) return dispatch_out<float>(a, stream);
   return dispatch_out<uint16_t>(a, stream);
+}
+
+hipError_t launch_compress_pair(const CompressArgs& a, const CompressArgs& b, hipStream_t stream) {
+  const bool fused = a.state.dtype == CSA_BF16 && b.state.dtype == CSA_BF16 && a.cache.ratio == 4 &&
+                     b.cache.ratio == 4 && a.cache.dtype == b.cache.dtype &&
+                     (a.cache.dtype == CSA_BF16 || a.cache.dtype == CSA_FP8_E4M3) && a.cache.dim == 512 &&
+                     b.cache.dim == 128;
+  if (!fused) {  // any other pair: one launch per cache
+    const hipError_t e = launch_compress(a, stream);
+    return e != hipSuccess ? e : launch_compress(b, stream);
+  }
+  const int64_t ba = compress_blocks(a), bb = compress_blocks(b);
+  if (ba + bb == 0) return hipSuccess;
+  if (ba + bb > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid(unsigned(ba + bb));
+  if (a.cache.dtype == CSA_BF16)
+    hipLaunchKernelGGL((compress_pair_kernel<uint16_t, 1, 512, 128>), grid, dim3(256), 0, stream, a, b, ba);
+  else
+    hipLaunchKernelGGL((compress_pair_kernel<uint16_t, 2, 512, 128>), grid, dim3(256), 0, stream, a, b, ba);
+  return hipGetLastError();
 }
 
 }  // namespace csa

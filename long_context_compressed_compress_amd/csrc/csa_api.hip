@@ -74,12 +74,16 @@ int64_t csa_raw_slot(const int32_t* bt_row, int64_t pos) {
   return int64_t(bt_row[pos / csa::kBlock]) * csa::kBlock + pos % csa::kBlock;
 }
 
-csa_status_t csa_compress_insert(const csa_cache_t* cache, const csa_raw_t* state, int32_t batch,
-                                 const int32_t* start_pos, const int32_t* cu_new, int32_t total_new,
-                                 int32_t max_new_per_seq, const void* kv_new, const void* logit_new,
-                                 const float* gamma, float rms_eps, const float* rope_cs, int32_t rope_rows,
-                                 int32_t* out_slots, int32_t max_entries_out, int32_t* out_new_entries,
-                                 hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Host validation of one compress_insert (every check made before any HIP call); fills *out on CSA_OK.
+csa_status_t compress_args(const csa_cache_t* cache, const csa_raw_t* state, int32_t batch, const int32_t* start_pos,
+                           const int32_t* cu_new, int32_t total_new, int32_t max_new_per_seq, const void* kv_new,
+                           const void* logit_new, const float* gamma, float rms_eps, const float* rope_cs,
+                           int32_t rope_rows, int32_t* out_slots, int32_t max_entries_out, int32_t* out_new_entries,
+                           csa::CompressArgs* out) {
   if (!valid_cache(cache) || !valid_raw_common(state, cache ? cache->dim : -1)) return CSA_ERR_INVALID_ARG;
   if (state->dtype != CSA_F32 && state->dtype != CSA_BF16) return CSA_ERR_INVALID_ARG;
   if (state->roles != cache->window / cache->ratio || !state->logit_pages || !aligned(state->logit_pages, 16))
@@ -92,11 +96,45 @@ csa_status_t csa_compress_insert(const csa_cache_t* cache, const csa_raw_t* stat
   if (cache->rope_dims > 0 && (!rope_cs || rope_rows < 1)) return CSA_ERR_INVALID_ARG;
   const int bound = (max_new_per_seq + cache->ratio - 1) / cache->ratio;
   if (out_slots && max_entries_out < bound) return CSA_ERR_INVALID_ARG;
-  if (batch == 0) return CSA_OK;
-  csa::CompressArgs a{*cache, *state, batch, start_pos, cu_new, total_new, max_new_per_seq, bound,
-                      kv_new, logit_new, gamma, rms_eps, rope_cs, rope_rows, out_slots,
-                      out_slots ? max_entries_out : 0, out_new_entries};
+  *out = csa::CompressArgs{*cache, *state, batch, start_pos, cu_new, total_new, max_new_per_seq, bound,
+                           kv_new, logit_new, gamma, rms_eps, rope_cs, rope_rows, out_slots,
+                           out_slots ? max_entries_out : 0, out_new_entries};
+  return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+csa_status_t csa_compress_insert(const csa_cache_t* cache, const csa_raw_t* state, int32_t batch,
+                                 const int32_t* start_pos, const int32_t* cu_new, int32_t total_new,
+                                 int32_t max_new_per_seq, const void* kv_new, const void* logit_new,
+                                 const float* gamma, float rms_eps, const float* rope_cs, int32_t rope_rows,
+                                 int32_t* out_slots, int32_t max_entries_out, int32_t* out_new_entries,
+                                 hipStream_t stream) {
+  csa::CompressArgs a;
+  const csa_status_t st = compress_args(cache, state, batch, start_pos, cu_new, total_new, max_new_per_seq, kv_new,
+                                        logit_new, gamma, rms_eps, rope_cs, rope_rows, out_slots, max_entries_out,
+                                        out_new_entries, &a);
+  if (st != CSA_OK || batch == 0) return st;
   return hip_status(csa::launch_compress(a, stream));
+}
+
+csa_status_t csa_compress_insert_pair(const csa_cache_t* cache_a, const csa_raw_t* state_a, const void* kv_a,
+                                      const void* logit_a, const float* gamma_a, const float* rope_cs_a,
+                                      int32_t rope_rows_a, const csa_cache_t* cache_b, const csa_raw_t* state_b,
+                                      const void* kv_b, const void* logit_b, const float* gamma_b,
+                                      const float* rope_cs_b, int32_t rope_rows_b, int32_t batch,
+                                      const int32_t* start_pos, const int32_t* cu_new, int32_t total_new,
+                                      int32_t max_new_per_seq, float rms_eps, hipStream_t stream) {
+  csa::CompressArgs a, b;
+  csa_status_t st = compress_args(cache_a, state_a, batch, start_pos, cu_new, total_new, max_new_per_seq, kv_a,
+                                  logit_a, gamma_a, rms_eps, rope_cs_a, rope_rows_a, nullptr, 0, nullptr, &a);
+  if (st != CSA_OK) return st;
+  st = compress_args(cache_b, state_b, batch, start_pos, cu_new, total_new, max_new_per_seq, kv_b, logit_b, gamma_b,
+                     rms_eps, rope_cs_b, rope_rows_b, nullptr, 0, nullptr, &b);
+  if (st != CSA_OK || batch == 0) return st;
+  return hip_status(csa::launch_compress_pair(a, b, stream));
 }
 
 size_t csa_index_topk_workspace(int32_t n_q, int64_t max_elig, int32_t k, int32_t n_heads) {

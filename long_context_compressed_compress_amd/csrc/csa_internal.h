@@ -118,6 +118,7 @@ struct CompressArgs {
   int32_t* out_new_entries;
 };
 hipError_t launch_compress(const CompressArgs& a, hipStream_t stream);
+hipError_t launch_compress_pair(const CompressArgs& a, const CompressArgs& b, hipStream_t stream);
 
 struct IndexArgs {
   csa_cache_t cache;

@@ -205,3 +205,19 @@ def test_prepare_qk_validation(L):
     assert call(swa=_raw(dim=100, roles=0, dtype=csa.BF16)) == INVALID
     assert call(qd=csa.BF16, swa=_raw(dim=512, roles=0, dtype=csa.F32)) == INVALID
     assert call(n=0, seq=None, pos=None, q=None, g=None, kv=None, out=None) == OK
+
+
+def test_compress_pair_validation(L):
+    f = L.csa_compress_insert_pair
+    good_c, good_s = _cache(dim=512), _raw(dim=512)
+    idx_c, idx_s = _cache(dim=128), _raw(dim=128)
+
+    def call(ca=good_c, sa=good_s, cb=idx_c, sb=idx_s, ga=FAKE, gb=FAKE, kva=FAKE, kvb=FAKE, batch=2, eps=1e-6):
+        return f(ctypes.byref(ca), ctypes.byref(sa), kva, FAKE, ga, FAKE, 10, ctypes.byref(cb), ctypes.byref(sb), kvb,
+                 FAKE, gb, FAKE, 10, batch, FAKE, FAKE, 2, 1, eps, None)
+    assert call(cb=_cache(dim=100)) == INVALID
+    assert call(sb=_raw(dim=512)) == INVALID          # state of the wrong dim for cache b
+    assert call(ga=None) == INVALID and call(gb=None) == INVALID
+    assert call(kvb=None) == INVALID and call(kvb=FAKE + 4) == INVALID
+    assert call(eps=-1.0) == INVALID
+    assert call(batch=0) == OK

@@ -109,6 +109,60 @@ def test_compress_chunk_split_and_determinism():
     assert torch.equal(a.g_cache.pages.view(torch.int16), c.g_cache.pages.view(torch.int16))
 
 
+@pytest.mark.parametrize("cd,dims,lens,n_new", [("bf16", (512, 128), [700, 259, 300, 1031, 7, 64], 1),
+                                                 ("fp8", (512, 128), [700, 259, 303, 1031], 1),
+                                                 ("bf16", (512, 128), [700, 259, 300], 37),
+                                                 ("bf16", (256, 64), [700, 259, 300], 5)])
+def test_compress_insert_pair_matches_two_calls(cd, dims, lens, n_new):
+    """compress_insert_pair (one launch for a 512 main + 128 indexer c4a pair, two launches otherwise) writes exactly
+    what two compress_insert calls write: caches, scales and compressor state, bit for bit."""
+    _log(f"compress pair cache={cd} dims={dims} lens={lens} n_new={n_new}")
+    import synth
+    g = synth.rng(88, dims[0] + n_new)
+    B = len(lens)
+    nb = max(lens) // 256 + 2
+    n_phys = B * nb + 2
+    bt = gu.dev_i32(synth.random_block_table(synth.rng(88, synth.STREAM_BT), B, nb, n_phys))
+    sides = []
+    for _ in range(2):
+        per = []
+        for d in dims:
+            pages = torch.zeros((n_phys * 64, d), dtype=torch.uint8 if cd == "fp8" else torch.bfloat16, device="cuda")
+            sc = torch.zeros(n_phys * 64, device="cuda") if cd == "fp8" else None
+            cache = csa.Cache(4, 8, d, 64 if d >= 128 else 32, pages, bt, sc)
+            state = csa.Raw(d, 2, torch.zeros((n_phys * 256, d), dtype=torch.bfloat16, device="cuda"), bt,
+                            torch.zeros((n_phys * 256, 2, d), dtype=torch.bfloat16, device="cuda"))
+            per.append((cache, state))
+        sides.append(per)
+    # history: positions 0..L-1 already in the caches (identical on both sides), then n_new tokens per sequence
+    rows = max(lens) + n_new + 1
+    ropes = [csa.rope_table(rows, 64 if d >= 128 else 32) for d in dims]
+    gammas = [gu.dev_f32(synth.uniform_f32(g, (d,), 0.5, 1.5)) for d in dims]
+    hist = [(gu.dev_bf16(synth.normal_bf16_bits(g, (sum(lens), d))), gu.dev_bf16(synth.normal_bf16_bits(g, (sum(lens), 2, d))))
+            for d in dims]
+    new = [(gu.dev_bf16(synth.normal_bf16_bits(g, (B * n_new, d))), gu.dev_bf16(synth.normal_bf16_bits(g, (B * n_new, 2, d))))
+           for d in dims]
+    cu_h = gu.dev_i32(np.concatenate([[0], np.cumsum(lens)]))
+    zero = gu.dev_i32(np.zeros(B))
+    start = gu.dev_i32(lens)
+    cu_n = gu.dev_i32(np.arange(B + 1) * n_new)
+    for per in sides:
+        for (cache, state), (kv, lg), gm, rp in zip(per, hist, gammas, ropes):
+            csa.compress_insert(cache, state, zero, cu_h, kv, lg, gm, 1e-6, rp, max(lens))
+    (ca, sa), (cb, sb) = sides[0]
+    csa.compress_insert_pair(ca, sa, new[0][0], new[0][1], gammas[0], ropes[0], cb, sb, new[1][0], new[1][1], gammas[1],
+                             ropes[1], start, cu_n, 1e-6, n_new)
+    for (cache, state), (kv, lg), gm, rp in zip(sides[1], new, gammas, ropes):
+        csa.compress_insert(cache, state, start, cu_n, kv, lg, gm, 1e-6, rp, n_new)
+    torch.cuda.synchronize()
+    for (c0, s0), (c1, s1) in zip(sides[0], sides[1]):
+        assert torch.equal(c0.pages.view(torch.uint8), c1.pages.view(torch.uint8))
+        if cd == "fp8":
+            assert torch.equal(c0.scales, c1.scales)
+        assert torch.equal(s0.kv_pages.view(torch.uint8), s1.kv_pages.view(torch.uint8))
+        assert torch.equal(s0.logit_pages.view(torch.uint8), s1.logit_pages.view(torch.uint8))
+
+
 # ------------------------------------------------------------------ index_topk
 def _gpu_cache(pc: si.PagedCache) -> csa.Cache:
     return csa.Cache(pc.ratio, pc.window, pc.dim, 0, gu.dev_store(pc.pages, pc.dtype), gu.dev_i32(pc.bt),
