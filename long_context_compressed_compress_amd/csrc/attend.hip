@@ -417,7 +417,8 @@ __host__ __device__ inline SplitPlan split_plan(int n_q, int n_hchunk, int64_t m
   const int64_t tiles = (max_keys + kTile - 1) / kTile;
   const int64_t want = (512 + int64_t(n_q) * n_hchunk - 1) / (int64_t(n_q) * n_hchunk);  // about two blocks per CU
   int64_t ns = want < 1 ? 1 : want;
-  const int64_t max_split = (tiles + 1) / 2;  // at least two tiles per split
+  // at least two tiles per split, unless one tile per split still fits one round of workgroups (one per CU)
+  const int64_t max_split = (int64_t(n_q) * n_hchunk * tiles <= 256) ? tiles : (tiles + 1) / 2;
   if (ns > max_split) ns = max_split < 1 ? 1 : max_split;
   const int64_t tiles_per = (tiles + ns - 1) / ns;
   sp.split_keys = int(tiles_per * kTile);
