@@ -59,7 +59,12 @@ typedef enum {
 typedef enum {
   CSA_F32 = 0,
   CSA_BF16 = 1,
-  CSA_FP8_E4M3 = 2 /* OCP e4m3fn (max 448), one fp32 scale per row: value = scale * e4m3(code) */
+  CSA_FP8_E4M3 = 2, /* OCP e4m3fn (max 448), one fp32 scale per row: value = scale * e4m3(code) */
+  CSA_FP4_E2M1 = 3  /* OCP MXFP4, compressed caches only (the indexer cache; [P1] "Memory Efficiency" names
+                       an fp4 indexer cache): a row of D channels is D/2 bytes, channel 2j in the low nibble
+                       of byte j; every block of 32 channels has one E8M0 byte X+127 and value = 2^X * e2m1.
+                       X = floor(log2(block amax)) - 2 (0 for an all-zero block), elements rounded to
+                       nearest-even and saturated at 6. D must be a multiple of 32. */
 } csa_dtype_t;
 
 typedef enum {
@@ -75,7 +80,8 @@ typedef struct {
   int32_t rope_dims;        /* R, even, 0 <= R <= D; rotated dims are [D-R, D) */
   csa_dtype_t dtype;        /* element type of pages */
   void* pages;              /* [n_phys * E][D] rows, E = 256 / ratio */
-  float* scales;            /* [n_phys * E] per-entry scales (fp8 only; NULL otherwise) */
+  float* scales;            /* fp8: [n_phys * E] per-entry fp32 scales; fp4: cast of a uint8 array
+                               [n_phys * E][D / 32] of E8M0 block exponents; NULL otherwise */
   const int32_t* block_table; /* [batch][bt_stride] logical 256-position block -> physical page id */
   int32_t batch, bt_stride; /* rows and columns of block_table */
   int32_t n_phys;           /* physical pages in `pages` */
@@ -102,7 +108,8 @@ typedef struct {
  * compressed entry is a weighted sum of its window's raw tokens; here the weight of raw row t of
  * the window for channel c is softmax_t(logit[t][c]) with logit[t] the row's role-(t / ratio)
  * logit vector. Then y = z / sqrt(mean(z^2) + rms_eps) * gamma, RoPE at the anchor, rounding to
- * the cache dtype (fp8: scale = amax/448, code = e4m3_rne(y * (448/amax)), computed in fp32).
+ * the cache dtype (fp8: scale = amax/448, code = e4m3_rne(y * (448/amax)), computed in fp32; fp4: the
+ * MXFP4 rule of CSA_FP4_E2M1 applied to the fp32 row).
  *
  * Sequence b appends n_b = cu_new[b+1] - cu_new[b] raw tokens at positions start_pos[b] ... to the
  * state pages (rows cu_new[b] .. of kv_new [total_new][D] and logit_new [total_new][roles][D],
@@ -128,7 +135,8 @@ csa_status_t csa_compress_insert(const csa_cache_t* cache, const csa_raw_t* stat
  * call. Each cache's arguments mean what they mean for csa_compress_insert (kv_a / logit_a / gamma_a /
  * rope_cs_a belong to cache_a, and so on); batch, start_pos, cu_new, total_new, max_new_per_seq and rms_eps
  * are shared; no slot or count outputs. Results are those of the two separate calls. A c4a bf16 / fp8 main
- * cache of dim 512 with an indexer cache of dim 128 and bf16 inputs runs as one kernel launch whose blocks
+ * cache of dim 512 with an indexer cache of dim 128 of the same dtype (or an fp4 indexer cache beside an fp8
+ * main cache) and bf16 inputs runs as one kernel launch whose blocks
  * each work for one of the two caches (each with its own per-dim code); any other pair runs as two launches.
  * Validation: both argument sets as for csa_compress_insert, before any HIP call.
  * ------------------------------------------------------------------------------------------- */
@@ -150,7 +158,10 @@ csa_status_t csa_compress_insert_pair(const csa_cache_t* cache_a, const csa_raw_
  * are entries 0 .. n_elig-1 with n_elig = csa_num_eligible(q_pos[q]), clamped to max_elig [host]
  * (max_elig <= 2^31-1).
  * q_idx is [n_q][n_heads][D] in q_dtype (CSA_F32 for an fp32 cache, CSA_BF16 otherwise);
- * head_w [n_q][n_heads] fp32 for WRELU, NULL for DOT. fp8 keys score as scale_e * (q . code_e).
+ * head_w [n_q][n_heads] fp32 for WRELU, NULL for DOT. fp8 keys score as scale_e * (q . code_e); fp4
+ * keys are dequantised exactly (2^X_b * e2m1) and score as q . k_e. An fp4 cache is scored for WRELU on
+ * c4a pages of dim 128 with 16, 32, 48 or 64 heads and CSA_BF16 q; other fp4 requests are
+ * CSA_ERR_UNSUPPORTED.
  * Order: score descending, ties to the lower entry index, -0 == +0, NaN below every number.
  * Output out_idx [n_q][k]: the min(k, n_elig) chosen entries in ascending index order, -1 padded;
  * out_count [n_q] (may be NULL); out_scores [n_q][k] fp32 scores in the same order, NaN padded
@@ -195,7 +206,8 @@ csa_status_t csa_index_select(const csa_cache_t* idx_cache, int32_t n_q, const i
  * topk_idx == NULL, every eligible entry (n_elig clamped to max_elig [host]); plus window rows
  * at positions max(0, p - swa_window + 1) .. p read from `swa`. One joint softmax over all keys:
  * o_h = sum_s softmax_s(softmax_scale * q_h . k_s) k_s over all D dims, in fp32.
- * q [n_q][n_heads][D] in q_dtype (CSA_F32 for fp32 caches, CSA_BF16 otherwise);
+ * q [n_q][n_heads][D] in q_dtype (CSA_F32 for fp32 caches, CSA_BF16 otherwise); an fp4 cache is
+ * CSA_ERR_UNSUPPORTED (fp4 is the indexer cache's format);
  * out [n_q][n_heads][D] fp32; out_lse [n_q][n_heads] natural-log sum of exp of the scaled
  * logits (may be NULL). fuse_inv_rope = 1 applies the inverse rotation at q_pos to out.
  * swa_window in [0, 1024]; n_heads in [1, 128]; k in [1, 2048] when topk_idx != NULL.

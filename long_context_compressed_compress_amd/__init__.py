@@ -17,7 +17,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libcsa.so")
 
-F32, BF16, FP8 = 0, 1, 2
+F32, BF16, FP8, FP4 = 0, 1, 2, 3
 SCORE_DOT, SCORE_WRELU = 0, 1
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "workspace missing or too small",
           4: "HIP launch failed"}
@@ -109,7 +109,7 @@ def _stream(stream) -> int:
 
 
 _DT = {torch.float32: F32, torch.bfloat16: BF16, torch.int16: BF16, torch.uint16: BF16, torch.uint8: FP8,
-       torch.float8_e4m3fn: FP8}
+       torch.float8_e4m3fn: FP8, torch.float4_e2m1fn_x2: FP4}
 
 
 def dtype_code(t: torch.Tensor) -> int:
@@ -119,7 +119,10 @@ def dtype_code(t: torch.Tensor) -> int:
 # ------------------------------------------------------------------ descriptors
 @dataclass
 class Cache:
-    """A compressed cache: pages [n_phys*256/ratio][dim], optional fp8 scales, block table [batch][bt_stride]."""
+    """A compressed cache: pages [n_phys*256/ratio][dim], optional fp8 scales, block table [batch][bt_stride].
+
+    An MXFP4 cache holds pages as torch.float4_e2m1fn_x2 [rows][dim/2] (two codes per byte) and scales as
+    uint8 [rows][dim/32] E8M0 block exponents."""
     ratio: int
     window: int
     dim: int

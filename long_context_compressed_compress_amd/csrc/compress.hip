@@ -229,7 +229,40 @@ __device__ __forceinline__ void compress_insert_body(const CompressArgs& a, int6
     }
   }
   const bool in_table = b < a.cache.batch && slot >= 0;
-  if (OUT == 2) {
+  if (OUT == 3) {
+    // MXFP4: the LPB lanes holding one 32-channel block share its amax; X = floor(log2 amax) - 2 comes from
+    // the fp32 exponent field (clamped to the E8M0 range), elements are y * 2^-X rounded to nearest-even
+    // e2m1 with saturation at 6
+    constexpr int LPB = 32 / CH;
+    static_assert(32 % CH == 0 && D % 32 == 0, "fp4 block split");
+    float amax = 0.f;
+#pragma unroll
+    for (int k = 0; k < CH; ++k) amax = fmaxf(amax, fabsf(y[k]));
+#pragma unroll
+    for (int off = 1; off < LPB; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    const int eb = int((__float_as_uint(amax) >> 23) & 0xFFu);  // biased exponent of amax
+    const int X = amax > 0.f ? max(eb - 129, -127) : 0;
+    const float inv = __uint_as_float(uint32_t(127 - X) << 23);  // 2^-X, normal for X in [-127, 125]
+    if (in_table && grp == 0) {
+      uint32_t nib[CH];
+#pragma unroll
+      for (int k = 0; k < CH; ++k) nib[k] = f32_to_e2m1_rne(y[k] * inv);
+      uint8_t* dst = reinterpret_cast<uint8_t*>(a.cache.pages) + slot * (D / 2) + ch0 / 2;
+      if (CH == 8) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int k = 0; k < CH; ++k) w |= nib[k] << (4 * k);
+        *reinterpret_cast<uint32_t*>(dst) = w;
+      } else {
+        uint32_t w = 0;
+#pragma unroll
+        for (int k = 0; k < CH; ++k) w |= nib[k] << (4 * k);
+        *reinterpret_cast<uint16_t*>(dst) = uint16_t(w);
+      }
+      if (ch_lane % LPB == 0)
+        reinterpret_cast<uint8_t*>(a.cache.scales)[slot * (D / 32) + ch0 / 32] = uint8_t(X + 127);
+    }
+  } else if (OUT == 2) {
     float amax = 0.f;
 #pragma unroll
     for (int k = 0; k < CH; ++k) amax = fmaxf(amax, fabsf(y[k]));
@@ -281,12 +314,12 @@ __global__ void __launch_bounds__(256) compress_insert_kernel(CompressArgs a) {
 }
 
 // Two c4a caches' compress_insert in one grid (a decode step's main and indexer caches): blocks [0, blocks_a)
-// run cache a's code for head dim DA, the rest cache b's for DB. Each cache keeps its own per-dim code, the
-// step saves one launch.
-template <typename TIn, int OUT, int DA, int DB>
+// run cache a's code for head dim DA and output type OA, the rest cache b's for DB and OB. Each cache keeps
+// its own code, the step saves one launch.
+template <typename TIn, int OA, int OB, int DA, int DB>
 __global__ void __launch_bounds__(256) compress_pair_kernel(CompressArgs a, CompressArgs b, int64_t blocks_a) {
-  if (int64_t(blockIdx.x) < blocks_a) compress_insert_body<TIn, OUT, DA, 4, 8>(a, blockIdx.x);
-  else compress_insert_body<TIn, OUT, DB, 4, 8>(b, int64_t(blockIdx.x) - blocks_a);
+  if (int64_t(blockIdx.x) < blocks_a) compress_insert_body<TIn, OA, DA, 4, 8>(a, blockIdx.x);
+  else compress_insert_body<TIn, OB, DB, 4, 8>(b, int64_t(blockIdx.x) - blocks_a);
 }
 
 inline int64_t compress_blocks(const CompressArgs& a) {
@@ -324,6 +357,7 @@ hipError_t dispatch_out(const CompressArgs& a, hipStream_t stream) {
     case CSA_F32: return dispatch_dim<TIn, 0>(a, stream);
     case CSA_BF16: return dispatch_dim<TIn, 1>(a, stream);
     case CSA_FP8_E4M3: return dispatch_dim<TIn, 2>(a, stream);
+    case CSA_FP4_E2M1: return dispatch_dim<TIn, 3>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -336,10 +370,10 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_compress_pair(const CompressArgs& a, const CompressArgs& b, hipStream_t stream) {
+  const bool same = a.cache.dtype == b.cache.dtype && (a.cache.dtype == CSA_BF16 || a.cache.dtype == CSA_FP8_E4M3);
+  const bool fp8_fp4 = a.cache.dtype == CSA_FP8_E4M3 && b.cache.dtype == CSA_FP4_E2M1;
   const bool fused = a.state.dtype == CSA_BF16 && b.state.dtype == CSA_BF16 && a.cache.ratio == 4 &&
-                     b.cache.ratio == 4 && a.cache.dtype == b.cache.dtype &&
-                     (a.cache.dtype == CSA_BF16 || a.cache.dtype == CSA_FP8_E4M3) && a.cache.dim == 512 &&
-                     b.cache.dim == 128;
+                     b.cache.ratio == 4 && (same || fp8_fp4) && a.cache.dim == 512 && b.cache.dim == 128;
   if (!fused) {  // any other pair: one launch per cache
     const hipError_t e = launch_compress(a, stream);
     return e != hipSuccess ? e : launch_compress(b, stream);
@@ -349,9 +383,11 @@ hipError_t launch_compress_pair(const CompressArgs& a, const CompressArgs& b, hi
   if (ba + bb > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid(unsigned(ba + bb));
   if (a.cache.dtype == CSA_BF16)
-    hipLaunchKernelGGL((compress_pair_kernel<uint16_t, 1, 512, 128>), grid, dim3(256), 0, stream, a, b, ba);
+    hipLaunchKernelGGL((compress_pair_kernel<uint16_t, 1, 1, 512, 128>), grid, dim3(256), 0, stream, a, b, ba);
+  else if (fp8_fp4)
+    hipLaunchKernelGGL((compress_pair_kernel<uint16_t, 2, 3, 512, 128>), grid, dim3(256), 0, stream, a, b, ba);
   else
-    hipLaunchKernelGGL((compress_pair_kernel<uint16_t, 2, 512, 128>), grid, dim3(256), 0, stream, a, b, ba);
+    hipLaunchKernelGGL((compress_pair_kernel<uint16_t, 2, 2, 512, 128>), grid, dim3(256), 0, stream, a, b, ba);
   return hipGetLastError();
 }
 

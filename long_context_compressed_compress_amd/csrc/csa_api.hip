@@ -12,13 +12,15 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 bool valid_shape(int ratio, int window) { return (ratio == 4 && window == 8) || (ratio == 128 && window == 128); }
 bool valid_dim(int d) { return d == 32 || d == 64 || d == 128 || d == 256 || d == 512; }
 bool valid_dtype(csa_dtype_t t) { return t == CSA_F32 || t == CSA_BF16 || t == CSA_FP8_E4M3; }
+bool valid_cache_dtype(csa_dtype_t t) { return valid_dtype(t) || t == CSA_FP4_E2M1; }
 
 bool valid_cache(const csa_cache_t* c) {
   if (!c) return false;
   if (!valid_shape(c->ratio, c->window) || !valid_dim(c->dim)) return false;
   if (c->rope_dims < 0 || c->rope_dims > c->dim || (c->rope_dims & 1)) return false;
-  if (!valid_dtype(c->dtype) || !c->pages || !aligned(c->pages, 16)) return false;
-  if (c->dtype == CSA_FP8_E4M3 && !c->scales) return false;
+  if (!valid_cache_dtype(c->dtype) || !c->pages || !aligned(c->pages, 16)) return false;
+  if ((c->dtype == CSA_FP8_E4M3 || c->dtype == CSA_FP4_E2M1) && !c->scales) return false;
+  if (c->dtype == CSA_FP4_E2M1 && (c->dim % 32 != 0 || !aligned(c->scales, 4))) return false;
   if (!c->block_table || c->batch < 1 || c->bt_stride < 1 || c->n_phys < 1) return false;
   return true;
 }
@@ -233,6 +235,7 @@ csa_status_t csa_attend(const csa_cache_t* kv_cache, const csa_raw_t* swa, int32
                         int32_t fuse_inv_rope, const float* rope_cs, int32_t rope_rows, float* out, float* out_lse,
                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!valid_cache(kv_cache) || !valid_raw_common(swa, kv_cache ? kv_cache->dim : -1)) return CSA_ERR_INVALID_ARG;
+  if (kv_cache->dtype == CSA_FP4_E2M1) return CSA_ERR_UNSUPPORTED;  // fp4 is the indexer cache's format
   if (swa->dtype != kv_cache->dtype || swa->roles != 0) return CSA_ERR_INVALID_ARG;
   if (swa->dtype == CSA_FP8_E4M3 && !swa->scales) return CSA_ERR_INVALID_ARG;
   if (swa_window < 0 || swa_window > 1024 || n_q < 0 || n_heads < 1 || n_heads > 128) return CSA_ERR_INVALID_ARG;

@@ -63,6 +63,16 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_rne(float f) {
   return s | code;
 }
 
+// Nearest e2m1 code (ties to the code with mantissa bit 0, saturation at 6) of a finite value; bit 3 is
+// the sign, set for every negative input. Magnitudes by code: 0, 0.5, 1, 1.5, 2, 3, 4, 6; each comparison
+// below is against a midpoint, strict where the lower code is the even one of the tie.
+__device__ __forceinline__ uint32_t f32_to_e2m1_rne(float f) {
+  const float a = fabsf(f);
+  const uint32_t m = uint32_t(a > 0.25f) + uint32_t(a >= 0.75f) + uint32_t(a > 1.25f) + uint32_t(a >= 1.75f) +
+                     uint32_t(a > 2.5f) + uint32_t(a >= 3.5f) + uint32_t(a > 5.0f);
+  return m | (f < 0.f ? 8u : 0u);
+}
+
 // Order-preserving 32-bit key of an fp32 score: larger score -> larger key.
 // -0 is folded onto +0 and every NaN maps to 0 (below -inf).
 __device__ __forceinline__ uint32_t score_key(float s) {

@@ -96,32 +96,56 @@ __device__ __forceinline__ void flush_hist(uint32_t* hist_s, uint32_t* hist_q) {
 constexpr int kPagesPerBlock = 32;
 constexpr int kQueryFastMin = 256;  // queries per launch from which the grid walks queries first
 
-template <bool FP8>
+// Key formats of the MFMA score: 0 bf16, 1 fp8 e4m3 (per-entry scale), 2 MXFP4 (per-32-channel E8M0 scale).
+// bf16 and fp8 lanes feed dims ks*32 + kg*8 .. +8 of k-step ks; an fp4 lane feeds dims kg*32 + ks*8 .. +8,
+// so its four k-steps are one contiguous 32-channel block (16 B, one scale) and the query fragments follow
+// the same permutation (a dot product does not depend on the order of its terms).
+template <int KF>
 struct PageBuf;
 template <>
-struct PageBuf<false> { uint4 v[4][4]; };  // [tile][k-step] 16 B
+struct PageBuf<0> { uint4 v[4][4]; };  // [tile][k-step] 16 B
 template <>
-struct PageBuf<true> { uint2 v[4][4]; float sc[4]; };  // 8 B codes + per-tile-column scale
+struct PageBuf<1> { uint2 v[4][4]; float sc[4]; };  // 8 B codes + per-tile-column scale
+template <>
+struct PageBuf<2> { uint4 v[4]; float sc[4]; };  // [tile] 32 codes of the lane's block + that block's 2^X
 
-template <bool FP8>
-__device__ __forceinline__ void load_page(PageBuf<FP8>& b, const void* pages, const float* scales, int64_t row0,
+// E8M0 byte -> 2^(e-127) as fp32 (e = 0 gives the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  return e ? __uint_as_float(e << 23) : __uint_as_float(0x00400000u);
+}
+
+template <int KF>
+__device__ __forceinline__ void load_page(PageBuf<KF>& b, const void* pages, const float* scales, int64_t row0,
                                           int col, int kg) {
   constexpr int DIM = 128;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int64_t row = row0 + u * 16 + col;
+    if constexpr (KF == 2) {
+      b.v[u] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(pages) + row * (DIM / 2) + kg * 16);
+      b.sc[u] = e8m0_to_f32(reinterpret_cast<const uint8_t*>(scales)[row * (DIM / 32) + kg]);
+    } else {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (FP8) {
-        reinterpret_cast<PageBuf<true>&>(b).v[u][ks] =
-            *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(pages) + row * DIM + ks * 32 + kg * 8);
-      } else {
-        reinterpret_cast<PageBuf<false>&>(b).v[u][ks] =
-            *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(pages) + row * DIM + ks * 32 + kg * 8);
+      for (int ks = 0; ks < 4; ++ks) {
+        if constexpr (KF == 1)
+          b.v[u][ks] = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(pages) + row * DIM + ks * 32 + kg * 8);
+        else
+          b.v[u][ks] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(pages) + row * DIM + ks * 32 + kg * 8);
       }
+      if constexpr (KF == 1) b.sc[u] = scales[row];
     }
-    if (FP8) reinterpret_cast<PageBuf<true>&>(b).sc[u] = scales[row];
   }
+}
+
+// 8 e2m1 codes (one 32-bit word, channel 2j in the low nibble of byte j) -> 8 bf16 times the block scale
+// 2^X (hardware OCP fp4 -> bf16 conversion; exact, since a power-of-two multiple of an e2m1 value has at
+// most two significant bits).
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16x8_hw(uint32_t w, float scale) {
+  const uint32_t o0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+  const uint32_t o1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+  const uint32_t o2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+  const uint32_t o3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+  return __builtin_bit_cast(bf16x8, make_uint4(o0, o1, o2, o3));
 }
 
 // 8 e4m3fn codes -> 8 bf16 (hardware OCP e4m3 -> f32 conversion, then exact truncation to bf16).
@@ -138,8 +162,8 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8_hw(uint2 v) {
   return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
 }
 
-template <bool FP8, int HT>
-__device__ __forceinline__ uint32_t score_page(const PageBuf<FP8>& b, const bf16x8 (&qa)[HT][4],
+template <int KF, int HT>
+__device__ __forceinline__ uint32_t score_page(const PageBuf<KF>& b, const bf16x8 (&qa)[HT][4],
                                                const float (&wv)[HT][4], int kg) {
   uint32_t mine = 0u;
   float mine_f = 0.f;
@@ -148,8 +172,14 @@ __device__ __forceinline__ uint32_t score_page(const PageBuf<FP8>& b, const bf16
     bf16x8 kb[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      if (FP8) kb[ks] = fp8x8_to_bf16x8_hw(reinterpret_cast<const PageBuf<true>&>(b).v[u][ks]);
-      else kb[ks] = __builtin_bit_cast(bf16x8, reinterpret_cast<const PageBuf<false>&>(b).v[u][ks]);
+      if constexpr (KF == 2) {
+        const uint4 c = b.v[u];
+        kb[ks] = fp4x8_to_bf16x8_hw(ks == 0 ? c.x : ks == 1 ? c.y : ks == 2 ? c.z : c.w, b.sc[u]);
+      } else if constexpr (KF == 1) {
+        kb[ks] = fp8x8_to_bf16x8_hw(b.v[u][ks]);
+      } else {
+        kb[ks] = __builtin_bit_cast(bf16x8, b.v[u][ks]);
+      }
     }
     float part = 0.f;
 #pragma unroll
@@ -162,7 +192,7 @@ __device__ __forceinline__ uint32_t score_page(const PageBuf<FP8>& b, const bf16
     }
     part += __shfl_xor(part, 16);
     part += __shfl_xor(part, 32);
-    if (FP8) part *= reinterpret_cast<const PageBuf<true>&>(b).sc[u];
+    if constexpr (KF == 1) part *= b.sc[u];
     if (kg == u) mine_f = part;
   }
   mine = score_key(mine_f);
@@ -172,7 +202,7 @@ __device__ __forceinline__ uint32_t score_page(const PageBuf<FP8>& b, const bf16
 // Grid order: with few queries (decode) blockIdx.x walks the page runs of one query; with many queries per
 // sequence (a prefill chunk) blockIdx.x walks the queries (query_fast), so the workgroups running at the same
 // time read the same run of pages and an XCD's L2 serves its queries' repeated reads of them.
-template <bool FP8, int HT>
+template <int KF, int HT>
 __global__ void __launch_bounds__(256, 2) score_mfma_kernel(IndexArgs a, Workspace ws, int query_fast) {
   constexpr int DIM = 128;
   constexpr int E = 64;
@@ -205,7 +235,8 @@ __global__ void __launch_bounds__(256, 2) score_mfma_kernel(IndexArgs a, Workspa
   for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      qa[ht][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + (ht * 16 + col) * DIM + ks * 32 + kg * 8));
+      qa[ht][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+                                                  qp + (ht * 16 + col) * DIM + (KF == 2 ? kg * 32 + ks * 8 : ks * 32 + kg * 8)));
   float wv[HT][4];
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht)
@@ -232,14 +263,14 @@ __global__ void __launch_bounds__(256, 2) score_mfma_kernel(IndexArgs a, Workspa
     }
   };
   if (n_mine > 0) {
-    PageBuf<FP8> b0, b1;
+    PageBuf<KF> b0, b1;
     bool ok0, ok1;
-    load_page<FP8>(b0, a.cache.pages, a.cache.scales, page_row(0, &ok0), col, kg);
+    load_page<KF>(b0, a.cache.pages, a.cache.scales, page_row(0, &ok0), col, kg);
     for (int j = 0; j < n_mine; j += 2) {
-      load_page<FP8>(b1, a.cache.pages, a.cache.scales, page_row(j + 1, &ok1), col, kg);
-      finish(j, score_page<FP8, HT>(b0, qa, wv, kg), ok0);
-      load_page<FP8>(b0, a.cache.pages, a.cache.scales, page_row(j + 2, &ok0), col, kg);
-      if (j + 1 < n_mine) finish(j + 1, score_page<FP8, HT>(b1, qa, wv, kg), ok1);
+      load_page<KF>(b1, a.cache.pages, a.cache.scales, page_row(j + 1, &ok1), col, kg);
+      finish(j, score_page<KF, HT>(b0, qa, wv, kg), ok0);
+      load_page<KF>(b0, a.cache.pages, a.cache.scales, page_row(j + 2, &ok0), col, kg);
+      if (j + 1 < n_mine) finish(j + 1, score_page<KF, HT>(b1, qa, wv, kg), ok1);
     }
   }
   flush_hist(hist_s, ws.hist + int64_t(q) * kHistBins);
@@ -377,18 +408,18 @@ __global__ void __launch_bounds__(kShareThreads, 1) score_shared_kernel(IndexArg
           lds_barrier();
           const int64_t pg = pg_begin + i;
           if (active && pg < w_npages[wave]) {
-            PageBuf<FP8> b;
+            PageBuf<FP8 ? 1 : 0> b;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
               const char* rowp = buf + (u * 16 + col) * L::ROW;
 #pragma unroll
               for (int ks = 0; ks < 4; ++ks) {
-                if (FP8) reinterpret_cast<PageBuf<true>&>(b).v[u][ks] = *reinterpret_cast<const uint2*>(rowp + ks * 32 + kg * 8);
-                else reinterpret_cast<PageBuf<false>&>(b).v[u][ks] = *reinterpret_cast<const uint4*>(rowp + ks * 64 + kg * 16);
+                if (FP8) reinterpret_cast<PageBuf<1>&>(b).v[u][ks] = *reinterpret_cast<const uint2*>(rowp + ks * 32 + kg * 8);
+                else reinterpret_cast<PageBuf<0>&>(b).v[u][ks] = *reinterpret_cast<const uint4*>(rowp + ks * 64 + kg * 16);
               }
-              if (FP8) reinterpret_cast<PageBuf<true>&>(b).sc[u] = scale_s[i & 1][u * 16 + col];
+              if (FP8) reinterpret_cast<PageBuf<1>&>(b).sc[u] = scale_s[i & 1][u * 16 + col];
             }
-            const uint32_t key = score_page<FP8, HT>(b, qa, wv, kg);
+            const uint32_t key = score_page<FP8 ? 1 : 0, HT>(b, qa, wv, kg);
             const int64_t e = pg * E + lane;
             if (e < n_elig) {
               const uint32_t k2 = pg_phys[i] >= 0 ? key : 0u;
@@ -889,6 +920,7 @@ bool index_supported(const csa_cache_t& c, csa_dtype_t q_dtype, int n_heads, csa
   if (c.dtype == CSA_F32) return q_dtype == CSA_F32 && n_heads * c.dim <= 8192;
   if (q_dtype != CSA_BF16) return false;
   const bool mfma = mode == CSA_SCORE_WRELU && c.ratio == 4 && c.dim == 128 && n_heads % 16 == 0 && n_heads <= 64;
+  if (c.dtype == CSA_FP4_E2M1) return mfma;  // fp4 pages are scored by the MFMA kernel only
   return mfma || n_heads * c.dim <= 8192;
 }
 
@@ -901,6 +933,13 @@ hipError_t launch_index_clear(void* ws_base, int n_q, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int HT>
+void launch_score_mfma(int kf, dim3 grid, const IndexArgs& a, const Workspace& ws, int qf, hipStream_t stream) {
+  if (kf == 2) hipLaunchKernelGGL((score_mfma_kernel<2, HT>), grid, dim3(256), 0, stream, a, ws, qf);
+  else if (kf == 1) hipLaunchKernelGGL((score_mfma_kernel<1, HT>), grid, dim3(256), 0, stream, a, ws, qf);
+  else hipLaunchKernelGGL((score_mfma_kernel<0, HT>), grid, dim3(256), 0, stream, a, ws, qf);
+}
+
 hipError_t launch_index_score(const IndexArgs& a, hipStream_t stream) {
   if (a.n_q == 0 || a.max_elig == 0) return hipSuccess;
   Workspace ws = carve(a.ws, a.n_q, a.max_elig);
@@ -910,7 +949,8 @@ hipError_t launch_index_score(const IndexArgs& a, hipStream_t stream) {
     const int64_t max_pages = (a.max_elig + 63) / 64;
     const int64_t runs = (max_pages + kPagesPerBlock - 1) / kPagesPerBlock;
     const bool fp8s = a.cache.dtype == CSA_FP8_E4M3;
-    if (a.n_q >= kQueryFastMin && runs <= 65535) {  // many queries per launch: pages shared through LDS
+    const bool fp4 = a.cache.dtype == CSA_FP4_E2M1;
+    if (!fp4 && a.n_q >= kQueryFastMin && runs <= 65535) {  // many queries per launch: pages shared through LDS
       const dim3 g2(unsigned((a.n_q + kShareQ - 1) / kShareQ), unsigned(runs));
       switch (a.n_heads / 16) {
         case 1: if (fp8s) hipLaunchKernelGGL((score_shared_kernel<true, 1>), g2, dim3(kShareThreads), 0, stream, a, ws);
@@ -926,16 +966,12 @@ hipError_t launch_index_score(const IndexArgs& a, hipStream_t stream) {
     }
     const int qf = (a.n_q >= kQueryFastMin && runs <= 65535) ? 1 : 0;
     const dim3 grid = qf ? dim3(unsigned(a.n_q), unsigned(runs)) : dim3(unsigned(runs), unsigned(a.n_q));
-    const bool fp8 = a.cache.dtype == CSA_FP8_E4M3;
+    const int kf = a.cache.dtype == CSA_FP8_E4M3 ? 1 : (fp4 ? 2 : 0);
     switch (a.n_heads / 16) {
-      case 1: if (fp8) hipLaunchKernelGGL((score_mfma_kernel<true, 1>), grid, dim3(256), 0, stream, a, ws, qf);
-              else hipLaunchKernelGGL((score_mfma_kernel<false, 1>), grid, dim3(256), 0, stream, a, ws, qf); break;
-      case 2: if (fp8) hipLaunchKernelGGL((score_mfma_kernel<true, 2>), grid, dim3(256), 0, stream, a, ws, qf);
-              else hipLaunchKernelGGL((score_mfma_kernel<false, 2>), grid, dim3(256), 0, stream, a, ws, qf); break;
-      case 3: if (fp8) hipLaunchKernelGGL((score_mfma_kernel<true, 3>), grid, dim3(256), 0, stream, a, ws, qf);
-              else hipLaunchKernelGGL((score_mfma_kernel<false, 3>), grid, dim3(256), 0, stream, a, ws, qf); break;
-      default: if (fp8) hipLaunchKernelGGL((score_mfma_kernel<true, 4>), grid, dim3(256), 0, stream, a, ws, qf);
-               else hipLaunchKernelGGL((score_mfma_kernel<false, 4>), grid, dim3(256), 0, stream, a, ws, qf); break;
+      case 1: launch_score_mfma<1>(kf, grid, a, ws, qf, stream); break;
+      case 2: launch_score_mfma<2>(kf, grid, a, ws, qf, stream); break;
+      case 3: launch_score_mfma<3>(kf, grid, a, ws, qf, stream); break;
+      default: launch_score_mfma<4>(kf, grid, a, ws, qf, stream); break;
     }
   } else {
     const dim3 grid(unsigned((a.max_elig + 255) / 256), unsigned(a.n_q));

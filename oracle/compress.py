@@ -33,9 +33,9 @@ class Cache:
     window: int
     dim: int
     rope_dims: int
-    dtype: str               # "f32" | "bf16" | "fp8"
-    pages: np.ndarray        # [n_phys * 256/ratio][dim] (float32 | uint16 | uint8)
-    scales: np.ndarray       # [n_phys * 256/ratio] float32, or None unless fp8
+    dtype: str               # "f32" | "bf16" | "fp8" | "fp4"
+    pages: np.ndarray        # [n_phys * 256/ratio][dim] (float32 | uint16 | uint8); fp4: [..][dim/2] packed uint8
+    scales: np.ndarray       # [n_phys * 256/ratio] float32 (fp8), [..][dim/32] uint8 E8M0 (fp4), else None
     block_table: np.ndarray  # [batch][bt_stride] int32
 
 

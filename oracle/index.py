@@ -11,7 +11,8 @@ Sources:
 The score formula is not on the pages. Two forms are provided:
 * DOT   s_e = q . k_e                          (one indexer head)
 * WRELU s_e = sum_h w_h * max(0, q_h . k_e)    (H indexer heads, per-query head weights)
-fp8 keys are dequantised as scale_e * k8_e (R11). No extra scale is applied.
+fp8 keys are dequantised as scale_e * k8_e (R11), fp4 keys block by block as 2^X_b * e2m1
+(R25). No extra scale is applied.
 
 Top-k order (R12): score descending, then entry index ascending; -0.0 equals
 +0.0; NaN ranks below every number. min(k, n_elig) entries are kept and
@@ -33,7 +34,7 @@ def eligible_keys(cache: Cache, seq: int, q_pos: int) -> np.ndarray:
     slots = [paging.entry_slot(cache.block_table[seq], i, cache.ratio) for i in range(n)]
     if n == 0:
         return np.zeros((0, cache.dim))
-    sc = cache.scales[slots] if cache.dtype == codecs.FP8 else None
+    sc = cache.scales[slots] if cache.dtype in (codecs.FP8, codecs.FP4) else None
     return codecs.load_rows(cache.pages[slots], cache.dtype, sc)
 
 
