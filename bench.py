@@ -38,13 +38,14 @@ K_TOP, SWA = 512, 128
 LEN_LO, LEN_HI = 98304, 131072
 CONFIG_ID = 3
 
-# HBM bytes per launch of the index score kernel on the 128K bf16 (c3) and 1M fp8 (c4) decode workloads, from one
+# HBM bytes per launch of the index score kernel on the 128K bf16 (c3), 1M fp8 (c4) and 1M fp8 with MXFP4 indexer
+# (c4f) decode workloads, from one
 # FETCH_SIZE and one WRITE_SIZE counter run (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0 as calibrated on a 1 GiB device
 # copy). The figures hold only for the kernel source they were measured on; for any other source the traffic is
 # reported as unknown.
 SCORE_TRAFFIC = {"source": "long_context_compressed_compress_amd/csrc/index_topk.hip",
-                 "sha256": "028c8c131c6b9f479a1fa657dcda8998c5442465fffc9ac6f5571c9b58a46cdf",
-                 "bytes": {"c3": 245951381, "c4": 143574976}}
+                 "sha256": "620b9ba1361971607870b805a17bbfd9caf65b6fafe37008fb755afeda576d12",
+                 "bytes": {"c3": 245793509, "c4": 143573210, "c4f": 76385133}}
 
 
 def log(msg):
@@ -54,7 +55,7 @@ def log(msg):
 def score_traffic(workload):
     with open(os.path.join(ROOT, SCORE_TRAFFIC["source"]), "rb") as f:
         same = hashlib.sha256(f.read()).hexdigest() == SCORE_TRAFFIC["sha256"]
-    return SCORE_TRAFFIC["bytes"][workload] if same else None
+    return SCORE_TRAFFIC["bytes"].get(workload) if same else None
 
 
 def workload_lengths():
@@ -413,21 +414,27 @@ def _decode_bytes(n_elig, p, e_main, e_idx, k, with_index):
     return score, (4 * k if with_index else 0), att
 
 
-def run_c4(args, torch, csa):
+def run_c4(args, torch, csa, fp4_idx=False):
     """c4a decode at 1M: batch 4, query at 2^20, fp8 main / indexer / window caches with per-entry scales, pages of
-    every layer drawn uniformly from one 200 GB pool; top-512 + window 128."""
+    every layer drawn uniformly from one 200 GB pool; top-512 + window 128. fp4_idx: the indexer cache is MXFP4
+    (64 B of e2m1 codes + 4 E8M0 block exponents per entry) instead of fp8."""
     B, P = 4, 1 << 20
     nb = P // 256 + 1
     n_layers = args.layers_c4
-    per_page = 64 * D + 64 * D_IDX + 2 * 64 * 4
+    row_i = D_IDX // 2 if fp4_idx else D_IDX
+    per_page = 64 * D + 64 * row_i + 2 * 64 * 4
     n_phys = POOL_BYTES // per_page
     cpu_gen = torch.Generator()
     cpu_gen.manual_seed(4007)
     gen = _gen(torch, 4100)
     pool_m = torch.empty((n_phys * 64, D), dtype=torch.uint8, device="cuda")
     pool_ms = torch.empty((n_phys * 64,), dtype=torch.float32, device="cuda")
-    pool_i = torch.empty((n_phys * 64, D_IDX), dtype=torch.uint8, device="cuda")
-    pool_is = torch.empty((n_phys * 64,), dtype=torch.float32, device="cuda")
+    if fp4_idx:
+        pool_i = torch.empty((n_phys * 64, row_i), dtype=torch.uint8, device="cuda").view(torch.float4_e2m1fn_x2)
+        pool_is = torch.empty((n_phys * 64, D_IDX // 32), dtype=torch.uint8, device="cuda")
+    else:
+        pool_i = torch.empty((n_phys * 64, D_IDX), dtype=torch.uint8, device="cuda")
+        pool_is = torch.empty((n_phys * 64,), dtype=torch.float32, device="cuda")
     ids = torch.randperm(n_phys, generator=cpu_gen)[: n_layers * B * nb].to(torch.int32)
     rope = csa.rope_table(P + 2, R)
     lens = [P] * B
@@ -495,24 +502,28 @@ def run_c4(args, torch, csa):
                               rope, out, workspace=att_ws))
     total_ms, mode, modes = best_graph_mode(torch, layers, args.steps, args.warmup, lambda ly: step(ly, None), fn)
     total_ms = eager_ms if total_ms is None else total_ms
-    sb, kb, ab = (B * x for x in _decode_bytes(max_elig, P, D + 4, D_IDX + 4, K_TOP, True))
+    sb, kb, ab = (B * x for x in _decode_bytes(max_elig, P, D + 4, row_i + 4, K_TOP, True))
     del layers, pool_m, pool_ms, pool_i, pool_is, ws
     torch.cuda.empty_cache()
     path_ms = stage["score"] + stage["select"] + stage["attend"]
     score_gbs = sb / (stage["score"] * 1e-3) / 1e9
+    idx_desc = ("MXFP4 (e2m1 + E8M0 per 32 channels)" if fp4_idx else "fp8")
     return {
         "workload": f"c4a fp8 decode, batch {B}, context 2^20 (262143 compressed entries), query at 2^20, 64 heads x "
-                    "K=V 512 fp8 e4m3 + per-entry fp32 scale, indexer 64 heads x 128 fp8 WRELU, top-512 + window 128, "
-                    f"pages uniform over a 200 GB pool ({n_phys} 256-position pages), {n_layers} layers rotated",
+                    f"K=V 512 fp8 e4m3 + per-entry fp32 scale, indexer 64 heads x 128 {idx_desc} WRELU, top-512 + "
+                    f"window 128, pages uniform over a 200 GB pool ({n_phys} 256-position pages), {n_layers} layers "
+                    "rotated",
         "value": round(B * args.steps / (total_ms * 1e-3), 1), "unit": "queries/s",
         "ms_per_step": round(total_ms / args.steps, 5), "step_mode": STEP_MODES[mode],
         "modes_ms_per_step": {"eager_with_stage_events": round(eager_ms / args.steps, 5),
                               **{k: round(v / args.steps, 5) for k, v in modes.items()}},
-        "dtype": "fp8 e4m3 caches, bf16 queries, fp32 accumulate",
+        "dtype": ("fp8 e4m3 main cache, MXFP4 indexer cache" if fp4_idx else "fp8 e4m3 caches") +
+                 ", bf16 queries, fp32 accumulate",
         "stages_us": {k: round(v * 1e3, 2) for k, v in stage.items()},
-        "roofline": {"bound": "hbm", "kernel": "score_mfma_kernel<fp8> (index score)", "achieved": round(score_gbs, 1),
+        "roofline": {"bound": "hbm", "kernel": f"score_mfma_kernel<{'fp4' if fp4_idx else 'fp8'}> (index score)",
+                     "achieved": round(score_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(score_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": score_traffic("c4"),
+                     "traffic": score_traffic("c4f" if fp4_idx else "c4"),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated)",
                      "alg_bytes_per_launch": sb, "avg_launch_us": round(stage["score"] * 1e3, 2)},
         "gathered_path": {"hbm_gbs": round((sb + kb + ab) / (path_ms * 1e-3) / 1e9, 1),
@@ -689,7 +700,9 @@ def run_c5(args, torch, csa):
     }
 
 
-SIDE = {"c4": ("c4a_fp8_1m", run_c4), "c2": ("c128a_dense_64k", run_c2), "c5": ("prefill_chunk_256k", run_c5)}
+SIDE = {"c4": ("c4a_fp8_1m", run_c4),
+        "c4f": ("c4a_fp8_fp4idx_1m", lambda args, torch, csa: run_c4(args, torch, csa, fp4_idx=True)),
+        "c2": ("c128a_dense_64k", run_c2), "c5": ("prefill_chunk_256k", run_c5)}
 
 
 # ------------------------------------------------------------------ CPU baseline: the oracle, untuned
@@ -747,9 +760,10 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layers", type=int, default=5)
-    ap.add_argument("--workloads", default="c3,c4,c2,c5",
+    ap.add_argument("--workloads", default="c3,c4,c4f,c2,c5",
                     help="c3 = the headline 128K bf16 decode (always run); side workloads c4 = 1M fp8 decode, "
-                         "c2 = c128a dense 64K decode, c5 = 2048-token prefill chunk at 256K")
+                         "c4f = the same with an MXFP4 indexer cache, c2 = c128a dense 64K decode, "
+                         "c5 = 2048-token prefill chunk at 256K")
     ap.add_argument("--layers-c4", type=int, default=4)
     ap.add_argument("--layers-c2", type=int, default=32)
     ap.add_argument("--layers-c5", type=int, default=2)

@@ -221,3 +221,17 @@ def test_compress_pair_validation(L):
     assert call(kvb=None) == INVALID and call(kvb=FAKE + 4) == INVALID
     assert call(eps=-1.0) == INVALID
     assert call(batch=0) == OK
+
+
+def test_fp4_cache_validation(L):
+    """MXFP4 caches: E8M0 exponents required and 4-byte aligned; scored only by the dim-128 WRELU MFMA path with
+    a multiple of 16 heads; never an attention cache or a state/window dtype."""
+    fp4 = lambda **kw: _cache(dtype=csa.FP4, scales=FAKE, **kw)
+    assert _compress(L, cache=_cache(dtype=csa.FP4, scales=None)) == INVALID
+    assert _compress(L, cache=_cache(dtype=csa.FP4, scales=FAKE + 2)) == INVALID
+    assert _compress(L, cache=fp4(), state=_raw(dtype=csa.FP4)) == INVALID
+    assert _index(L, cache=fp4(), mode=csa.SCORE_DOT, heads=1, w=None) == UNSUPPORTED
+    assert _index(L, cache=fp4(), heads=8) == UNSUPPORTED
+    assert _index(L, cache=fp4(dim=64)) == UNSUPPORTED
+    assert _index(L, cache=fp4(ratio=128, window=128)) == UNSUPPORTED
+    assert _attend(L, cache=_cache(dim=512, dtype=csa.FP4, scales=FAKE)) == UNSUPPORTED
