@@ -314,6 +314,49 @@ def test_c4_1m_fp8_index_and_attend():
     _check_attend(g_out, g_lse, o_out, o_lse, "fp8", "c4 1M fp8")
 
 
+def test_c4_1m_fp4_indexer_index():
+    """The 1M decode with an MXFP4 indexer cache (the benchmark's fp4 variant): batch 4 at position 2^20, indexer pages
+    drawn uniformly from the 200 GB pool sized for fp8 main + fp4 indexer pages; exact-grid e2m1 keys with block
+    exponents -2..0 on the sequences' pages, code 6 with the E8M0 NaN exponent everywhere else; top-k sets and scores
+    bit-exact."""
+    _fresh()
+    B, P = 4, 1 << 20
+    nb = P // 256 + 1
+    per_page = 64 * D + 64 * (D_IDX // 2) + 2 * 64 * 4
+    n_phys = POOL_BYTES // per_page
+    _log(f"c4 1M fp4 indexer: batch {B}, {nb} blocks per sequence over a pool of {n_phys} pages")
+    bt = synth.random_block_table(synth.rng(C4 + 40, synth.STREAM_BT), B, nb, n_phys)
+    compact = np.arange(B * nb, dtype=np.int32).reshape(B, nb)
+    ids = gu.dev_i32(bt.reshape(-1)).long()
+    g = synth.rng(C4 + 40, synth.STREAM_IDX_KV)
+    rows = B * nb * 64
+    codes = (g.integers(0, 5, size=(rows, D_IDX)) | (g.integers(0, 2, size=(rows, D_IDX)) << 3)).astype(np.uint8)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    del codes
+    exps = (127 - g.integers(0, 3, size=(rows, D_IDX // 32))).astype(np.uint8)
+    g_ipages = torch.full((n_phys * 64, D_IDX // 2), 0x77, dtype=torch.uint8, device="cuda")
+    g_iexps = torch.full((n_phys * 64, D_IDX // 32), 0xFF, dtype=torch.uint8, device="cuda")
+    g_ipages.view(n_phys, 64 * D_IDX // 2)[ids] = gu.dev_u8(packed).view(B * nb, 64 * D_IDX // 2)
+    g_iexps.view(n_phys, 64 * D_IDX // 32)[ids] = gu.dev_u8(exps).view(B * nb, 64 * D_IDX // 32)
+    q_idx = si.grid_bf16(synth.grid_values(synth.rng(C4 + 40, synth.STREAM_QIDX), (B, H_IDX, D_IDX)))
+    w = si.grid_weights(synth.rng(C4 + 40, synth.STREAM_HEADW), (B, H_IDX))
+    pos = np.full(B, P, np.int64)
+    max_elig = paging.num_eligible(P, 4, 8)
+    o_idx, o_cnt, o_sc = oi.index_topk(oc.Cache(4, 8, D_IDX, R_IDX, "fp4", packed, exps, compact), np.arange(B), pos,
+                                       codecs.load_rows(q_idx, "bf16"), w, oi.WRELU, K_TOP)
+    del packed, exps
+    icache = csa.Cache(4, 8, D_IDX, R_IDX, g_ipages.view(torch.float4_e2m1fn_x2), gu.dev_i32(bt), g_iexps)
+    out, cnt, sc = _run_index(icache, gu.dev_i32(np.arange(B)), gu.dev_i32(pos), max_elig, gu.dev_bf16(q_idx),
+                              gu.dev_f32(w), K_TOP)
+    del icache, g_ipages, g_iexps
+    _fresh()
+    assert np.array_equal(cnt, o_cnt)
+    assert np.array_equal(out, o_idx)
+    m = o_idx >= 0
+    assert np.array_equal(sc[m].astype(np.float64), o_sc[m])
+    _log("c4 1M fp4 indexer: 4 top-k sets over 262143 entries bit-exact")
+
+
 # ------------------------------------------------------------------ c128a bf16 dense decode: batch 16, context 64K
 C2 = 2
 
