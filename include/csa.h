@@ -60,9 +60,10 @@ typedef enum {
   CSA_F32 = 0,
   CSA_BF16 = 1,
   CSA_FP8_E4M3 = 2, /* OCP e4m3fn (max 448), one fp32 scale per row: value = scale * e4m3(code) */
-  CSA_FP4_E2M1 = 3  /* OCP MXFP4, compressed caches only (the indexer cache; [P1] "Memory Efficiency" names
-                       an fp4 indexer cache): a row of D channels is D/2 bytes, channel 2j in the low nibble
-                       of byte j; every block of 32 channels has one E8M0 byte X+127 and value = 2^X * e2m1.
+  CSA_FP4_E2M1 = 3  /* OCP MXFP4, compressed caches only (the indexer cache; [P1] "DeepSeek V4 Attention
+                       Architecture" and [P2] "一、官方部署 Recipe" name an fp4 indexer cache): a row of D
+                       channels is D/2 bytes, channel 2j in the low nibble of byte j; every block of 32
+                       channels has one E8M0 byte X+127 and value = 2^X * e2m1.
                        X = floor(log2(block amax)) - 2 (0 for an all-zero block), elements rounded to
                        nearest-even and saturated at 6. D must be a multiple of 32. */
 } csa_dtype_t;

@@ -11,8 +11,8 @@ bf16 and e4m3fn are written from their format definitions:
   pattern S.1111.111 is NaN; largest finite magnitude 448; subnormal step 2^-9.
 Rounding is round-to-nearest, ties to even, applied once to the exact value.
 
-fp4 (the indexer cache; [P1] "Memory Efficiency" and the deployment flags name an fp4 indexer cache
-without a format; reading R25) is OCP MXFP4, written from the OCP Microscaling Formats v1.0
+fp4 (the indexer cache; [P1] "DeepSeek V4 Attention Architecture" (its memory figures) and the fp4
+indexer-cache flag of [P2] "一、官方部署 Recipe" name an fp4 indexer cache without a format; reading R25) is OCP MXFP4, written from the OCP Microscaling Formats v1.0
 definition: e2m1 elements (1 sign, 2 exponent bits with bias 1, 1 mantissa bit; magnitudes 0, 0.5, 1,
 1.5, 2, 3, 4, 6; no infinities or NaN), and one E8M0 scale 2^X per block of 32 consecutive channels of
 an entry, with X = floor(log2(amax of the block)) - 2 and elements rounded to nearest (ties to the even
