@@ -7,8 +7,9 @@
 //
 // Two launches on the caller's stream (csa_index_score, then csa_index_select):
 //   1. score     -- one workgroup per (query, run of entries). WRELU with 16*HT heads over dim-128
-//                   bf16 / fp8 keys runs on MFMA (v_mfma_f32_16x16x32_bf16: heads x 16 entries x 32 dims
-//                   per instruction, fp8 codes widened exactly to bf16); other shapes run on a VALU path.
+//                   bf16 / fp8 / MXFP4 keys runs on MFMA (v_mfma_f32_16x16x32_bf16: heads x 16 entries x 32
+//                   dims per instruction; fp8 and fp4 codes widened exactly to bf16, fp4 with its block's
+//                   power-of-two scale folded in); other shapes run on a VALU path (not for fp4).
 //                   Each score becomes an order-preserving 32-bit key; a 4096-bin LDS histogram of
 //                   the top 12 key bits is flushed into the query's global histogram.
 //   2. select    -- one 1024-thread workgroup per query: find the histogram bin that holds the k-th
