@@ -34,14 +34,16 @@ def _cache(ratio, dim, rope, pages_u8, scales_u8, bt):
     return csa.Cache(ratio, 8 if ratio == 4 else 128, dim, rope, pages_u8.view(torch.float4_e2m1fn_x2), bt, scales_u8)
 
 
-@pytest.mark.parametrize("ratio,dim,rope,ind,lens", [
-    (4, 128, 64, "bf16", [700, 259, 303]),
-    (4, 32, 16, "f32", [517, 6]),
-    (4, 128, 64, "f32", [300]),
-    (128, 64, 32, "bf16", [900, 255]),
+@pytest.mark.parametrize("ratio,dim,rope,ind,lens,zero_seq", [
+    (4, 128, 64, "bf16", [700, 259, 303], None),
+    (4, 32, 16, "f32", [517, 6], None),
+    (4, 128, 64, "f32", [300], None),
+    (128, 64, 32, "bf16", [900, 255], None),
+    (4, 512, 64, "bf16", [400, 129], None),
+    (4, 128, 64, "bf16", [300, 260], 1),   # sequence 1's raw rows are all zero: every block of its entries is zero
 ])
-def test_compress_insert_fp4_parity(ratio, dim, rope, ind, lens):
-    _log(f"fp4 compress ratio={ratio} dim={dim} rope={rope} in={ind} lens={lens}")
+def test_compress_insert_fp4_parity(ratio, dim, rope, ind, lens, zero_seq):
+    _log(f"fp4 compress ratio={ratio} dim={dim} rope={rope} in={ind} lens={lens} zero_seq={zero_seq}")
     seed = 500 + dim + ratio
     window = 8 if ratio == 4 else 128
     roles = window // ratio
@@ -54,6 +56,9 @@ def test_compress_insert_fp4_parity(ratio, dim, rope, ind, lens):
     kv = synth.normal_f32(g, (n, dim))
     lg = synth.normal_f32(g, (n, roles, dim))
     gamma = (1.0 + 0.25 * g.standard_normal(dim)).astype(np.float32)
+    if zero_seq is not None:
+        c0 = sum(lens[:zero_seq])
+        kv[c0:c0 + lens[zero_seq]] = 0.0
     if ind == "bf16":
         kv_s, lg_s = codecs.f64_to_bf16(kv), codecs.f64_to_bf16(lg)
     else:
@@ -98,6 +103,10 @@ def test_compress_insert_fp4_parity(ratio, dim, rope, ind, lens):
     ov = codecs.mxfp4_to_f64(o4.pages[written], o4.scales[written])
     step = np.repeat(np.ldexp(2.0, oe - 127), 32, axis=-1)  # largest e2m1 step (2) times the block scale
     assert np.all(np.abs(gv - ov) <= step), "fp4 values differ by more than one step"
+    if zero_seq is not None:
+        for i in range(paging.num_entries(lens[zero_seq], ratio, window)):
+            slot = paging.entry_slot(bt[zero_seq], i, ratio)
+            assert np.all(gp[slot] == 0) and np.all(gs[slot] == 127), f"zero entry {i}"
     same = np.mean(gp[written] == o4.pages[written])
     _log(f"fp4 identical code bytes {same:.5f}, identical exponents {np.mean(ge == oe):.5f}")
     assert same > 0.99
