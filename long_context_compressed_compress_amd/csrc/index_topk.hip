@@ -288,41 +288,49 @@ constexpr int kShareQ = 8;
 constexpr int kShareThreads = 64 * kShareQ;
 constexpr int kShareAhead = 4;
 
-template <bool FP8>
+// Page geometry per key format (KF as for PageBuf): a page is 64 rows of RAW_ROW bytes in HBM, copied in
+// CHUNKS 16-byte chunks (1024 bf16, 512 fp8, 256 fp4: threads >= CHUNKS copy none of an fp4 page).
+template <int KF>
 struct SharedPage {
-  static constexpr int ROW = FP8 ? 144 : 272;        // LDS bytes per page row (padded: rows start 4 banks apart)
-  static constexpr int CHUNKS = FP8 ? 512 : 1024;    // 16-byte chunks of one page in HBM
-  static constexpr int PER_T = CHUNKS / kShareThreads;  // chunks each thread copies
-  static constexpr int RAW_ROW = FP8 ? 128 : 256;    // bytes per page row in HBM
+  static constexpr int RAW_ROW = KF == 1 ? 128 : (KF == 2 ? 64 : 256);  // bytes per page row in HBM
+  static constexpr int ROW = RAW_ROW + 16;           // LDS bytes per page row (padded: rows start 4 banks apart)
+  static constexpr int CHUNKS = 64 * RAW_ROW / 16;   // 16-byte chunks of one page in HBM
+  static constexpr int PER_T = CHUNKS > kShareThreads ? CHUNKS / kShareThreads : 1;  // chunks each thread copies
 };
 
-// Page i of the run (clamped to the last one) -> this thread's 16-byte chunks (and, fp8, scale `tid` of the page).
-// A forced-inline function, so the caller's register arrays are never address-taken (a lambda called this way
-// was left out of line and its arrays went to scratch memory).
-template <bool FP8>
+// Page i of the run (clamped to the last one) -> this thread's 16-byte chunks and, for fp8 / fp4, scale word `tid`
+// of the page (fp8: the entry's fp32 scale bits; fp4: the entry's four E8M0 bytes). A forced-inline function, so
+// the caller's register arrays are never address-taken (a lambda called this way was left out of line and its
+// arrays went to scratch memory).
+template <int KF>
 __device__ __forceinline__ void fetch_shared_page(const IndexArgs& a, const int32_t* pg_phys, int i, int n_pg, int tid,
-                                                  uint4& c0, uint4& c1, float& sc) {
-  using L = SharedPage<FP8>;
+                                                  uint4& c0, uint4& c1, uint32_t& sc) {
+  using L = SharedPage<KF>;
   static_assert(L::PER_T == 1 || L::PER_T == 2, "one or two chunks per thread");
   const int ii = i < n_pg ? i : n_pg - 1;
   const int32_t phys = pg_phys[ii];
   const int64_t page = phys >= 0 ? phys : 0;
   const char* src = static_cast<const char*>(a.cache.pages) + page * 64 * L::RAW_ROW;
-  c0 = *reinterpret_cast<const uint4*>(src + tid * 16);
+  if constexpr (KF == 2) {
+    // threads >= CHUNKS load a copy of a chunk of the page and never store it
+    c0 = *reinterpret_cast<const uint4*>(src + (tid % L::CHUNKS) * 16);
+  } else {
+    c0 = *reinterpret_cast<const uint4*>(src + tid * 16);
+  }
   if (L::PER_T == 2) c1 = *reinterpret_cast<const uint4*>(src + (tid + kShareThreads) * 16);
-  if (FP8) sc = tid < 64 ? a.cache.scales[page * 64 + tid] : 0.f;
+  if (KF != 0) sc = tid < 64 ? reinterpret_cast<const uint32_t*>(a.cache.scales)[page * 64 + tid] : 0u;
 }
 
-template <bool FP8, int HT>
+template <int KF, int HT>
 __global__ void __launch_bounds__(kShareThreads, 1) score_shared_kernel(IndexArgs a, Workspace ws) {
-  using L = SharedPage<FP8>;
+  using L = SharedPage<KF>;
   constexpr int DIM = 128;
   constexpr int E = 64;
   // per-query histograms with two 16-bit bins per word (a workgroup counts at most kPagesPerBlock * 64 keys
   // per query)
   __shared__ uint32_t hist_s[kShareQ][kHistBins / 2];
   __shared__ __attribute__((aligned(16))) char page_s[2][E * L::ROW];
-  __shared__ float scale_s[2][E];
+  __shared__ uint32_t scale_s[2][E];
   __shared__ int32_t pg_phys[kPagesPerBlock];
   __shared__ int32_t w_seq[kShareQ];
   __shared__ int32_t w_npages[kShareQ];
@@ -351,11 +359,19 @@ __global__ void __launch_bounds__(kShareThreads, 1) score_shared_kernel(IndexArg
   {
     const int qq = q_ok ? q : 0;
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + int64_t(qq) * H * DIM;
+    if constexpr (KF == 2) {  // the fp4 channel order of score_page
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht)
+      for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        qa[ht][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + (ht * 16 + col) * DIM + ks * 32 + kg * 8));
+        for (int ks = 0; ks < 4; ++ks)
+          qa[ht][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + (ht * 16 + col) * DIM + kg * 32 + ks * 8));
+    } else {
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          qa[ht][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + (ht * 16 + col) * DIM + ks * 32 + kg * 8));
+    }
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
@@ -387,11 +403,12 @@ __global__ void __launch_bounds__(kShareThreads, 1) score_shared_kernel(IndexArg
       pg_phys[tid] = (phys >= 0 && phys < a.cache.n_phys) ? phys : -1;
     }
     __syncthreads();
-    // page i of the run -> registers: each thread copies PER_T 16-byte chunks (and fp8 threads < 64 one scale)
+    // page i of the run -> registers: each thread copies PER_T 16-byte chunks (and fp8 / fp4 threads < 64 one
+    // scale word)
     uint4 pre0[kShareAhead], pre1[kShareAhead];  // this thread's first and second chunk of each page in flight
-    float pre_sc[kShareAhead] = {};
+    uint32_t pre_sc[kShareAhead] = {};
 #pragma unroll
-    for (int s = 0; s < kShareAhead; ++s) fetch_shared_page<FP8>(a, pg_phys, s, n_pg, tid, pre0[s], pre1[s], pre_sc[s]);
+    for (int s = 0; s < kShareAhead; ++s) fetch_shared_page<KF>(a, pg_phys, s, n_pg, tid, pre0[s], pre1[s], pre_sc[s]);
     for (int i0 = 0; i0 < n_pg; i0 += kShareAhead) {
 #pragma unroll
       for (int s = 0; s < kShareAhead; ++s) {
@@ -402,25 +419,31 @@ __global__ void __launch_bounds__(kShareThreads, 1) score_shared_kernel(IndexArg
           for (int c = 0; c < L::PER_T; ++c) {
             const int chunk = tid + kShareThreads * c;
             const int row = chunk / (L::RAW_ROW / 16), off = (chunk % (L::RAW_ROW / 16)) * 16;
-            *reinterpret_cast<uint4*>(buf + row * L::ROW + off) = c == 0 ? pre0[s] : pre1[s];
+            if (L::CHUNKS >= kShareThreads || chunk < L::CHUNKS)
+              *reinterpret_cast<uint4*>(buf + row * L::ROW + off) = c == 0 ? pre0[s] : pre1[s];
           }
-          if (FP8 && tid < E) scale_s[i & 1][tid] = pre_sc[s];
-          fetch_shared_page<FP8>(a, pg_phys, i + kShareAhead, n_pg, tid, pre0[s], pre1[s], pre_sc[s]);
+          if (KF != 0 && tid < E) scale_s[i & 1][tid] = pre_sc[s];
+          fetch_shared_page<KF>(a, pg_phys, i + kShareAhead, n_pg, tid, pre0[s], pre1[s], pre_sc[s]);
           lds_barrier();
           const int64_t pg = pg_begin + i;
           if (active && pg < w_npages[wave]) {
-            PageBuf<FP8 ? 1 : 0> b;
+            PageBuf<KF> b;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
               const char* rowp = buf + (u * 16 + col) * L::ROW;
+              if constexpr (KF == 2) {
+                b.v[u] = *reinterpret_cast<const uint4*>(rowp + kg * 16);
+                b.sc[u] = e8m0_to_f32((scale_s[i & 1][u * 16 + col] >> (8 * kg)) & 0xFFu);
+              } else {
 #pragma unroll
-              for (int ks = 0; ks < 4; ++ks) {
-                if (FP8) reinterpret_cast<PageBuf<1>&>(b).v[u][ks] = *reinterpret_cast<const uint2*>(rowp + ks * 32 + kg * 8);
-                else reinterpret_cast<PageBuf<0>&>(b).v[u][ks] = *reinterpret_cast<const uint4*>(rowp + ks * 64 + kg * 16);
+                for (int ks = 0; ks < 4; ++ks) {
+                  if constexpr (KF == 1) b.v[u][ks] = *reinterpret_cast<const uint2*>(rowp + ks * 32 + kg * 8);
+                  else b.v[u][ks] = *reinterpret_cast<const uint4*>(rowp + ks * 64 + kg * 16);
+                }
+                if constexpr (KF == 1) b.sc[u] = __uint_as_float(scale_s[i & 1][u * 16 + col]);
               }
-              if (FP8) reinterpret_cast<PageBuf<1>&>(b).sc[u] = scale_s[i & 1][u * 16 + col];
             }
-            const uint32_t key = score_page<FP8 ? 1 : 0, HT>(b, qa, wv, kg);
+            const uint32_t key = score_page<KF, HT>(b, qa, wv, kg);
             const int64_t e = pg * E + lane;
             if (e < n_elig) {
               const uint32_t k2 = pg_phys[i] >= 0 ? key : 0u;
@@ -935,6 +958,13 @@ hipError_t launch_index_clear(void* ws_base, int n_q, hipStream_t stream) {
 }
 
 template <int HT>
+void launch_score_shared(int kf, dim3 grid, const IndexArgs& a, const Workspace& ws, hipStream_t stream) {
+  if (kf == 2) hipLaunchKernelGGL((score_shared_kernel<2, HT>), grid, dim3(kShareThreads), 0, stream, a, ws);
+  else if (kf == 1) hipLaunchKernelGGL((score_shared_kernel<1, HT>), grid, dim3(kShareThreads), 0, stream, a, ws);
+  else hipLaunchKernelGGL((score_shared_kernel<0, HT>), grid, dim3(kShareThreads), 0, stream, a, ws);
+}
+
+template <int HT>
 void launch_score_mfma(int kf, dim3 grid, const IndexArgs& a, const Workspace& ws, int qf, hipStream_t stream) {
   if (kf == 2) hipLaunchKernelGGL((score_mfma_kernel<2, HT>), grid, dim3(256), 0, stream, a, ws, qf);
   else if (kf == 1) hipLaunchKernelGGL((score_mfma_kernel<1, HT>), grid, dim3(256), 0, stream, a, ws, qf);
@@ -951,23 +981,19 @@ hipError_t launch_index_score(const IndexArgs& a, hipStream_t stream) {
     const int64_t runs = (max_pages + kPagesPerBlock - 1) / kPagesPerBlock;
     const bool fp8s = a.cache.dtype == CSA_FP8_E4M3;
     const bool fp4 = a.cache.dtype == CSA_FP4_E2M1;
-    if (!fp4 && a.n_q >= kQueryFastMin && runs <= 65535) {  // many queries per launch: pages shared through LDS
+    const int kf = fp8s ? 1 : (fp4 ? 2 : 0);
+    if (a.n_q >= kQueryFastMin && runs <= 65535) {  // many queries per launch: pages shared through LDS
       const dim3 g2(unsigned((a.n_q + kShareQ - 1) / kShareQ), unsigned(runs));
       switch (a.n_heads / 16) {
-        case 1: if (fp8s) hipLaunchKernelGGL((score_shared_kernel<true, 1>), g2, dim3(kShareThreads), 0, stream, a, ws);
-                else hipLaunchKernelGGL((score_shared_kernel<false, 1>), g2, dim3(kShareThreads), 0, stream, a, ws); break;
-        case 2: if (fp8s) hipLaunchKernelGGL((score_shared_kernel<true, 2>), g2, dim3(kShareThreads), 0, stream, a, ws);
-                else hipLaunchKernelGGL((score_shared_kernel<false, 2>), g2, dim3(kShareThreads), 0, stream, a, ws); break;
-        case 3: if (fp8s) hipLaunchKernelGGL((score_shared_kernel<true, 3>), g2, dim3(kShareThreads), 0, stream, a, ws);
-                else hipLaunchKernelGGL((score_shared_kernel<false, 3>), g2, dim3(kShareThreads), 0, stream, a, ws); break;
-        default: if (fp8s) hipLaunchKernelGGL((score_shared_kernel<true, 4>), g2, dim3(kShareThreads), 0, stream, a, ws);
-                 else hipLaunchKernelGGL((score_shared_kernel<false, 4>), g2, dim3(kShareThreads), 0, stream, a, ws); break;
+        case 1: launch_score_shared<1>(kf, g2, a, ws, stream); break;
+        case 2: launch_score_shared<2>(kf, g2, a, ws, stream); break;
+        case 3: launch_score_shared<3>(kf, g2, a, ws, stream); break;
+        default: launch_score_shared<4>(kf, g2, a, ws, stream); break;
       }
       return hipGetLastError();
     }
     const int qf = (a.n_q >= kQueryFastMin && runs <= 65535) ? 1 : 0;
     const dim3 grid = qf ? dim3(unsigned(a.n_q), unsigned(runs)) : dim3(unsigned(runs), unsigned(a.n_q));
-    const int kf = a.cache.dtype == CSA_FP8_E4M3 ? 1 : (fp4 ? 2 : 0);
     switch (a.n_heads / 16) {
       case 1: launch_score_mfma<1>(kf, grid, a, ws, qf, stream); break;
       case 2: launch_score_mfma<2>(kf, grid, a, ws, qf, stream); break;

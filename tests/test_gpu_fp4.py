@@ -3,7 +3,8 @@
 * compress_insert into an fp4 cache: E8M0 exponents and e2m1 codes equal the oracle's wherever the fp32
   row is not within rounding distance of a decision (a power-of-two block amax, an e2m1 midpoint); every
   dequantised element is within one e2m1 step of the oracle's.
-* index score + select over fp4 pages: exact-grid keys (e2m1 codes with block exponents -2..0), queries
+* index score + select over fp4 pages (few queries: the per-query kernel; >= 256 queries: the kernel whose
+  workgroups share each page among 8 queries): exact-grid keys (e2m1 codes with block exponents -2..0), queries
   and weights make every score exact in fp32, so top-k sets and scores are bit-exact.
 * compress_insert_pair with an fp8 main cache and an fp4 indexer cache equals the two separate calls.
 """
@@ -134,7 +135,8 @@ def _grid_fp4_cache(cfg, positions, spare=3):
     (16, 64, [5000, 300]),
     (64, 2048, [12000, 8203]),
     (32, 512, [300000, 70000]),                       # > 2^16 entries: the mark-pass select
-    (64, 512, [300 + 13 * i for i in range(270)]),   # many queries: the query-first grid
+    (64, 512, [300 + 13 * i for i in range(270)]),   # many queries: pages shared through LDS by 8 queries
+    (16, 100, [5000 - 17 * i for i in range(260)]),  # the same with one 16-head tile
 ])
 def test_index_topk_fp4_exact_grid_bit_exact(heads, k, positions):
     _log(f"fp4 index grid H={heads} k={k} n_q={len(positions)} max_pos={max(positions)}")
