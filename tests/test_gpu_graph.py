@@ -1,8 +1,8 @@
 """The decode step captured in a HIP graph, with the main-cache compress_insert on a second stream beside the
 indexer pipeline (the way the benchmark runs it), replays to the eager result.
 
-Shapes are the real ones (64 heads x K=V 512 bf16, indexer 64 heads x 128 WRELU, top-512 + window 128) at a few
-short contexts. Each replay runs after eager work of its own and a synchronisation; every replay's top-k lists,
+Shapes are the real ones (64 heads x K=V 512 bf16, indexer 64 heads x 128 WRELU in bf16 or MXFP4, top-512 +
+window 128) at a few short contexts. Each replay runs after eager work of its own and a synchronisation; every replay's top-k lists,
 attention output and written cache rows must equal the eager step's bit for bit (every kernel is
 deterministic), and the eager step itself is checked against the oracle by the parity tests.
 """
@@ -27,7 +27,7 @@ def _log(msg):
 
 
 class _Layer:
-    def __init__(self, seed):
+    def __init__(self, seed, fp4_idx=False):
         dev = "cuda"
         g = torch.Generator(device=dev)
         g.manual_seed(seed)
@@ -48,7 +48,15 @@ class _Layer:
         self.tail = tail.to(dev)
         bf = torch.bfloat16
         self.cache = csa.Cache(4, 8, D, R, torch.zeros((n_phys * 64, D), dtype=bf, device=dev), self.bt)
-        self.icache = csa.Cache(4, 8, D_IDX, R, torch.zeros((n_phys * 64, D_IDX), dtype=bf, device=dev), self.bt)
+        if fp4_idx:  # MXFP4 indexer cache: packed codes and E8M0 block exponents
+            ipages = torch.zeros((n_phys * 64, D_IDX // 2), dtype=torch.uint8, device=dev)
+            self.iscales = torch.zeros((n_phys * 64, D_IDX // 32), dtype=torch.uint8, device=dev)
+            self.icache = csa.Cache(4, 8, D_IDX, R, ipages.view(torch.float4_e2m1fn_x2), self.bt, self.iscales)
+        else:
+            ipages = torch.zeros((n_phys * 64, D_IDX), dtype=bf, device=dev)
+            self.iscales = torch.zeros((1,), dtype=torch.uint8, device=dev)  # unused
+            self.icache = csa.Cache(4, 8, D_IDX, R, ipages, self.bt)
+        self.ipages_u8 = ipages.view(torch.uint8)
         z = lambda *s: torch.zeros(s, dtype=bf, device=dev)
         self.state = csa.Raw(D, 2, z(2 * B * 256, D), self.tail, z(2 * B * 256, 2, D))
         self.istate = csa.Raw(D_IDX, 2, z(2 * B * 256, D_IDX), self.tail, z(2 * B * 256, 2, D_IDX))
@@ -94,7 +102,7 @@ class _Layer:
 
     def results(self):
         torch.cuda.synchronize()
-        return [t.clone() for t in (self.topk, self.out, self.lse, self.cache.pages, self.icache.pages,
+        return [t.clone() for t in (self.topk, self.out, self.lse, self.cache.pages, self.ipages_u8, self.iscales,
                                     self.state.kv_pages, self.istate.kv_pages)]
 
     def poison(self):
@@ -105,16 +113,20 @@ class _Layer:
         for L, b in zip(self.lens, range(B)):
             if L % 4 == 3:  # the decode token completes entry (L - 7) / 4
                 i = (L - 7) // 4
-                for c in (self.cache, self.icache):
-                    c.pages[int(self.bt[b, i // 64]) * 64 + i % 64].fill_(float("nan"))
+                row = int(self.bt[b, i // 64]) * 64 + i % 64
+                self.cache.pages[row].fill_(float("nan"))
+                self.ipages_u8[row].fill_(0xA5)
+                if self.iscales.shape[0] > row:
+                    self.iscales[row].fill_(0xA5)
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("fp4_idx", [False, True])
+def test_graph_replay_matches_eager(fp4_idx):
     torch.cuda.synchronize()
-    ly = _Layer(81)
-    other = _Layer(82)
+    ly = _Layer(81, fp4_idx)
+    other = _Layer(82, fp4_idx)
     side = torch.cuda.Stream()
-    _log(f"graph replay: contexts {ly.lens}")
+    _log(f"graph replay: contexts {ly.lens}, fp4 indexer cache {fp4_idx}")
     ly.step(side)
     ref = ly.results()
     assert int((ref[0] >= 0).sum()) == B * K_TOP
@@ -128,7 +140,7 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         g.replay()
         got = ly.results()
-        for name, a, b in zip(["topk", "out", "lse", "pages", "idx pages", "state", "idx state"], got, ref):
+        for name, a, b in zip(["topk", "out", "lse", "pages", "idx pages", "idx scales", "state", "idx state"], got, ref):
             assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
                                b.view(torch.uint8) if b.dtype == torch.bfloat16 else b), f"replay {rep}: {name} differs"
         _log(f"replay {rep}: identical to the eager step")
