@@ -737,15 +737,43 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(IndexArgs a, Worksp
   // longer queries keep their bitmap in the workspace
   uint32_t* bitmap = n_words <= kBitmapLds ? bitmap_s : bits_g;
   uint32_t* hist2_g = ws.hist2 + int64_t(q) * kHistBins;
+  // after a mark pass every global read of the set-up (score histogram, bitmap words, second histogram) is
+  // issued here, before any of them is used, so they cost one round trip together
+  constexpr int PER = kHistBins / kSelThreads;
+  const uint32_t* hist = ws.hist + int64_t(q) * kHistBins;
+  uint32_t h[PER];
   if (pre) {
-    if (bitmap != bits_g)
-      for (int64_t w = tid; w < n_words; w += kSelThreads) bitmap[w] = bits_g[w];
-    for (int b = tid; b < kHistBins; b += kSelThreads) {
-      hist2[b] = hist2_g[b];
-      hist2_g[b] = 0u;  // left zero for the next mark pass
+#pragma unroll
+    for (int j = 0; j < PER; ++j) h[j] = hist[tid * PER + j];
+  }
+  if (pre) {
+    constexpr int BW = kBitmapLds / kSelThreads;  // bitmap words per thread when the bitmap fits LDS
+    const bool lds_bits = bitmap != bits_g;
+    uint32_t bw[BW], h2[PER];
+    if (lds_bits) {
+#pragma unroll
+      for (int j = 0; j < BW; ++j) {
+        const int64_t w = tid + int64_t(kSelThreads) * j;
+        bw[j] = bits_g[w < n_words ? w : 0];  // clamped, unconditional load
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) h2[j] = hist2_g[tid + kSelThreads * j];
+    const uint32_t nc = tid == 0 ? ws.ncand[q] : 0u;
+    if (lds_bits) {
+#pragma unroll
+      for (int j = 0; j < BW; ++j) {
+        const int64_t w = tid + int64_t(kSelThreads) * j;
+        if (w < n_words) bitmap[w] = bw[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      hist2[tid + kSelThreads * j] = h2[j];
+      hist2_g[tid + kSelThreads * j] = 0u;  // left zero for the next mark pass
     }
     if (tid == 0) {
-      s_cnt[1] = ws.ncand[q];
+      s_cnt[1] = nc;
       ws.ncand[q] = 0u;
     }
   } else {
@@ -757,12 +785,13 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(IndexArgs a, Worksp
   // ---- boundary bin of the score histogram: largest b0 with count(bins >= b0) >= kk
   int b0 = -1;
   if (n_elig > a.k) {
-    const uint32_t* hist = ws.hist + int64_t(q) * kHistBins;
-    constexpr int PER = kHistBins / kSelThreads;
-    uint32_t h[PER];
+    if (!pre) {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) h[j] = hist[tid * PER + j];
+    }
     uint32_t local = 0;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) { h[j] = hist[tid * PER + j]; local += h[j]; }
+    for (int j = 0; j < PER; ++j) local += h[j];
     uint32_t excl;
     const uint32_t total = block_excl_scan(local, tmp, &excl);
     uint32_t run = total - excl - local;
