@@ -219,3 +219,104 @@ class Step:
 
     def q_f64(self, arr, dtype):
         return codecs.load_rows(arr, "f32" if dtype == "f32" else "bf16")
+
+    # ------------------------------------------------------------------ unrounded oracle rows
+    def run_oracle_unrounded(self):
+        """The oracle's compressed rows before storage rounding (an fp32 cache fed the same raw tokens)."""
+        c = self.cfg
+        zeros, lens = [0] * self.B, list(c.lens)
+        ends = [L + 1 for L in lens]
+        self.o_cache32 = self._o_cache(c.dim, c.rope_dims, "f32")
+        st = self._o_state(c.dim, self.coff)
+        self._o_compress(self.o_cache32, st, self.kv, self.lg, self.gamma, self.o_rope, zeros, lens)
+        self._o_compress(self.o_cache32, st, self.kv, self.lg, self.gamma, self.o_rope, lens, ends)
+        if c.indexer:
+            self.o_icache32 = self._o_cache(c.idx_dim, c.idx_rope, "f32")
+            st = self._o_state(c.idx_dim, 2)
+            self._o_compress(self.o_icache32, st, self.ikv, self.ilg, self.igamma, self.o_irope, zeros, lens)
+            self._o_compress(self.o_icache32, st, self.ikv, self.ilg, self.igamma, self.o_irope, lens, ends)
+
+    def gpu_attend_with(self, topk: np.ndarray) -> np.ndarray:
+        """GPU attention of every query over a given top-k list (the oracle's), on the GPU-built caches."""
+        c = self.cfg
+        out = torch.full((self.B, c.heads, c.dim), -7.0, dtype=torch.float32, device="cuda")
+        lse = torch.full((self.B, c.heads), -7.0, dtype=torch.float32, device="cuda")
+        csa.attend(self.g_cache, self.g_swa, c.swa_window, gu.dev_i32(self.q_seq), gu.dev_i32(self.q_pos),
+                   _dev_in(self.q, self.q_dtype), gu.dev_i32(topk), self.max_elig, self.scale, True, self.g_rope, out,
+                   lse)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), lse.cpu().numpy()
+
+
+def _stored(cache, rows):
+    return cache.pages[rows], (cache.scales[rows] if cache.scales is not None else None)
+
+
+def verify(st: Step, out_tol: float, lse_tol: float, log=None) -> dict:
+    """Check a whole decode step of the GPU library against the oracle run from the same raw tokens.
+
+    * entry counts and slots of both compress calls: bit-exact;
+    * every eligible row of the main and indexer caches: within the rounding-aware element bound of
+      gpu_util.stored_elem_bound (codes equal except where the unrounded value sits at a rounding midpoint);
+    * top-k sets: equal to the oracle's except for swaps certified as near-ties, where each score may differ
+      by the fp32 accumulation bound plus the storage bound of the indexer rows (any other difference fails);
+    * attention output of every sequence within out_tol (max over rows of max|d| / max|ref|) and its lse:
+      sequences whose GPU set equals the oracle's are compared as they came out of the GPU chain; a sequence
+      whose set differs by certified swaps is re-attended on the GPU over the oracle's set (an oracle
+      output fed to the GPU, never the reverse) and compared the same way.
+    """
+    c = st.cfg
+    log = log or (lambda m: None)
+    res = {"swaps": 0, "reattended": []}
+    window = st.window
+    for (gs, gc), (os_, oc_) in ((st.g_prefill, st.o_prefill), (st.g_decode, st.o_decode)):
+        assert np.array_equal(gc.cpu().numpy(), oc_)
+        assert np.array_equal(gs.cpu().numpy()[:, : os_.shape[1]], os_[:, : gs.shape[1]])
+    st.run_oracle_unrounded()
+    gmain = (gu.host_store(st.g_cache.pages), st.g_cache.scales.cpu().numpy() if st.g_cache.scales is not None else None)
+    if c.indexer:
+        gidx = (gu.host_store(st.g_icache.pages),
+                st.g_icache.scales.cpu().numpy() if st.g_icache.scales is not None else None)
+    gi = st.g_topk.cpu().numpy() if c.indexer else None
+    gcnt = st.g_cnt.cpu().numpy() if c.indexer else None
+    g_out = st.g_out.cpu().numpy()
+    g_lse = st.g_lse.cpu().numpy()
+    differing = []
+    for b in range(st.B):
+        p = int(st.q_pos[b])
+        n = paging.num_eligible(p, c.ratio, window)
+        rows = np.array([paging.entry_slot(st.bt[b], i, c.ratio) for i in range(n)], np.int64)
+        if n:
+            rp, rs = _stored(st.o_cache, rows)
+            gu.stored_elem_bound(c.cache_dtype, st.o_cache32.pages[rows], rp, rs, gmain[0][rows],
+                                 None if gmain[1] is None else gmain[1][rows])
+        if not c.indexer:
+            continue
+        if n:
+            rp, rs = _stored(st.o_icache, rows)
+            u = gu.stored_elem_bound(c.idx_dtype, st.o_icache32.pages[rows], rp, rs, gidx[0][rows],
+                                     None if gidx[1] is None else gidx[1][rows])
+            keys = codecs.load_rows(rp, c.idx_dtype, rs)
+        else:
+            u = keys = np.zeros((0, c.idx_dim))
+        qi = st.q_f64(st.q_idx, st.qi_dtype)[b]
+        w = None if st.head_w is None else st.head_w[b].astype(np.float64)
+        s = oi.scores(keys, qi, w, c.mode)
+        delta = gu.wrelu_score_delta(keys, u, qi, w, c.mode, c.idx_dim, c.idx_heads)
+        swaps = gu.check_topk_near_ties(gi[b], gcnt[b], s, c.k, delta)
+        res["swaps"] += swaps
+        if not np.array_equal(gi[b], st.o_topk[b]):
+            differing.append(b)
+    res["attend_err"] = gu.rowwise_rel_err(np.delete(g_out, differing, axis=0), np.delete(st.o_out, differing, axis=0)) \
+        if len(differing) < st.B else 0.0
+    lse_ok = [b for b in range(st.B) if b not in differing]
+    assert np.allclose(g_lse[lse_ok], st.o_lse[lse_ok], rtol=0, atol=lse_tol), "lse differs from the oracle's"
+    if differing:
+        re, re_lse = st.gpu_attend_with(st.o_topk)
+        res["reattended"] = differing
+        res["reattend_err"] = gu.rowwise_rel_err(re[differing], st.o_out[differing])
+        assert res["reattend_err"] <= out_tol, res
+        assert np.allclose(re_lse[differing], st.o_lse[differing], rtol=0, atol=lse_tol)
+    log(f"chain: {res}")
+    assert res["attend_err"] <= out_tol, res
+    return res

@@ -518,28 +518,18 @@ def test_c1_chain_end_to_end():
 
 @pytest.mark.parametrize("cache_dtype", ["bf16", "fp8"])
 def test_bf16_chain_end_to_end(cache_dtype):
-    """c4a decode with bf16 raw tokens, D 512 / 64 heads, indexer 64 heads x 128 (WRELU), top-512 + window."""
+    """c4a decode with bf16 raw tokens, D 512 / 64 heads, indexer 64 heads x 128 (WRELU), top-512 + window.
+
+    Strict: counts and slots bit-exact; every eligible cache row within the rounding-aware storage bound; the
+    top-k sets equal up to certified near-ties (scores differing by at most fp32 accumulation plus the bound
+    on the stored keys); attention of every sequence within the benchmark spec's tolerance (2e-3 bf16, 5e-2 fp8)."""
     _log(f"bf16 chain cache={cache_dtype}")
+    from tests.chain import verify
     cfg = StepConfig(seed=71, ratio=4, lens=[6000, 4093, 811], dim=512, rope_dims=64, heads=64, cache_dtype=cache_dtype,
                      in_dtype="bf16", indexer=True, idx_dim=128, idx_rope=64, idx_heads=64, idx_dtype=cache_dtype,
                      mode=oi.WRELU, k=512)
     st = Step(cfg)
     st.run_gpu()
     st.run_oracle()
-    gi, gc = st.g_topk.cpu().numpy(), st.g_cnt.cpu().numpy()
-    same = 0
-    for b in range(st.B):
-        n = paging.num_eligible(int(st.q_pos[b]), 4, 8)
-        assert gc[b] == min(512, n)
-        ov = set(st.o_topk[b][: st.o_cnt[b]].tolist())
-        gv = set(gi[b][: gc[b]].tolist())
-        overlap = len(ov & gv) / max(len(ov), 1)
-        _log(f"seq {b}: top-k overlap with the oracle chain {overlap:.4f}")
-        # the caches themselves differ by storage rounding, so near the boundary the sets may differ a little
-        assert overlap >= 0.97
-        same += gv == ov
-        if gv == ov:
-            err = gu.rowwise_rel_err(st.g_out.cpu().numpy()[b], st.o_out[b])
-            _log(f"seq {b}: end-to-end rowwise err {err:.3e}")
-            assert err <= TOL[cache_dtype] * 2
-    assert same >= 1
+    res = verify(st, TOL[cache_dtype], 1e-4, log=_log)
+    _log(f"certified swaps {res['swaps']}, re-attended sequences {res['reattended']}")
