@@ -17,7 +17,8 @@
  *
  * Conventions
  *   - Every pointer is DEVICE memory unless marked [host]. Every call is asynchronous on
- *     `stream`; the library never synchronises, allocates, frees or keeps global state.
+ *     `stream`; the library never synchronises, allocates or frees. Its only global state is the
+ *     fixed per-GPU scratch array of csa_index_topk_noalloc.
  *   - The caller owns every buffer (pages, block tables, inputs, outputs, workspaces).
  *   - Arguments are validated on the host BEFORE any HIP call; an invalid call returns a
  *     non-zero status and touches nothing. A failed launch returns CSA_ERR_HIP and
@@ -53,7 +54,8 @@ typedef enum {
   CSA_ERR_INVALID_ARG = 1, /* null pointer, bad size, bad enum, inconsistent descriptor */
   CSA_ERR_UNSUPPORTED = 2, /* valid request with no kernel (dtype combination, head count, dim) */
   CSA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the matching *_workspace() size */
-  CSA_ERR_HIP = 4          /* a HIP launch failed; see csa_last_hip_error() */
+  CSA_ERR_HIP = 4,         /* a HIP launch failed; see csa_last_hip_error() */
+  CSA_ERR_TOO_LARGE = 5    /* the request needs more than the fixed scratch of a no-allocation entry point */
 } csa_status_t;
 
 typedef enum {
@@ -196,6 +198,30 @@ csa_status_t csa_index_select(const csa_cache_t* idx_cache, int32_t n_q, const i
                               const int32_t* q_pos, int64_t max_elig, int32_t k, int32_t* out_idx,
                               int32_t* out_count, float* out_scores, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * csa_index_topk_noalloc -- csa_index_topk for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. Same arguments, meaning and
+ * results as csa_index_topk, without the workspace: the score keys, histograms, candidate list and
+ * bitmap live in a library-owned static device array of CSA_NOALLOC_SCRATCH_BYTES (64 MiB), one per
+ * GPU the library runs on, held until the process ends. No call allocates or frees anything.
+ *   - A request whose csa_index_topk_workspace(n_q, max_elig, k, n_heads) exceeds CSA_NOALLOC_SCRATCH_BYTES
+ *     returns CSA_ERR_TOO_LARGE before any HIP call (e.g. 32 queries of 32767 entries need 13.7 MB, 4 of
+ *     262143 need 12.7 MB; a 4096-query prefill chunk does not fit).
+ *   - Each call first zero-fills the histogram region it uses (a fill kernel on `stream`), then runs the
+ *     score and select launches of csa_index_topk on the scratch.
+ *   - All calls on one GPU share that GPU's scratch and it keeps the last call's contents: calls that
+ *     overlap on one GPU (on different streams, or from different threads without ordering) race and
+ *     give undefined results. Order them on one stream or with events.
+ *   - The first call on a device (the current device) looks up that device's copy of the array
+ *     (hipGetSymbolAddress); a failed lookup returns CSA_ERR_HIP.
+ * ------------------------------------------------------------------------------------------- */
+#define CSA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+csa_status_t csa_index_topk_noalloc(const csa_cache_t* idx_cache, int32_t n_q, const int32_t* q_seq,
+                                    const int32_t* q_pos, int64_t max_elig, const void* q_idx,
+                                    csa_dtype_t q_dtype, int32_t n_heads, const float* head_w,
+                                    csa_score_t mode, int32_t k, int32_t* out_idx, int32_t* out_count,
+                                    float* out_scores, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * csa_attend -- shared-K=V attention over selected compressed entries plus the raw sliding window.

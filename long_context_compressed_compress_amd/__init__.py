@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(_PKG, "libcsa.so")
 F32, BF16, FP8, FP4 = 0, 1, 2, 3
 SCORE_DOT, SCORE_WRELU = 0, 1
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "workspace missing or too small",
-          4: "HIP launch failed"}
+          4: "HIP launch failed", 5: "request exceeds the fixed scratch of a no-allocation entry point"}
+NOALLOC_SCRATCH_BYTES = 64 << 20  # CSA_NOALLOC_SCRATCH_BYTES
 
 
 class CsaError(RuntimeError):
@@ -65,6 +66,7 @@ def lib() -> ctypes.CDLL:
             "csa_index_topk_workspace": (SZ, [I32, I64, I32, I32]),
             "csa_index_topk": (I32, [CP, I32, P, P, I64, P, I32, I32, P, I32, I32, P, P, P, P, SZ, P]),
             "csa_index_workspace_clear": (I32, [P, SZ, I32, P]),
+            "csa_index_topk_noalloc": (I32, [CP, I32, P, P, I64, P, I32, I32, P, I32, I32, P, P, P, P]),
             "csa_index_score": (I32, [CP, I32, P, P, I64, P, I32, I32, P, I32, I32, P, SZ, P]),
             "csa_index_select": (I32, [CP, I32, P, P, I64, I32, P, P, P, P, SZ, P]),
             "csa_attend_workspace": (SZ, [I32, I32, I32, I32]),
@@ -210,6 +212,19 @@ def index_topk(cache: Cache, q_seq: torch.Tensor, q_pos: torch.Tensor, max_elig:
         ctypes.byref(cd), n_q, _ptr(q_seq), _ptr(q_pos), max_elig, _ptr(q_idx), dtype_code(q_idx), n_heads,
         _ptr(head_w), mode, k, _ptr(out_idx), _ptr(out_count), _ptr(out_scores), _ptr(workspace),
         workspace.numel(), _stream(stream)))
+
+
+def index_topk_noalloc(cache: Cache, q_seq: torch.Tensor, q_pos: torch.Tensor, max_elig: int, q_idx: torch.Tensor,
+                       head_w: Optional[torch.Tensor], mode: int, k: int, out_idx: torch.Tensor,
+                       out_count: Optional[torch.Tensor] = None, out_scores: Optional[torch.Tensor] = None,
+                       stream=None) -> None:
+    """csa_index_topk_noalloc: index_topk on the library's fixed per-GPU scratch; allocates nothing (the caller
+    passes inputs and outputs)."""
+    n_q, n_heads = q_idx.shape[0], q_idx.shape[1]
+    cd = cache.desc()
+    _check("csa_index_topk_noalloc", lib().csa_index_topk_noalloc(
+        ctypes.byref(cd), n_q, _ptr(q_seq), _ptr(q_pos), max_elig, _ptr(q_idx), dtype_code(q_idx), n_heads,
+        _ptr(head_w), mode, k, _ptr(out_idx), _ptr(out_count), _ptr(out_scores), _stream(stream)))
 
 
 def index_score(cache: Cache, q_seq: torch.Tensor, q_pos: torch.Tensor, max_elig: int, q_idx: torch.Tensor,

@@ -2,6 +2,8 @@
 // dispatch to the kernel launchers. Declarations and semantics: include/csa.h.
 #include <math.h>
 
+#include <mutex>
+
 #include "csa_internal.h"
 
 namespace {
@@ -50,6 +52,7 @@ const char* csa_status_string(csa_status_t s) {
     case CSA_ERR_UNSUPPORTED: return "unsupported configuration";
     case CSA_ERR_WORKSPACE: return "workspace missing or too small";
     case CSA_ERR_HIP: return "HIP launch failed";
+    case CSA_ERR_TOO_LARGE: return "request exceeds the fixed scratch of a no-allocation entry point";
     default: return "unknown status";
   }
 }
@@ -220,6 +223,64 @@ csa_status_t csa_index_topk(const csa_cache_t* idx_cache, int32_t n_q, const int
   csa::IndexArgs a{*idx_cache, n_q, q_seq, q_pos, max_elig, q_idx, q_dtype, n_heads, head_w, mode, k,
                    out_idx, out_count, out_scores, workspace};
   hipError_t e = csa::launch_index_score(a, stream);
+  if (e == hipSuccess) e = csa::launch_index_select(a, stream);
+  return hip_status(e);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of csa_index_topk_noalloc: a static device array, one copy per GPU (each device's copy is created
+// when the library's code object is loaded on it). Host code never passes the array's name to a kernel: in
+// host code it is a stand-in, not a device address. Its device address is looked up once per device with
+// hipGetSymbolAddress and kept here.
+__device__ __align__(256) static uint8_t scratch[CSA_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+csa_status_t csa_index_topk_noalloc(const csa_cache_t* idx_cache, int32_t n_q, const int32_t* q_seq,
+                                    const int32_t* q_pos, int64_t max_elig, const void* q_idx, csa_dtype_t q_dtype,
+                                    int32_t n_heads, const float* head_w, csa_score_t mode, int32_t k,
+                                    int32_t* out_idx, int32_t* out_count, float* out_scores, hipStream_t stream) {
+  if (!valid_cache(idx_cache) || n_q < 0 || max_elig < 0 || max_elig > 0x7FFFFFFF) return CSA_ERR_INVALID_ARG;
+  if (k < 1 || k > csa::kMaxK) return CSA_ERR_INVALID_ARG;
+  if (n_q > 0 && (!q_seq || !q_pos)) return CSA_ERR_INVALID_ARG;
+  csa_status_t st = score_check(idx_cache, n_q, q_idx, q_dtype, n_heads, head_w, mode);
+  if (st != CSA_OK) return st;
+  if (n_q > 0 && !out_idx) return CSA_ERR_INVALID_ARG;
+  if (csa::index_workspace(n_q, max_elig, k) > CSA_NOALLOC_SCRATCH_BYTES) return CSA_ERR_TOO_LARGE;
+  if (n_q == 0) return CSA_OK;
+  void* ws = nullptr;
+  hipError_t e = scratch_of_current_device(&ws);
+  if (e != hipSuccess) return hip_status(e);
+  csa::IndexArgs a{*idx_cache, n_q, q_seq, q_pos, max_elig, q_idx, q_dtype, n_heads, head_w, mode, k,
+                   out_idx, out_count, out_scores, ws};
+  // the scratch keeps whatever the previous call on this device left: zero the histogram region first
+  e = csa::launch_index_clear(ws, n_q, stream);
+  if (e == hipSuccess) e = csa::launch_index_score(a, stream);
   if (e == hipSuccess) e = csa::launch_index_select(a, stream);
   return hip_status(e);
 }

@@ -235,3 +235,35 @@ def test_fp4_cache_validation(L):
     assert _index(L, cache=fp4(dim=64)) == UNSUPPORTED
     assert _index(L, cache=fp4(ratio=128, window=128)) == UNSUPPORTED
     assert _attend(L, cache=_cache(dim=512, dtype=csa.FP4, scales=FAKE)) == UNSUPPORTED
+
+
+def _index_noalloc(L, cache=None, **kw):
+    a = dict(n_q=2, q_seq=FAKE, q_pos=FAKE, max_elig=1000, q=FAKE, q_dtype=csa.BF16, heads=64, w=FAKE,
+             mode=csa.SCORE_WRELU, k=512, out=FAKE, cnt=None, sc=None)
+    a.update(kw)
+    c = cache if cache is not None else _cache()
+    return L.csa_index_topk_noalloc(ctypes.byref(c), a["n_q"], a["q_seq"], a["q_pos"], a["max_elig"], a["q"],
+                                    a["q_dtype"], a["heads"], a["w"], a["mode"], a["k"], a["out"], a["cnt"], a["sc"],
+                                    None)
+
+
+TOO_LARGE = 5
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(k=0), INVALID), (dict(heads=129), INVALID), (dict(w=None), INVALID), (dict(out=None), INVALID),
+    (dict(max_elig=-1), INVALID), (dict(q_dtype=csa.F32), UNSUPPORTED),
+    # beyond the fixed scratch: a 4096-query prefill chunk of 66047 entries, and 4 queries of 2^31-1 entries
+    (dict(n_q=4096, max_elig=66047), TOO_LARGE), (dict(n_q=4, max_elig=0x7FFFFFFF), TOO_LARGE),
+])
+def test_index_noalloc_validation(L, bad, code):
+    """Rejected before any HIP call (no scratch lookup, no launch)."""
+    assert _index_noalloc(L, **bad) == code
+
+
+def test_index_noalloc_scratch_holds_decode_sizes(L):
+    """The fixed scratch takes the decode workloads: 32 queries of 32767 entries, 4 of 262143."""
+    assert L.csa_index_topk_workspace(32, 32767, 512, 64) <= csa.NOALLOC_SCRATCH_BYTES
+    assert L.csa_index_topk_workspace(4, 262143, 512, 64) <= csa.NOALLOC_SCRATCH_BYTES
+    assert L.csa_index_topk_workspace(4096, 66047, 512, 64) > csa.NOALLOC_SCRATCH_BYTES
+    assert L.csa_status_string(TOO_LARGE).startswith(b"request exceeds")
