@@ -6,10 +6,13 @@
 // indexer pipeline (its own compressor instance, score, top-k) is separate from the main cache.
 //
 // Two launches on the caller's stream (csa_index_score, then csa_index_select):
-//   1. score     -- one workgroup per (query, run of entries). WRELU with 16*HT heads over dim-128
+//   1. score     -- one workgroup per (query, run of pages). WRELU with 16*HT heads over dim-128
 //                   bf16 / fp8 / MXFP4 keys runs on MFMA (v_mfma_f32_16x16x32_bf16: heads x 16 entries x 32
 //                   dims per instruction; fp8 and fp4 codes widened exactly to bf16, fp4 with its block's
-//                   power-of-two scale folded in); other shapes run on a VALU path (not for fp4).
+//                   power-of-two scale folded in); bf16 / fp8 pages are loaded 1 KiB per instruction and
+//                   transposed through LDS (score_lt_kernel), fp4 pages straight into operand layout
+//                   (score_mfma_kernel), a prefill launch shares pages among 8 queries (score_shared_kernel);
+//                   other shapes run on a VALU path (not for fp4).
 //                   Each score becomes an order-preserving 32-bit key; a 4096-bin LDS histogram of
 //                   the top 12 key bits is flushed into the query's global histogram.
 //   2. select    -- one 1024-thread workgroup per query: find the histogram bin that holds the k-th
@@ -95,7 +98,7 @@ __device__ __forceinline__ void flush_hist(uint32_t* hist_s, uint32_t* hist_q) {
 // groups hold the 16 scores of a tile, and lane l keeps the score of entry l of the page, so each page ends
 // in one coalesced 256-byte key store.
 constexpr int kPagesPerBlock = 32;
-constexpr int kQueryFastMin = 256;  // queries per launch from which the grid walks queries first
+constexpr int kQueryFastMin = 256;  // queries per launch from which workgroups share pages among queries
 
 // Key formats of the MFMA score: 0 bf16, 1 fp8 e4m3 (per-entry scale), 2 MXFP4 (per-32-channel E8M0 scale).
 // bf16 and fp8 lanes feed dims ks*32 + kg*8 .. +8 of k-step ks; an fp4 lane feeds dims kg*32 + ks*8 .. +8,
@@ -200,22 +203,21 @@ __device__ __forceinline__ uint32_t score_page(const PageBuf<KF>& b, const bf16x
   return mine;
 }
 
-// Grid order: with few queries (decode) blockIdx.x walks the page runs of one query; with many queries per
-// sequence (a prefill chunk) blockIdx.x walks the queries (query_fast), so the workgroups running at the same
-// time read the same run of pages and an XCD's L2 serves its queries' repeated reads of them.
+// Decode score for MXFP4 pages: one workgroup per (query, run of pages), blockIdx.x = run. An fp4 row is 64 bytes,
+// so the operand-layout loads of a 16-entry tile read whole 128-byte lines and no LDS stage is needed.
 template <int KF, int HT>
-__global__ void __launch_bounds__(256, 2) score_mfma_kernel(IndexArgs a, Workspace ws, int query_fast) {
+__global__ void __launch_bounds__(256, 2) score_mfma_kernel(IndexArgs a, Workspace ws, int run) {
   constexpr int DIM = 128;
   constexpr int E = 64;
   __shared__ uint32_t hist_s[kHistBins];
   __shared__ int32_t pg_phys[kPagesPerBlock];  // physical page of each page of this block, -1 if unmapped
-  const int q = query_fast ? blockIdx.x : blockIdx.y;
+  const int q = blockIdx.y;
   int seq;
   const int64_t n_elig = query_elig(a, q, &seq);
   const int64_t n_pages = (n_elig + E - 1) / E;
-  const int64_t pg_begin = int64_t(query_fast ? blockIdx.y : blockIdx.x) * kPagesPerBlock;
+  const int64_t pg_begin = int64_t(blockIdx.x) * run;
   if (pg_begin >= n_pages) return;  // uniform per block
-  const int64_t pg_end = min(n_pages, pg_begin + kPagesPerBlock);
+  const int64_t pg_end = min(n_pages, pg_begin + run);
   for (int b = threadIdx.x; b < kHistBins; b += blockDim.x) hist_s[b] = 0u;
   if (threadIdx.x < kPagesPerBlock) {
     const int64_t pg = pg_begin + threadIdx.x;
@@ -467,6 +469,175 @@ __global__ void __launch_bounds__(kShareThreads, 1) score_shared_kernel(IndexArg
       if (v & 0xFFFFu) atomicAdd(hq + 2 * b, v & 0xFFFFu);
       if (v >> 16) atomicAdd(hq + 2 * b + 1, v >> 16);
     }
+  }
+}
+
+// ------------------------------------------------------------------ MFMA score with contiguous page loads (decode)
+// Each wavefront walks its own pages (no workgroup barrier in the loop) with all heads of the query in registers,
+// like score_mfma_kernel, but loads a page the way HBM serves it best: every load instruction reads 1 KiB of
+// consecutive bytes (full 128-byte lines). The MFMA operand layout wants 16 rows x 64 bytes per instruction instead,
+// i.e. half of 16 lines, which costs about 10% of gather bandwidth when MFMA work runs beside it; so the page is
+// written to a private LDS stage of the wave and read back in operand layout. kLtAhead pages per wave stay in
+// flight in registers. The scores are exactly score_page's.
+constexpr int kLtPages = 32;  // pages per workgroup run (8 per wave)
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;  // plain vector: loads and stores
+                                                                                // of it stay in registers
+
+template <int KF>
+struct LtPage {
+  static constexpr int RAW_ROW = KF == 1 ? 128 : (KF == 2 ? 64 : 256);  // bytes per page row in HBM
+  static constexpr int ROW = RAW_ROW + 16;                              // LDS bytes per row (rows 4 banks apart)
+  static constexpr int LOADS = 64 * RAW_ROW / 1024;                     // 1 KiB load instructions per page: 16, 8, 4
+  static constexpr int AHEAD = 2;                                       // pages in flight per wave
+};
+
+// Page `phys` (clamped to 0 when unmapped) -> this lane's registers: 16 bytes of each 1 KiB of the page; fp8 / fp4:
+// lane l also takes entry l's scale word (fp8 scale bits, fp4 the four E8M0 bytes).
+template <int KF>
+__device__ __forceinline__ void lt_fetch(const IndexArgs& a, int32_t phys, int lane, u32x4 (&c)[LtPage<KF>::LOADS],
+                                         uint32_t& sc) {
+  using L = LtPage<KF>;
+  const int64_t page = phys >= 0 ? phys : 0;
+  const char* src = static_cast<const char*>(a.cache.pages) + page * 64 * L::RAW_ROW + lane * 16;
+#pragma unroll
+  for (int i = 0; i < L::LOADS; ++i) c[i] = *reinterpret_cast<const u32x4*>(src + i * 1024);
+  if (KF != 0) sc = reinterpret_cast<const uint32_t*>(a.cache.scales)[page * 64 + lane];
+}
+
+// score_page on a page staged in LDS (rows of L::ROW bytes, scale words in sc_s), reading each 16-entry tile's
+// operands just before its MFMAs; the arithmetic and its order are score_page's.
+template <int KF, int HT>
+__device__ __forceinline__ uint32_t lt_score_page(const char* st, const uint32_t* sc_s, const bf16x8 (&qa)[HT][4],
+                                                  const float (&wv)[HT][4], int col, int kg) {
+  using L = LtPage<KF>;
+  float mine_f = 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const char* rowp = st + (u * 16 + col) * L::ROW;
+    bf16x8 kb[4];
+    float sc = 1.f;
+    if constexpr (KF == 2) {
+      const uint4 c = *reinterpret_cast<const uint4*>(rowp + kg * 16);
+      const float bs = e8m0_to_f32((sc_s[u * 16 + col] >> (8 * kg)) & 0xFFu);
+      kb[0] = fp4x8_to_bf16x8_hw(c.x, bs);
+      kb[1] = fp4x8_to_bf16x8_hw(c.y, bs);
+      kb[2] = fp4x8_to_bf16x8_hw(c.z, bs);
+      kb[3] = fp4x8_to_bf16x8_hw(c.w, bs);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        if constexpr (KF == 1) kb[ks] = fp8x8_to_bf16x8_hw(*reinterpret_cast<const uint2*>(rowp + ks * 32 + kg * 8));
+        else kb[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rowp + ks * 64 + kg * 16));
+      }
+      if constexpr (KF == 1) sc = __uint_as_float(sc_s[u * 16 + col]);
+    }
+    float part = 0.f;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ht][ks], kb[ks], acc, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part += wv[ht][i] * fmaxf(acc[i], 0.f);
+    }
+    part += __shfl_xor(part, 16);
+    part += __shfl_xor(part, 32);
+    if constexpr (KF == 1) part *= sc;
+    if (kg == u) mine_f = part;
+  }
+  return score_key(mine_f);
+}
+
+template <int KF, int HT>
+__global__ void __launch_bounds__(256, 2) score_lt_kernel(IndexArgs a, Workspace ws) {
+  using L = LtPage<KF>;
+  constexpr int DIM = 128;
+  constexpr int E = 64;
+  constexpr int AHEAD = L::AHEAD;
+  __shared__ uint32_t hist_s[kHistBins / 2];  // two 16-bit bins per word (at most 2048 keys per workgroup)
+  __shared__ __attribute__((aligned(16))) char stage_s[4][E * L::ROW];
+  __shared__ uint32_t scale_s[4][E];
+  __shared__ int32_t pg_phys[kLtPages];
+  const int q = blockIdx.y;
+  int seq;
+  const int64_t n_elig = query_elig(a, q, &seq);
+  const int64_t n_pages = (n_elig + E - 1) / E;
+  const int64_t pg_begin = int64_t(blockIdx.x) * kLtPages;
+  if (pg_begin >= n_pages) return;  // uniform per block
+  const int64_t pg_end = min(n_pages, pg_begin + kLtPages);
+  for (int b = threadIdx.x; b < kHistBins / 2; b += blockDim.x) hist_s[b] = 0u;
+  if (threadIdx.x < kLtPages) {
+    const int64_t pg = pg_begin + threadIdx.x;
+    const int32_t* bt = a.cache.block_table + int64_t(seq) * a.cache.bt_stride;
+    const int32_t phys = (pg < pg_end && pg < a.cache.bt_stride) ? bt[pg] : -1;
+    pg_phys[threadIdx.x] = (phys >= 0 && phys < a.cache.n_phys) ? phys : -1;
+  }
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int kg = lane >> 4;
+  const int H = HT * 16;
+  bf16x8 qa[HT][4];
+  const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + int64_t(q) * H * DIM;
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qa[ht][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+                                                  qp + (ht * 16 + col) * DIM + (KF == 2 ? kg * 32 + ks * 8 : ks * 32 + kg * 8)));
+  float wv[HT][4];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[ht][i] = a.head_w[int64_t(q) * H + ht * 16 + kg * 4 + i];
+  lds_barrier();  // pg_phys and the cleared histogram are visible; the loads above stay in flight
+
+  uint32_t* keys_q = ws.keys + int64_t(q) * a.max_elig;
+  char* st = stage_s[wave];
+  // this wave's pages: pg_begin + wave, +4, ... < pg_end
+  const int64_t first = __builtin_amdgcn_readfirstlane(int(pg_begin + wave));
+  const int n_mine = first < pg_end ? int((pg_end - 1 - first) / 4 + 1) : 0;
+  if (n_mine > 0) {
+    u32x4 land[AHEAD][L::LOADS];
+    uint32_t land_sc[AHEAD] = {};
+#pragma unroll
+    for (int s = 0; s < AHEAD; ++s)
+      if (s < n_mine) lt_fetch<KF>(a, pg_phys[wave + 4 * s], lane, land[s], land_sc[s]);
+    for (int j0 = 0; j0 < n_mine; j0 += AHEAD) {
+#pragma unroll
+      for (int s = 0; s < AHEAD; ++s) {
+        const int j = j0 + s;
+        if (j < n_mine) {  // uniform over the wave
+          // stage page j: byte offset 16 * (lane + 64 i) of the page is row (lane + 64 i) / (RAW_ROW / 16)
+#pragma unroll
+          for (int i = 0; i < L::LOADS; ++i) {
+            const int chunk = lane + 64 * i;
+            const int row = chunk / (L::RAW_ROW / 16), off = (chunk % (L::RAW_ROW / 16)) * 16;
+            *reinterpret_cast<u32x4*>(st + row * L::ROW + off) = land[s][i];
+          }
+          if (KF != 0) scale_s[wave][lane] = land_sc[s];
+          const int32_t phys_j = pg_phys[wave + 4 * j];
+          if (j + AHEAD < n_mine) lt_fetch<KF>(a, pg_phys[wave + 4 * (j + AHEAD)], lane, land[s], land_sc[s]);
+          __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the stage is written before this wave reads it
+          __builtin_amdgcn_wave_barrier();
+          const uint32_t key = lt_score_page<KF, HT>(st, scale_s[wave], qa, wv, col, kg);
+          const int64_t e = (first + 4 * int64_t(j)) * E + lane;
+          if (e < n_elig) {
+            const uint32_t k2 = phys_j >= 0 ? key : 0u;
+            keys_q[e] = k2;
+            const uint32_t bin = k2 >> (32 - kHistBits);
+            atomicAdd(&hist_s[bin >> 1], 1u << ((bin & 1u) * 16));
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t* hq = ws.hist + int64_t(q) * kHistBins;
+  for (int b = threadIdx.x; b < kHistBins / 2; b += blockDim.x) {
+    const uint32_t v = hist_s[b];
+    if (v & 0xFFFFu) atomicAdd(hq + 2 * b, v & 0xFFFFu);
+    if (v >> 16) atomicAdd(hq + 2 * b + 1, v >> 16);
   }
 }
 
@@ -994,10 +1165,15 @@ void launch_score_shared(int kf, dim3 grid, const IndexArgs& a, const Workspace&
 }
 
 template <int HT>
-void launch_score_mfma(int kf, dim3 grid, const IndexArgs& a, const Workspace& ws, int qf, hipStream_t stream) {
-  if (kf == 2) hipLaunchKernelGGL((score_mfma_kernel<2, HT>), grid, dim3(256), 0, stream, a, ws, qf);
-  else if (kf == 1) hipLaunchKernelGGL((score_mfma_kernel<1, HT>), grid, dim3(256), 0, stream, a, ws, qf);
-  else hipLaunchKernelGGL((score_mfma_kernel<0, HT>), grid, dim3(256), 0, stream, a, ws, qf);
+void launch_score_fp4(dim3 grid, const IndexArgs& a, const Workspace& ws, int run, hipStream_t stream) {
+  hipLaunchKernelGGL((score_mfma_kernel<2, HT>), grid, dim3(256), 0, stream, a, ws, run);
+}
+
+template <int HT>
+void launch_score_lt(int kf, dim3 grid, const IndexArgs& a, const Workspace& ws, hipStream_t stream) {
+  if (kf == 2) hipLaunchKernelGGL((score_lt_kernel<2, HT>), grid, dim3(256), 0, stream, a, ws);
+  else if (kf == 1) hipLaunchKernelGGL((score_lt_kernel<1, HT>), grid, dim3(256), 0, stream, a, ws);
+  else hipLaunchKernelGGL((score_lt_kernel<0, HT>), grid, dim3(256), 0, stream, a, ws);
 }
 
 hipError_t launch_index_score(const IndexArgs& a, hipStream_t stream) {
@@ -1021,13 +1197,23 @@ hipError_t launch_index_score(const IndexArgs& a, hipStream_t stream) {
       }
       return hipGetLastError();
     }
-    const int qf = (a.n_q >= kQueryFastMin && runs <= 65535) ? 1 : 0;
-    const dim3 grid = qf ? dim3(unsigned(a.n_q), unsigned(runs)) : dim3(unsigned(runs), unsigned(a.n_q));
-    switch (a.n_heads / 16) {
-      case 1: launch_score_mfma<1>(kf, grid, a, ws, qf, stream); break;
-      case 2: launch_score_mfma<2>(kf, grid, a, ws, qf, stream); break;
-      case 3: launch_score_mfma<3>(kf, grid, a, ws, qf, stream); break;
-      default: launch_score_mfma<4>(kf, grid, a, ws, qf, stream); break;
+    if (fp4) {  // fp4 rows are 64 bytes: the operand-layout loads already read whole lines
+      const int run = kPagesPerBlock;
+      const dim3 grid(unsigned((max_pages + run - 1) / run), unsigned(a.n_q));
+      switch (a.n_heads / 16) {
+        case 1: launch_score_fp4<1>(grid, a, ws, run, stream); break;
+        case 2: launch_score_fp4<2>(grid, a, ws, run, stream); break;
+        case 3: launch_score_fp4<3>(grid, a, ws, run, stream); break;
+        default: launch_score_fp4<4>(grid, a, ws, run, stream); break;
+      }
+    } else {
+      const dim3 grid(unsigned((max_pages + kLtPages - 1) / kLtPages), unsigned(a.n_q));
+      switch (a.n_heads / 16) {
+        case 1: launch_score_lt<1>(kf, grid, a, ws, stream); break;
+        case 2: launch_score_lt<2>(kf, grid, a, ws, stream); break;
+        case 3: launch_score_lt<3>(kf, grid, a, ws, stream); break;
+        default: launch_score_lt<4>(kf, grid, a, ws, stream); break;
+      }
     }
   } else {
     const dim3 grid(unsigned((a.max_elig + 255) / 256), unsigned(a.n_q));
