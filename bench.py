@@ -359,8 +359,31 @@ def time_output_epilogue(torch, csa, layers, step, out, topk, max_elig, scale, r
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / iters
     alg = raw.numel() * 4 + codes.numel() + scales.numel() * 4
-    return {"kernel": "inv_rope_quant_kernel", "group": group, "us": round(us, 2), "alg_bytes": alg,
-            "gbs": round(alg / (us * 1e-6) / 1e9, 1), "frac_peak": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+    # the same output produced by the attention itself (csa_attend_quant_fp8: the fp32 output never reaches HBM),
+    # against the attention with an fp32 output (fused inverse RoPE), both over the rotated layers
+    def attn_us(fn):
+        for i in range(5):
+            fn(layers[i % len(layers)])
+        torch.cuda.synchronize()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for i in range(iters):
+            fn(layers[i % len(layers)])
+        a1.record()
+        torch.cuda.synchronize()
+        return a0.elapsed_time(a1) * 1e3 / iters
+    fused = attn_us(lambda l: csa.attend_quant_fp8(l.cache, l.swa, SWA, l.seq, l.pos, l.q, topk, max_elig, scale, rope,
+                                                   group, codes, scales, workspace=att_ws))
+    fp32 = attn_us(lambda l: csa.attend(l.cache, l.swa, SWA, l.seq, l.pos, l.q, topk, max_elig, scale, True, rope, out,
+                                        workspace=att_ws))
+    return {"kernel": "inv_rope_quant_kernel (separate pass over the fp32 output)", "group": group, "us": round(us, 2),
+            "alg_bytes": alg, "gbs": round(alg / (us * 1e-6) / 1e9, 1),
+            "frac_peak": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "fused": {"call": "csa_attend_quant_fp8 (attention with the inverse RoPE + fp8 epilogue fused in)",
+                      "attend_fp8_out_us": round(fused, 2), "attend_fp32_out_us": round(fp32, 2),
+                      "unfused_attend_plus_pass_us": round(fp32 + us, 2),
+                      "topk_note": "the top-k of the last timed step is reused for every layer"}}
 
 
 # ------------------------------------------------------------------ side workloads, measured in the same run

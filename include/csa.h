@@ -13,6 +13,7 @@
  *   csa_attend           (top-k entries + raw sliding window, or dense for c128a; optional fused inverse RoPE)
  *   csa_inv_rope         (standalone inverse RoPE, when not fused)
  *   csa_inv_rope_quant_fp8 (inverse RoPE fused with fp8 quantisation of the output, for an fp8 projection)
+ *   csa_attend_quant_fp8 (csa_attend with that fp8 output epilogue fused into the attention kernels)
  * and, upstream of the step, csa_prepare_qk (query norm + RoPE, window-key RoPE + insert).
  *
  * Conventions
@@ -250,6 +251,28 @@ csa_status_t csa_attend(const csa_cache_t* kv_cache, const csa_raw_t* swa, int32
                         int64_t max_elig, float softmax_scale, int32_t fuse_inv_rope,
                         const float* rope_cs, int32_t rope_rows, float* out, float* out_lse,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * csa_attend_quant_fp8 -- csa_attend with the output epilogue of an fp8 output projection fused in.
+ * [P1] "GPU Compute Saturation" (kernel fusions) / [P2] "3.2 內核": the attention output goes through the
+ * inverse RoPE and into the fp8 batched matmul of the o_lora projection, and the two steps are fused so the
+ * output skips an HBM round trip. Same arguments and attention as csa_attend with fuse_inv_rope = 1; instead of
+ * an fp32 output, each (query, head) row of the inverse-rotated output is written as groups of `group`
+ * consecutive channels in OCP e4m3fn with one fp32 scale per group, by the rule of csa_inv_rope_quant_fp8
+ * (amax = max|y|, code = e4m3_rne(y * (448 / amax)), scale = amax / 448, computed in fp32; zero codes and scale
+ * 1 for an all-zero group). The fp32 output never reaches memory.
+ *   out_codes  [n_q][n_heads][D] uint8 (8-byte aligned); out_scales [n_q][n_heads][D / group] fp32;
+ *   out_lse    as for csa_attend (may be NULL).
+ *   group in {16, 32, 64, 128}. Supported for D = 512 with bf16 / fp8 caches and a multiple of 16 heads (the
+ *   MFMA attention kernels); other shapes return CSA_ERR_UNSUPPORTED (use csa_attend + csa_inv_rope_quant_fp8).
+ *   Workspace: as for csa_attend (csa_attend_workspace).
+ * ------------------------------------------------------------------------------------------- */
+csa_status_t csa_attend_quant_fp8(const csa_cache_t* kv_cache, const csa_raw_t* swa, int32_t swa_window,
+                                  int32_t n_q, const int32_t* q_seq, const int32_t* q_pos, const void* q,
+                                  csa_dtype_t q_dtype, int32_t n_heads, const int32_t* topk_idx, int32_t k,
+                                  int64_t max_elig, float softmax_scale, const float* rope_cs, int32_t rope_rows,
+                                  int32_t group, uint8_t* out_codes, float* out_scales, float* out_lse,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * csa_inv_rope -- inverse rotation (u, v) -> (u c + v s, -u s + v c) of the last rope_dims dims of

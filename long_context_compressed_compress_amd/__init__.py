@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
             "csa_inv_rope": (I32, [I32, I32, I32, I32, P, P, I32, P, P]),
             "csa_rope_table": (I32, [I32, I32, D, P, P]),
             "csa_inv_rope_quant_fp8": (I32, [I32, I32, I32, I32, P, P, I32, P, I32, P, P, P]),
+            "csa_attend_quant_fp8": (I32, [CP, RP, I32, I32, P, P, P, I32, I32, P, I32, I64, F, P, I32, I32, P, P, P, P,
+                                           SZ, P]),
             "csa_prepare_qk": (I32, [I32, I32, P, P, P, I32, P, F, P, RP, I32, P, I32, P, P]),
             "csa_num_entries": (I64, [I64, I32, I32]),
             "csa_num_eligible": (I64, [I64, I32, I32]),
@@ -259,6 +261,25 @@ def attend(cache: Cache, swa: Raw, swa_window: int, q_seq: torch.Tensor, q_pos: 
         ctypes.byref(cd), ctypes.byref(sd), swa_window, n_q, _ptr(q_seq), _ptr(q_pos), _ptr(q), dtype_code(q),
         n_heads, _ptr(topk_idx), k, max_elig, softmax_scale, int(fuse_inv_rope), _ptr(rope_cs), rope_cs.shape[0],
         _ptr(out), _ptr(out_lse), _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))
+
+
+def attend_quant_fp8(cache: Cache, swa: Raw, swa_window: int, q_seq: torch.Tensor, q_pos: torch.Tensor,
+                     q: torch.Tensor, topk_idx: Optional[torch.Tensor], max_elig: int, softmax_scale: float,
+                     rope_cs: torch.Tensor, group: int, out_codes: torch.Tensor, out_scales: torch.Tensor,
+                     out_lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                     stream=None) -> None:
+    """csa_attend_quant_fp8: attention with the inverse RoPE + grouped fp8 output epilogue fused in."""
+    n_q, n_heads = q.shape[0], q.shape[1]
+    cd, sd = cache.desc(), swa.desc()
+    k = 0 if topk_idx is None else topk_idx.shape[1]
+    if workspace is None:
+        need = attend_workspace(n_q, n_heads, q.shape[2], (k if topk_idx is not None else max_elig) + swa_window)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+    _check("csa_attend_quant_fp8", lib().csa_attend_quant_fp8(
+        ctypes.byref(cd), ctypes.byref(sd), swa_window, n_q, _ptr(q_seq), _ptr(q_pos), _ptr(q), dtype_code(q),
+        n_heads, _ptr(topk_idx), k, max_elig, softmax_scale, _ptr(rope_cs), rope_cs.shape[0], group, _ptr(out_codes),
+        _ptr(out_scales), _ptr(out_lse), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+        _stream(stream)))
 
 
 def attend_workspace(n_q: int, n_heads: int, dim: int, max_keys: int) -> int:

@@ -105,6 +105,52 @@ __device__ __forceinline__ float pair_swap(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
 }
 
+// ---- output epilogue, fp32 or fp8 (the inverse rotation is applied before either).
+// A lane holds rr[nt][i] = output of head (kg * 4 + i) of its 16-head group at dim d0 + nt * 16 + col. The fp8
+// form stores groups of GN * 16 consecutive channels of one head as e4m3 codes with one fp32 scale: amax over the
+// group (GN registers of the lane, then the 16 lanes of its DPP row), code = e4m3_rne(y * (448 / amax)),
+// scale = amax / 448, zero codes and scale 1 for an all-zero group.
+template <int NT, int GN>
+__device__ __forceinline__ void store_fp8_groups(const float (&rr)[NT][4], uint8_t* codes, float* scales, int64_t row0,
+                                                 int d0, int col, int group) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint8_t* crow = codes + (row0 + i) * kD;
+    float* srow = scales + (row0 + i) * (kD / group);
+#pragma unroll
+    for (int g = 0; g < NT; g += GN) {
+      float amax = 0.f;
+#pragma unroll
+      for (int n = 0; n < GN; ++n) amax = fmaxf(amax, fabsf(rr[g + n][i]));
+      amax = row_max16(amax);
+      const float inv = 448.0f / amax;
+#pragma unroll
+      for (int n = 0; n < GN; ++n)
+        crow[d0 + (g + n) * 16 + col] = amax > 0.f ? uint8_t(f32_to_e4m3_rne(rr[g + n][i] * inv)) : uint8_t(0);
+      if (col == 0) srow[(d0 + g * 16) / group] = amax > 0.f ? amax / 448.0f : 1.0f;
+    }
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void store_output(const AttendArgs& a, const float (&rr)[NT][4], int q, int h0, int d0,
+                                             int col) {
+  const int64_t row0 = int64_t(q) * a.n_heads + h0;
+  if (a.out) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a.out[(row0 + i) * kD + d0 + nt * 16 + col] = rr[nt][i];
+    return;
+  }
+  switch (a.group) {
+    case 16: store_fp8_groups<NT, 1>(rr, a.out_codes, a.out_scales, row0, d0, col, 16); break;
+    case 32: store_fp8_groups<NT, 2>(rr, a.out_codes, a.out_scales, row0, d0, col, 32); break;
+    case 64: store_fp8_groups<NT, 4>(rr, a.out_codes, a.out_scales, row0, d0, col, 64); break;
+    default: store_fp8_groups<NT, 8>(rr, a.out_codes, a.out_scales, row0, d0, col, 128); break;
+  }
+}
+
 template <bool FP8>
 struct TileRegs;
 template <>
@@ -369,11 +415,12 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a) {
     __syncthreads();  // the next pass rewrites the row table
   }
 
-  // ---- epilogue: normalise, optional inverse RoPE, store
+  // ---- epilogue: normalise, optional inverse RoPE, store (fp32 or grouped fp8)
   const int R_ = a.cache.rope_dims;
   const int base = kD - R_;
   const bool rot = a.fuse_inv_rope && R_ > 0 && p >= 0 && p < a.rope_rows;
   const float* cs = rot ? a.rope_cs + p * int64_t(R_) : a.rope_cs;
+  float rr[8][4];
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) {
     const int d = wave * 128 + nt * 16 + col;
@@ -388,10 +435,10 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a) {
         const float c = cs[2 * j], sn = cs[2 * j + 1];
         r = (d & 1) ? (-partner * sn + v * c) : (v * c + partner * sn);
       }
-      const int h = hg * 16 + kg * 4 + i;
-      a.out[(int64_t(q) * a.n_heads + h) * kD + d] = r;
+      rr[nt][i] = r;
     }
   }
+  store_output<8>(a, rr, q, hg * 16 + kg * 4, wave * 128, col);
   if (a.out_lse && wave == 0 && col == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -700,6 +747,7 @@ __global__ void __launch_bounds__(512) attend_split_kernel(AttendArgs a, SplitPl
     const int base = kD - R_;
     const bool rot = a.fuse_inv_rope && R_ > 0 && p >= 0 && p < a.rope_rows;
     const float* cs = rot ? a.rope_cs + p * int64_t(R_) : a.rope_cs;
+    float rr[16][4];
 #pragma unroll
     for (int nt = 0; nt < 16; ++nt) {
       const int d = sw * 256 + nt * 16 + col;
@@ -714,9 +762,10 @@ __global__ void __launch_bounds__(512) attend_split_kernel(AttendArgs a, SplitPl
           const float c = cs[2 * j], sn = cs[2 * j + 1];
           r = (d & 1) ? (-partner * sn + v * c) : (v * c + partner * sn);
         }
-        a.out[(int64_t(q) * a.n_heads + head0 + kg * 4 + i) * kD + d] = r;
+        rr[nt][i] = r;
       }
     }
+    store_output<16>(a, rr, q, head0 + kg * 4, sw * 256, col);
     if (a.out_lse && sw == 0 && col == 0)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -784,9 +833,31 @@ __global__ void __launch_bounds__(256) attend_combine_kernel(AttendArgs a, Split
       }
     }
   }
-  float4* dst = reinterpret_cast<float4*>(a.out + (int64_t(q) * a.n_heads + h) * kD + d0);
-  dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-  dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  if (a.out) {
+    float4* dst = reinterpret_cast<float4*>(a.out + (int64_t(q) * a.n_heads + h) * kD + d0);
+    dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  } else {
+    // grouped fp8: a group of G channels is G / 8 consecutive lanes of this wave (the R23 rule, as in the
+    // single-split epilogue)
+    float amax = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(acc[k]));
+    const int lanes = a.group / 8;
+    for (int off = 1; off < lanes; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    uint32_t w0 = 0u, w1 = 0u;
+    if (amax > 0.f) {
+      const float inv = 448.0f / amax;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        w0 |= f32_to_e4m3_rne(acc[k] * inv) << (8 * k);
+        w1 |= f32_to_e4m3_rne(acc[k + 4] * inv) << (8 * k);
+      }
+    }
+    const int64_t row = int64_t(q) * a.n_heads + h;
+    *reinterpret_cast<uint2*>(a.out_codes + row * kD + d0) = make_uint2(w0, w1);
+    if ((d0 / 8) % lanes == 0) a.out_scales[row * (kD / a.group) + d0 / a.group] = amax > 0.f ? amax / 448.0f : 1.0f;
+  }
   if (a.out_lse && d0 == 0) a.out_lse[int64_t(q) * a.n_heads + h] = (L > 0.f) ? M + logf(L) : -INFINITY;
 }
 
@@ -908,6 +979,11 @@ bool attend_supported(const csa_cache_t& c, csa_dtype_t q_dtype, int n_heads) {
   if (int64_t(c.n_phys) * (kBlock / c.ratio) > 0x7FFFFFFF) return false;  // page rows are 32-bit
   if (c.dtype == CSA_F32) return q_dtype == CSA_F32 && c.dim <= 512;
   return q_dtype == CSA_BF16 && c.dim <= 512 && n_heads >= 1;
+}
+
+bool attend_quant_supported(const csa_cache_t& c, csa_dtype_t q_dtype, int n_heads, int group) {
+  const bool g_ok = group == 16 || group == 32 || group == 64 || group == 128;
+  return g_ok && attend_supported(c, q_dtype, n_heads) && c.dtype != CSA_F32 && c.dim == kD && n_heads % 16 == 0;
 }
 
 static bool use_split_path(const AttendArgs& a) {

@@ -290,11 +290,16 @@ size_t csa_attend_workspace(int32_t n_q, int32_t n_heads, int32_t dim, int32_t m
   return csa::attend_workspace(n_q, n_heads, dim, max_keys);
 }
 
-csa_status_t csa_attend(const csa_cache_t* kv_cache, const csa_raw_t* swa, int32_t swa_window, int32_t n_q,
-                        const int32_t* q_seq, const int32_t* q_pos, const void* q, csa_dtype_t q_dtype,
-                        int32_t n_heads, const int32_t* topk_idx, int32_t k, int64_t max_elig, float softmax_scale,
-                        int32_t fuse_inv_rope, const float* rope_cs, int32_t rope_rows, float* out, float* out_lse,
-                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by csa_attend and csa_attend_quant_fp8 (everything but the output buffers); fills *a.
+csa_status_t attend_args(const csa_cache_t* kv_cache, const csa_raw_t* swa, int32_t swa_window, int32_t n_q,
+                         const int32_t* q_seq, const int32_t* q_pos, const void* q, csa_dtype_t q_dtype,
+                         int32_t n_heads, const int32_t* topk_idx, int32_t k, int64_t max_elig, float softmax_scale,
+                         int32_t fuse_inv_rope, const float* rope_cs, int32_t rope_rows, void* workspace,
+                         size_t workspace_bytes, csa::AttendArgs* a) {
   if (!valid_cache(kv_cache) || !valid_raw_common(swa, kv_cache ? kv_cache->dim : -1)) return CSA_ERR_INVALID_ARG;
   if (kv_cache->dtype == CSA_FP4_E2M1) return CSA_ERR_UNSUPPORTED;  // fp4 is the indexer cache's format
   if (swa->dtype != kv_cache->dtype || swa->roles != 0) return CSA_ERR_INVALID_ARG;
@@ -303,16 +308,58 @@ csa_status_t csa_attend(const csa_cache_t* kv_cache, const csa_raw_t* swa, int32
   if (topk_idx && (k < 1 || k > csa::kMaxK)) return CSA_ERR_INVALID_ARG;
   if (max_elig < 0 || !isfinite(softmax_scale) || (fuse_inv_rope != 0 && fuse_inv_rope != 1)) return CSA_ERR_INVALID_ARG;
   if (q_dtype != CSA_F32 && q_dtype != CSA_BF16) return CSA_ERR_INVALID_ARG;
-  if (n_q > 0 && (!q_seq || !q_pos || !q || !out || !aligned(q, 16))) return CSA_ERR_INVALID_ARG;
+  if (n_q > 0 && (!q_seq || !q_pos || !q || !aligned(q, 16))) return CSA_ERR_INVALID_ARG;
   if (fuse_inv_rope && kv_cache->rope_dims > 0 && (!rope_cs || rope_rows < 1)) return CSA_ERR_INVALID_ARG;
   if (!csa::attend_supported(*kv_cache, q_dtype, n_heads)) return CSA_ERR_UNSUPPORTED;
   if (int64_t(swa->n_phys) * csa::kBlock > 0x7FFFFFFF) return CSA_ERR_UNSUPPORTED;  // window rows are 32-bit
   const int64_t max_keys = (topk_idx ? int64_t(k) : max_elig) + swa_window;
   const size_t need = max_keys <= 0x7FFFFFFF ? csa::attend_workspace(n_q, n_heads, kv_cache->dim, max_keys) : 0;
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16))) return CSA_ERR_WORKSPACE;
+  *a = csa::AttendArgs{*kv_cache, *swa, swa_window, n_q, q_seq, q_pos, q, q_dtype, n_heads, topk_idx,
+                       topk_idx ? k : 0, max_elig, softmax_scale, fuse_inv_rope, rope_cs, rope_rows, nullptr, nullptr,
+                       nullptr, nullptr, 0};
+  return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+csa_status_t csa_attend(const csa_cache_t* kv_cache, const csa_raw_t* swa, int32_t swa_window, int32_t n_q,
+                        const int32_t* q_seq, const int32_t* q_pos, const void* q, csa_dtype_t q_dtype,
+                        int32_t n_heads, const int32_t* topk_idx, int32_t k, int64_t max_elig, float softmax_scale,
+                        int32_t fuse_inv_rope, const float* rope_cs, int32_t rope_rows, float* out, float* out_lse,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (n_q > 0 && !out) return CSA_ERR_INVALID_ARG;
+  csa::AttendArgs a;
+  const csa_status_t st = attend_args(kv_cache, swa, swa_window, n_q, q_seq, q_pos, q, q_dtype, n_heads, topk_idx, k,
+                                      max_elig, softmax_scale, fuse_inv_rope, rope_cs, rope_rows, workspace,
+                                      workspace_bytes, &a);
+  if (st != CSA_OK || n_q == 0) return st;
+  a.out = out;
+  a.out_lse = out_lse;
+  return hip_status(csa::launch_attend(a, workspace, workspace_bytes, stream));
+}
+
+csa_status_t csa_attend_quant_fp8(const csa_cache_t* kv_cache, const csa_raw_t* swa, int32_t swa_window, int32_t n_q,
+                                  const int32_t* q_seq, const int32_t* q_pos, const void* q, csa_dtype_t q_dtype,
+                                  int32_t n_heads, const int32_t* topk_idx, int32_t k, int64_t max_elig,
+                                  float softmax_scale, const float* rope_cs, int32_t rope_rows, int32_t group,
+                                  uint8_t* out_codes, float* out_scales, float* out_lse, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  if (group != 16 && group != 32 && group != 64 && group != 128) return CSA_ERR_INVALID_ARG;
+  if (n_q > 0 && (!out_codes || !out_scales || !aligned(out_codes, 8) || !aligned(out_scales, 4)))
+    return CSA_ERR_INVALID_ARG;
+  csa::AttendArgs a;
+  csa_status_t st = attend_args(kv_cache, swa, swa_window, n_q, q_seq, q_pos, q, q_dtype, n_heads, topk_idx, k,
+                                max_elig, softmax_scale, 1, rope_cs, rope_rows, workspace, workspace_bytes, &a);
+  if (st != CSA_OK) return st;
+  if (!csa::attend_quant_supported(*kv_cache, q_dtype, n_heads, group)) return CSA_ERR_UNSUPPORTED;
   if (n_q == 0) return CSA_OK;
-  csa::AttendArgs a{*kv_cache, *swa, swa_window, n_q, q_seq, q_pos, q, q_dtype, n_heads, topk_idx,
-                    topk_idx ? k : 0, max_elig, softmax_scale, fuse_inv_rope, rope_cs, rope_rows, out, out_lse};
+  a.out_lse = out_lse;
+  a.out_codes = out_codes;
+  a.out_scales = out_scales;
+  a.group = group;
   return hip_status(csa::launch_attend(a, workspace, workspace_bytes, stream));
 }
 

@@ -173,7 +173,13 @@ struct AttendArgs {
   int rope_rows;
   float* out;
   float* out_lse;
+  // fp8 output (out == nullptr): inverse-rotated rows stored as grouped e4m3 codes [n_q][H][D] and one fp32 scale
+  // per `group` channels [n_q][H][D / group]
+  uint8_t* out_codes;
+  float* out_scales;
+  int group;
 };
+bool attend_quant_supported(const csa_cache_t& c, csa_dtype_t q_dtype, int n_heads, int group);
 bool attend_supported(const csa_cache_t& c, csa_dtype_t q_dtype, int n_heads);
 size_t attend_workspace(int n_q, int n_heads, int dim, int64_t max_keys);
 hipError_t launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t stream);

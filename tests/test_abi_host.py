@@ -267,3 +267,27 @@ def test_index_noalloc_scratch_holds_decode_sizes(L):
     assert L.csa_index_topk_workspace(4, 262143, 512, 64) <= csa.NOALLOC_SCRATCH_BYTES
     assert L.csa_index_topk_workspace(4096, 66047, 512, 64) > csa.NOALLOC_SCRATCH_BYTES
     assert L.csa_status_string(TOO_LARGE).startswith(b"request exceeds")
+
+
+def _attend_q(L, cache=None, swa=None, **kw):
+    a = dict(win=128, n_q=2, q_seq=FAKE, q_pos=FAKE, q=FAKE, q_dtype=csa.BF16, heads=64, topk=FAKE, k=512,
+             max_elig=1000, scale=0.05, cs=FAKE, rows=10, group=128, codes=FAKE, scales=FAKE, lse=None)
+    a.update(kw)
+    c = cache if cache is not None else _cache(dim=512)
+    s = swa if swa is not None else _raw(dim=512, roles=0, logit_pages=None)
+    return L.csa_attend_quant_fp8(ctypes.byref(c), ctypes.byref(s), a["win"], a["n_q"], a["q_seq"], a["q_pos"], a["q"],
+                                  a["q_dtype"], a["heads"], a["topk"], a["k"], a["max_elig"], a["scale"], a["cs"],
+                                  a["rows"], a["group"], a["codes"], a["scales"], a["lse"], FAKE, 1 << 40, None)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(group=8), INVALID), (dict(group=256), INVALID), (dict(group=48), INVALID), (dict(codes=None), INVALID),
+    (dict(scales=None), INVALID), (dict(codes=FAKE + 4), INVALID), (dict(cs=None), INVALID), (dict(heads=0), INVALID),
+    (dict(heads=8), UNSUPPORTED),                                  # not a multiple of 16 heads: no fused epilogue
+    (dict(cache=_cache(dim=256), swa=_raw(dim=256, roles=0, logit_pages=None)), UNSUPPORTED),
+    (dict(cache=_cache(dim=512, dtype=csa.F32), swa=_raw(dim=512, roles=0, logit_pages=None, dtype=csa.F32),
+          q_dtype=csa.F32), UNSUPPORTED),
+])
+def test_attend_quant_fp8_validation(L, bad, code):
+    """Rejected before any HIP call."""
+    assert _attend_q(L, **bad) == code

@@ -535,3 +535,68 @@ def test_bf16_chain_end_to_end(cache_dtype):
     st.run_oracle()
     res = verify(st, TOL[cache_dtype], 1e-4, log=_log)
     _log(f"certified swaps {res['swaps']}, re-attended sequences {res['reattended']}")
+
+
+# ------------------------------------------------------------------ attention with the fp8 output epilogue fused in
+@pytest.mark.parametrize("ratio,heads,dtype,k,group,positions", [
+    (4, 64, "bf16", 512, 128, [9000, 3001, 40, 5]),                      # several key splits: the merge kernel
+    (4, 64, "fp8", 512, 64, [7000, 2222]),
+    (4, 64, "bf16", 64, 32, [300 + (37 * i) % 400 for i in range(520)]),  # one split: the attention epilogue
+    (128, 32, "bf16", 0, 16, [3000, 127, 1025]),                          # 16-head groups, dense c128a
+    (4, 16, "fp8", 2048, 128, [9000]),
+])
+def test_attend_quant_fp8_parity(ratio, heads, dtype, k, group, positions):
+    """csa_attend_quant_fp8 against the oracle's attention followed by its inverse RoPE + grouped fp8 rule (R23).
+
+    The pre-quantisation output may differ from the oracle's by the attention tolerance yerr = TOL * max|row|, so
+    each group's scale may differ by yerr / 448 and each dequantised element by one e4m3 step of the oracle's code
+    (times its scale) plus 2 yerr; the codes must also agree with the unfused GPU path (csa_attend, then
+    csa_inv_rope_quant_fp8) to the same bar."""
+    _log(f"attend quant fp8 ratio={ratio} H={heads} dtype={dtype} k={k} G={group} n_q={len(positions)}")
+    import synth
+    from oracle import output_quant as oq
+    dim, R = 512, 64
+    cfg = 61 + heads + k + group
+    pc = si.paged_cache(cfg, ratio, dim, dtype, positions)
+    n_phys = pc.bt.max() + 1 + 3
+    swa_pages, swa_sc = si.window_rows(cfg, dim, dtype, n_phys)
+    q = synth.normal_bf16_bits(synth.rng(cfg, synth.STREAM_Q), (len(positions), heads, dim))
+    tk = si.topk_lists(cfg, positions, ratio, k) if k else None
+    rows = max(positions) + 1
+    scale = float(1.0 / np.sqrt(dim))
+    table = orope.rope_table(rows, R)
+    o_raw, o_lse = oa.attend(pc.oracle(R), oc.Raw(dtype, dim, 0, swa_pages, None, swa_sc, pc.bt), 128,
+                             np.arange(len(positions)), positions, codecs.load_rows(q, "bf16"), tk, scale, False, table)
+    ref_codes, ref_scales = oq.inv_rope_quant(o_raw, np.asarray(positions), table, R, group)
+    y_ref = orope.inv_rope_queries(o_raw, np.asarray(positions), table, R)
+    gcache = csa.Cache(ratio, pc.window, dim, R, gu.dev_store(pc.pages, dtype), gu.dev_i32(pc.bt),
+                       gu.dev_f32(pc.scales) if pc.scales is not None else None)
+    gswa = csa.Raw(dim, 0, gu.dev_store(swa_pages, dtype), gu.dev_i32(pc.bt), None,
+                   gu.dev_f32(swa_sc) if swa_sc is not None else None)
+    grope = csa.rope_table(rows, R)
+    qs, qp, qd = gu.dev_i32(np.arange(len(positions))), gu.dev_i32(positions), gu.dev_bf16(q)
+    gtk = gu.dev_i32(tk) if tk is not None else None
+    max_elig = max(paging.num_eligible(p, ratio, pc.window) for p in positions)
+    n_q = len(positions)
+    codes = torch.full((n_q, heads, dim), 0xA5, dtype=torch.uint8, device="cuda")
+    scales = torch.full((n_q, heads, dim // group), -7.0, device="cuda")
+    lse = torch.full((n_q, heads), -7.0, device="cuda")
+    csa.attend_quant_fp8(gcache, gswa, 128, qs, qp, qd, gtk, max_elig, scale, grope, group, codes, scales, lse)
+    raw = torch.full((n_q, heads, dim), -7.0, device="cuda")
+    csa.attend(gcache, gswa, 128, qs, qp, qd, gtk, max_elig, scale, False, grope, raw)
+    u_codes, u_scales = csa.inv_rope_quant_fp8(raw, qp, R, grope, group)
+    torch.cuda.synchronize()
+    gc, gs = codes.cpu().numpy(), scales.cpu().numpy()
+    tol = TOL[dtype]
+    yerr = tol * np.abs(y_ref).max(axis=-1, keepdims=True)           # [n_q][H][1]
+    for label, cc, ss in (("oracle", ref_codes, ref_scales), ("unfused GPU", u_codes.cpu().numpy(),
+                                                              u_scales.cpu().numpy())):
+        rs = ss.astype(np.float64)
+        assert np.all(np.abs(gs - rs) <= yerr / 448.0 + 2.0 ** -22 * rs), f"group scales differ from the {label}'s"
+        gv = oq.dequant(gc, gs, group)
+        rv = oq.dequant(cc, ss, group)
+        mag = np.maximum(np.abs(codecs.e4m3_to_f64(cc)), 2.0 ** -6)
+        step = np.ldexp(1.0, np.floor(np.log2(mag)).astype(int) - 3) * np.repeat(rs, group, axis=-1)
+        assert np.all(np.abs(gv - rv) <= 1.01 * step + 2.0 * yerr), f"fp8 outputs differ from the {label}'s"
+        _log(f"identical codes vs {label}: {np.mean(gc == cc):.5f}")
+    assert np.allclose(lse.cpu().numpy(), o_lse, rtol=0, atol=1e-4)
