@@ -169,7 +169,9 @@ EAGER_ONLY = False
 STEP_MODES = {"eager": "eager launches on one stream with an event between stages",
               "graph": "one HIP graph per layer, every call on one stream",
               "graph_2stream": "one HIP graph per layer, main-cache compress_insert on a second stream beside the "
-                               "indexer pipeline"}
+                               "indexer pipeline",
+              "graph_partition": "one HIP graph per layer, the indexer pipeline (its compress_insert, score, select) on "
+                                 "a second stream beside the main-cache compress_insert"}
 
 
 def capture_graphs(torch, layers, fn):
@@ -200,21 +202,100 @@ def time_graphs(torch, graphs, steps, warmup):
     return t0.elapsed_time(t1)
 
 
-def best_graph_mode(torch, layers, steps, warmup, sequential, two_stream):
-    """Time the step as one HIP graph per layer, issued on one stream and with the main-cache compress on a second
-    stream; returns (ms of the faster mode, its name, ms of each mode). With --eager-only (profiler runs) no graph
-    is built and (None, "eager", {}) comes back."""
+def replay_percentiles(torch, graphs, steps):
+    """Each replay between its own pair of events (a separate pass after the timed region): p10 / median / p90 of
+    the per-step time in microseconds."""
+    ev = []
+    for i in range(steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        graphs[i % len(graphs)].replay()
+        b.record()
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    v = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    return {"p10": round(float(np.percentile(v, 10)), 2), "median": round(float(np.median(v)), 2),
+            "p90": round(float(np.percentile(v, 90)), 2), "n": int(len(v))}
+
+
+LAST_PERCENTILES = {}
+
+
+def best_graph_mode(torch, layers, steps, warmup, sequential, two_stream, partitioned=None):
+    """Time the step as one HIP graph per layer in each stream arrangement given (all on one stream; main-cache
+    compress on a second stream; the indexer pipeline on a second stream); returns (ms of the fastest, its name, ms
+    of each). The per-step percentiles of the fastest are left in LAST_PERCENTILES. With --eager-only (profiler
+    runs) no graph is built and (None, "eager", {}) comes back."""
+    LAST_PERCENTILES.clear()
     if EAGER_ONLY:
         return None, "eager", {}
-    modes = {}
-    for name, fn in (("graph", sequential), ("graph_2stream", two_stream)):
+    modes, kept = {}, {}
+    for name, fn in (("graph", sequential), ("graph_2stream", two_stream), ("graph_partition", partitioned)):
         if fn is None:
             continue
         graphs = capture_graphs(torch, layers, fn)
         modes[name] = time_graphs(torch, graphs, steps, warmup)
-        del graphs
+        kept[name] = graphs
     best = min(modes, key=modes.get)
+    LAST_PERCENTILES.update(replay_percentiles(torch, kept[best], steps))
+    del kept
     return modes[best], best, modes
+
+
+def partition_modes(torch, layers, steps, warmup, prepare, main_compress, index_path, attend, pair=None):
+    """The step with the query / window-key preparation in front (csa_prepare_qk), captured two ways: every call on
+    one stream (the indexer and main compress as one paired launch when `pair` is given), and the pages' two-stream
+    partition -- on a c4a layer the indexer pipeline (its compress, score, select) on a second stream beside main
+    compress + window insert, on a c128a layer (index_path None) main compress beside the window insert; attention
+    joins. Returns ms per step of each, or {} without graphs."""
+    if EAGER_ONLY:
+        return {}
+    side = torch.cuda.Stream()
+
+    def single(ly):
+        prepare(ly)
+        if pair is not None:
+            pair(ly)
+        else:
+            main_compress(ly)
+        if index_path is not None:
+            index_path(ly)
+        attend(ly)
+
+    def split(ly):
+        cur = torch.cuda.current_stream()
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            if index_path is not None:
+                index_path(ly)
+            else:
+                main_compress(ly)
+        if index_path is not None:
+            main_compress(ly)
+        prepare(ly)
+        cur.wait_stream(side)
+        attend(ly)
+
+    out = {}
+    for name, fn in (("single_stream", single), ("partition_2stream", split)):
+        graphs = capture_graphs(torch, layers, fn)
+        out[name] = time_graphs(torch, graphs, steps, warmup) / steps
+        del graphs
+    return {k: round(v, 5) for k, v in out.items()}
+
+
+def partitioned(torch, side, main_compress, index_path, attend):
+    """The decode step with the indexer pipeline on a second stream beside the main-cache compress ([P1] "GPU Compute
+    Saturation", [P2] "3.2 內核"); attention joins both."""
+    def fn(ly):
+        cur = torch.cuda.current_stream()
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            index_path(ly)
+        main_compress(ly)
+        cur.wait_stream(side)
+        attend(ly)
+    return fn
 
 
 def overlapped(torch, side, main_compress, index_path, attend):
@@ -299,8 +380,7 @@ def run_gpu(args, lens):
 
     # the step as deployed: one HIP graph per layer, main-cache compress overlapped with the indexer pipeline
     side = torch.cuda.Stream()
-    fn = overlapped(
-        torch, side,
+    parts = (
         lambda ly: csa.compress_insert(ly.cache, ly.state, ly.pos, ly.cu1, ly.kv1, ly.lg1, ly.gamma, 1e-6, rope_main, 1),
         lambda ly: (csa.compress_insert(ly.icache, ly.istate, ly.pos, ly.cu1, ly.ikv1, ly.ilg1, ly.igamma, 1e-6,
                                         rope_idx, 1),
@@ -310,9 +390,32 @@ def run_gpu(args, lens):
         lambda ly: csa.attend(ly.cache, ly.swa, SWA, ly.seq, ly.pos, ly.q, topk, max_elig, scale, True, rope_main, out,
                               workspace=att_ws))
     wall0 = time.time()
-    total_ms, mode, modes = best_graph_mode(torch, layers, args.steps, args.warmup, lambda ly: step(ly, None), fn)
+    fn = overlapped(torch, side, *parts)
+    fn_p = partitioned(torch, torch.cuda.Stream(), *parts)
+    total_ms, mode, modes = best_graph_mode(torch, layers, args.steps, args.warmup, lambda ly: step(ly, None), fn,
+                                            fn_p)
     wall = time.time() - wall0
+    pct = dict(LAST_PERCENTILES)
+    for ly in layers:
+        ly.q_raw = ly.q.clone()          # synthetic un-normed queries; prepare writes the attention's query
+        ly.q_gamma = torch.ones(D, device="cuda")
+    f4 = partition_modes(
+        torch, layers, args.steps, args.warmup,
+        lambda ly: csa.prepare_qk(ly.q_raw, ly.kv1, ly.seq, ly.pos, ly.q_gamma, 1e-6, ly.swa, R, rope_main, ly.q),
+        lambda ly: csa.compress_insert(ly.cache, ly.state, ly.pos, ly.cu1, ly.kv1, ly.lg1, ly.gamma, 1e-6, rope_main, 1),
+        lambda ly: (csa.compress_insert(ly.icache, ly.istate, ly.pos, ly.cu1, ly.ikv1, ly.ilg1, ly.igamma, 1e-6,
+                                        rope_idx, 1),
+                    csa.index_score(ly.icache, ly.seq, ly.pos, max_elig, ly.q_idx, ly.head_w, csa.SCORE_WRELU, K_TOP,
+                                    ws),
+                    csa.index_select(ly.icache, ly.seq, ly.pos, max_elig, K_TOP, topk, ws)),
+        lambda ly: csa.attend(ly.cache, ly.swa, SWA, ly.seq, ly.pos, ly.q, topk, max_elig, scale, True, rope_main, out,
+                              workspace=att_ws),
+        pair=lambda ly: csa.compress_insert_pair(ly.cache, ly.state, ly.kv1, ly.lg1, ly.gamma, rope_main, ly.icache,
+                                                 ly.istate, ly.ikv1, ly.ilg1, ly.igamma, rope_idx, ly.pos, ly.cu1, 1e-6,
+                                                 1))
     epilogue = time_output_epilogue(torch, csa, layers, step, out, topk, max_elig, scale, rope_main, att_ws)
+    epilogue["step_with_prepare_ms"] = f4
+    epilogue["step_us_percentiles"] = pct
     epilogue["upstream_prepare"] = time_prepare(torch, csa, layers[-1], rope_main)
     return total_ms, eager_ms, wall, stage_ms, copy_gbs, mode, modes, epilogue
 
@@ -514,8 +617,7 @@ def run_c4(args, torch, csa, fp4_idx=False):
     eager_ms, st = time_steps(torch, step, layers, args.steps, args.warmup, 4)
     stage = dict(zip(["compress", "score", "select", "attend"], st))
     side = torch.cuda.Stream()
-    fn = overlapped(
-        torch, side,
+    parts = (
         lambda ly: csa.compress_insert(ly.cache, ly.state, ly.pos, ly.cu1, ly.kv1, ly.lg1, ly.gamma, 1e-6, rope, 1),
         lambda ly: (csa.compress_insert(ly.icache, ly.istate, ly.pos, ly.cu1, ly.ikv1, ly.ilg1, ly.igamma, 1e-6, rope, 1),
                     csa.index_score(ly.icache, ly.seq, ly.pos, max_elig, ly.q_idx, ly.head_w, csa.SCORE_WRELU, K_TOP,
@@ -523,8 +625,26 @@ def run_c4(args, torch, csa, fp4_idx=False):
                     csa.index_select(ly.icache, ly.seq, ly.pos, max_elig, K_TOP, topk, ws)),
         lambda ly: csa.attend(ly.cache, ly.swa, SWA, ly.seq, ly.pos, ly.q, topk, max_elig, 1.0 / math.sqrt(D), True,
                               rope, out, workspace=att_ws))
-    total_ms, mode, modes = best_graph_mode(torch, layers, args.steps, args.warmup, lambda ly: step(ly, None), fn)
+    fn = overlapped(torch, side, *parts)
+    fn_p = partitioned(torch, torch.cuda.Stream(), *parts)
+    total_ms, mode, modes = best_graph_mode(torch, layers, args.steps, args.warmup, lambda ly: step(ly, None), fn,
+                                            fn_p)
     total_ms = eager_ms if total_ms is None else total_ms
+    pct = dict(LAST_PERCENTILES)
+    for ly in layers:
+        ly.q_raw, ly.q_gamma = ly.q.clone(), torch.ones(D, device="cuda")
+    f4 = partition_modes(
+        torch, layers, args.steps, args.warmup,
+        lambda ly: csa.prepare_qk(ly.q_raw, ly.kv1, ly.seq, ly.pos, ly.q_gamma, 1e-6, ly.swa, R, rope, ly.q),
+        lambda ly: csa.compress_insert(ly.cache, ly.state, ly.pos, ly.cu1, ly.kv1, ly.lg1, ly.gamma, 1e-6, rope, 1),
+        lambda ly: (csa.compress_insert(ly.icache, ly.istate, ly.pos, ly.cu1, ly.ikv1, ly.ilg1, ly.igamma, 1e-6, rope, 1),
+                    csa.index_score(ly.icache, ly.seq, ly.pos, max_elig, ly.q_idx, ly.head_w, csa.SCORE_WRELU, K_TOP,
+                                    ws),
+                    csa.index_select(ly.icache, ly.seq, ly.pos, max_elig, K_TOP, topk, ws)),
+        lambda ly: csa.attend(ly.cache, ly.swa, SWA, ly.seq, ly.pos, ly.q, topk, max_elig, 1.0 / math.sqrt(D), True,
+                              rope, out, workspace=att_ws),
+        pair=lambda ly: csa.compress_insert_pair(ly.cache, ly.state, ly.kv1, ly.lg1, ly.gamma, rope, ly.icache,
+                                                 ly.istate, ly.ikv1, ly.ilg1, ly.igamma, rope, ly.pos, ly.cu1, 1e-6, 1))
     sb, kb, ab = (B * x for x in _decode_bytes(max_elig, P, D + 4, row_i + 4, K_TOP, True))
     del layers, pool_m, pool_ms, pool_i, pool_is, ws
     torch.cuda.empty_cache()
@@ -542,8 +662,11 @@ def run_c4(args, torch, csa, fp4_idx=False):
                               **{k: round(v / args.steps, 5) for k, v in modes.items()}},
         "dtype": ("fp8 e4m3 main cache, MXFP4 indexer cache" if fp4_idx else "fp8 e4m3 caches") +
                  ", bf16 queries, fp32 accumulate",
+        "step_us_percentiles": pct,
         "stages_us": {k: round(v * 1e3, 2) for k, v in stage.items()},
-        "roofline": {"bound": "hbm", "kernel": f"score_mfma_kernel<{'fp4' if fp4_idx else 'fp8'}> (index score)",
+        "step_with_prepare_ms": f4,
+        "roofline": {"bound": "hbm", "kernel": f"{'score_mfma_kernel<fp4>' if fp4_idx else 'score_lt_kernel<fp8>'} "
+                                               "(index score)",
                      "achieved": round(score_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(score_gbs / HBM_PEAK_GBS, 4),
                      "traffic": score_traffic("c4f" if fp4_idx else "c4"),
@@ -603,6 +726,16 @@ def run_c2(args, torch, csa):
     stage = dict(zip(["compress", "attend"], st))
     total_ms, mode, modes = best_graph_mode(torch, layers, args.steps, args.warmup, lambda ly: step(ly, None), None)
     total_ms = eager_ms if total_ms is None else total_ms
+    pct = dict(LAST_PERCENTILES)
+    for ly in layers:
+        ly.q_raw, ly.q_gamma = ly.q.clone(), torch.ones(D, device="cuda")
+    f4 = partition_modes(
+        torch, layers, args.steps, args.warmup,
+        lambda ly: csa.prepare_qk(ly.q_raw, ly.kv1, ly.seq, ly.pos, ly.q_gamma, 1e-6, ly.swa, R, rope, ly.q),
+        lambda ly: csa.compress_insert(ly.cache, ly.state, ly.pos, ly.cu1, ly.kv1, ly.lg1, gamma, 1e-6, rope, 1),
+        None,
+        lambda ly: csa.attend(ly.cache, ly.swa, SWA, ly.seq, ly.pos, ly.q, None, n_elig, 1.0 / math.sqrt(D), True,
+                              rope, out, workspace=att_ws))
     _, _, ab = (B * x for x in _decode_bytes(n_elig, P, 2 * D, 0, 0, False))
     del layers
     torch.cuda.empty_cache()
@@ -615,7 +748,9 @@ def run_c2(args, torch, csa):
         "modes_ms_per_step": {"eager_with_stage_events": round(eager_ms / args.steps, 5),
                               **{k: round(v / args.steps, 5) for k, v in modes.items()}},
         "dtype": "bf16",
+        "step_us_percentiles": pct,
         "stages_us": {k: round(v * 1e3, 2) for k, v in stage.items()},
+        "step_with_prepare_ms": dict(f4, note="main compress beside the window insert on c128a layers"),
         "roofline": {"bound": "hbm", "kernel": "attend_split_kernel + attend_combine_kernel (dense)",
                      "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": ab,
@@ -716,7 +851,7 @@ def run_c5(args, torch, csa):
         "stages_us": {k: round(v * 1e3, 1) for k, v in stage.items()},
         "mfma": {k: {"flop": fl, "tflops": round(tf(fl, ms), 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "frac": round(tf(fl, ms) / MFMA_BF16_PEAK_TFLOPS, 4)} for k, (fl, ms) in mf.items()},
-        "roofline": {"bound": "mfma", "kernel": "score_mfma_kernel (index score, 4096 queries)",
+        "roofline": {"bound": "mfma", "kernel": "score_shared_kernel (index score, 4096 queries)",
                      "achieved": round(tf(score_fl, stage["score"]), 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tf(score_fl, stage["score"]) / MFMA_BF16_PEAK_TFLOPS, 4),
                      "avg_launch_us": round(stage["score"] * 1e3, 1)},
@@ -729,52 +864,209 @@ SIDE = {"c4": ("c4a_fp8_1m", run_c4),
 
 
 # ------------------------------------------------------------------ CPU baseline: the oracle, untuned
-def cpu_baseline(lens, min_seconds=10.0, n_seq=8):
-    import synth
-    from oracle import attend as oa, codecs, compress as oc, index as oi, paging, rope as orope
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = os.cpu_count() or 1
-    g = synth.rng(CONFIG_ID, 40)
-    seqs = []
-    for b in range(n_seq):
-        L = int(lens[b])
-        nb = L // 256 + 1
-        bt = np.arange(nb, dtype=np.int32)[None]
-        tail = np.full((1, nb), -1, np.int32)  # window / state pages: only the last two blocks are mapped
-        tail[0, nb - 2], tail[0, nb - 1] = 0, 1
-        mc = oc.Cache(4, 8, D, R, "bf16", synth.normal_bf16_bits(g, (nb * 64, D)), None, bt)
-        ic = oc.Cache(4, 8, D_IDX, R_IDX, "bf16", synth.normal_bf16_bits(g, (nb * 64, D_IDX)), None, bt)
-        swa = oc.Raw("bf16", D, 0, synth.normal_bf16_bits(g, (512, D)), None, None, tail)
-        st = oc.Raw("bf16", D, 2, synth.normal_bf16_bits(g, (512, D)), synth.normal_bf16_bits(g, (512, 2, D)), None, tail)
-        ist = oc.Raw("bf16", D_IDX, 2, synth.normal_bf16_bits(g, (512, D_IDX)),
-                     synth.normal_bf16_bits(g, (512, 2, D_IDX)), None, tail)
-        new = (synth.normal_bf16_bits(g, (1, D)), synth.normal_bf16_bits(g, (1, 2, D)),
-               synth.normal_bf16_bits(g, (1, D_IDX)), synth.normal_bf16_bits(g, (1, 2, D_IDX)))
-        q = codecs.load_rows(synth.normal_bf16_bits(g, (1, H, D)), "bf16")
-        qi = codecs.load_rows(synth.normal_bf16_bits(g, (1, H_IDX, D_IDX)), "bf16")
-        w = synth.uniform_f32(g, (1, H_IDX))
-        seqs.append((L, mc, ic, swa, st, ist, new, q, qi, w))
-    table = orope.rope_table(LEN_HI + 2, R)
-    itable = orope.rope_table(LEN_HI + 2, R_IDX)
-    one = np.array([0, 1], np.int32)
-    queries, t0 = 0, time.time()
+        return os.cpu_count() or 1
+
+
+def _time_units(fn, min_seconds):
+    """Call fn() (one unit of work each) until min_seconds have passed; (units, seconds)."""
+    n, t0 = 0, time.time()
     while True:
-        for (L, mc, ic, swa, st, ist, new, q, qi, w) in seqs:
-            oc.compress_insert(mc, st, [L], one, new[0], new[1], np.ones(D), 1e-6, table, 1)
-            oc.compress_insert(ic, ist, [L], one, new[2], new[3], np.ones(D_IDX), 1e-6, itable, 1)
-            idx, _, _ = oi.index_topk(ic, [0], [L], qi, w, oi.WRELU, K_TOP)
-            oa.attend(mc, swa, SWA, [0], [L], q, idx, 1.0 / math.sqrt(D), True, table)
-            queries += 1
+        fn(n)
+        n += 1
         if time.time() - t0 >= min_seconds:
-            break
-    dt = time.time() - t0
-    return {"value": queries / dt, "unit": "queries/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{queries} decode queries ({n_seq} sequences of the workload, contexts "
-                      f"{int(min(lens[:n_seq]))}-{int(max(lens[:n_seq]))}, repeated) through the numpy fp64 oracle: "
-                      f"compress_insert x2, index_topk, attend with inverse RoPE; {dt:.1f} s"}
+            return n, time.time() - t0
+
+
+def _timed_both(fn, min_seconds, unit, sample):
+    """The oracle at the BLAS library's default thread count and at one thread."""
+    from threadpoolctl import threadpool_limits
+    threads = _blas_threads()
+    n, dt = _time_units(fn, min_seconds)
+    with threadpool_limits(limits=1):
+        n1, dt1 = _time_units(fn, min_seconds)
+    return {"value": n / dt, "unit": unit, "cores": int(threads), "kind": "oracle",
+            "value_1_thread": n1 / dt1, "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+            "sample": sample + f"; {n} units in {dt:.1f} s at {threads} BLAS threads, {n1} in {dt1:.1f} s at 1 thread"}
+
+
+def _host_decode_layer(g, L, ratio, main_dt, idx_dt, dim_i, fp4_idx=False):
+    """Oracle host caches of one sequence at position L: identity block table, every entry drawn (bf16 N(0,1) rows
+    or the per-row e4m3 rows of synth), window / compressor-state pages for the last two blocks only."""
+    import synth
+    from oracle import codecs, compress as oc
+    nb = L // 256 + 1
+    E = 256 // ratio
+    window = 8 if ratio == 4 else 128
+    bt = np.arange(nb, dtype=np.int32)[None]
+    tail = np.full((1, nb), -1, np.int32)
+    tail[0, nb - 2], tail[0, nb - 1] = 0, 1
+
+    def cache(dim, dt, rope):
+        if dt == "bf16":
+            return oc.Cache(ratio, window, dim, rope, "bf16", synth.normal_bf16_bits(g, (nb * E, dim)), None, bt)
+        if dt == "fp8":
+            codes, sc = synth.e4m3_rows(g, nb * E, dim)
+            return oc.Cache(ratio, window, dim, rope, "fp8", codes, sc, bt)
+        # MXFP4: random e2m1 codes and block exponents around 2^-2
+        pk = g.integers(0, 256, size=(nb * E, dim // 2), dtype=np.uint8)
+        ex = (125 + g.integers(0, 3, size=(nb * E, dim // 32))).astype(np.uint8)
+        return oc.Cache(ratio, window, dim, rope, "fp4", pk, ex, bt)
+
+    mc = cache(D, main_dt, R)
+    ic = cache(dim_i, idx_dt, R_IDX) if dim_i else None
+    if main_dt == "fp8":
+        wp, ws_ = synth.e4m3_rows(g, 512, D)
+        swa = oc.Raw("fp8", D, 0, wp, None, ws_, tail)
+    else:
+        swa = oc.Raw("bf16", D, 0, synth.normal_bf16_bits(g, (512, D)), None, None, tail)
+    roles = window // ratio
+    st = oc.Raw("bf16", D, roles, synth.normal_bf16_bits(g, (512, D)), synth.normal_bf16_bits(g, (512, roles, D)), None,
+                tail)
+    ist = oc.Raw("bf16", dim_i, 2, synth.normal_bf16_bits(g, (512, dim_i)),
+                 synth.normal_bf16_bits(g, (512, 2, dim_i)), None, tail) if dim_i else None
+    return mc, ic, swa, st, ist
+
+
+def _decode_unit(L, layer, g, tables, with_index):
+    """One decode query through the oracle: compress_insert of the token (main and, with an index, indexer),
+    index_topk, attention with inverse RoPE."""
+    import synth
+    from oracle import attend as oa, codecs, compress as oc, index as oi
+    mc, ic, swa, st, ist = layer
+    table, itable = tables
+    roles = st.roles
+    new = (synth.normal_bf16_bits(g, (1, D)), synth.normal_bf16_bits(g, (1, roles, D)))
+    q = codecs.load_rows(synth.normal_bf16_bits(g, (1, H, D)), "bf16")
+    one = np.array([0, 1], np.int32)
+
+    def run(_):
+        oc.compress_insert(mc, st, [L], one, new[0], new[1], np.ones(D), 1e-6, table, 1)
+        idx = None
+        if with_index:
+            inew = (synth.normal_bf16_bits(g, (1, D_IDX)), synth.normal_bf16_bits(g, (1, 2, D_IDX)))
+            oc.compress_insert(ic, ist, [L], one, inew[0], inew[1], np.ones(D_IDX), 1e-6, itable, 1)
+            qi = codecs.load_rows(synth.normal_bf16_bits(g, (1, H_IDX, D_IDX)), "bf16")
+            idx, _, _ = oi.index_topk(ic, [0], [L], qi, synth.uniform_f32(g, (1, H_IDX)), oi.WRELU, K_TOP)
+        oa.attend(mc, swa, SWA, [0], [L], q, idx, 1.0 / math.sqrt(D), True, table)
+    return run
+
+
+def cpu_baseline(lens, min_seconds=10.0, n_seq=8):
+    """128K bf16 decode: the full step for 8 sequences of the workload, repeated."""
+    import synth
+    from oracle import rope as orope
+    g = synth.rng(CONFIG_ID, 40)
+    tables = (orope.rope_table(LEN_HI + 2, R), orope.rope_table(LEN_HI + 2, R_IDX))
+    units = [_decode_unit(int(lens[b]), _host_decode_layer(g, int(lens[b]), 4, "bf16", "bf16", D_IDX), g, tables, True)
+             for b in range(n_seq)]
+    return _timed_both(lambda n: units[n % n_seq](n), min_seconds, "queries/s",
+                       f"decode queries of {n_seq} sequences of the workload (contexts {int(min(lens[:n_seq]))}-"
+                       f"{int(max(lens[:n_seq]))}) through the numpy fp64 oracle: compress_insert x2, index_topk, "
+                       "attend with inverse RoPE")
+
+
+def cpu_baseline_c4(min_seconds, fp4_idx=False):
+    """1M fp8 decode (fp8 or MXFP4 indexer cache): the full step of one sequence at 2^20, repeated."""
+    import synth
+    from oracle import rope as orope
+    P = 1 << 20
+    g = synth.rng(4, 40)
+    tables = (orope.rope_table(P + 2, R), orope.rope_table(P + 2, R_IDX))
+    unit = _decode_unit(P, _host_decode_layer(g, P, 4, "fp8", "fp4" if fp4_idx else "fp8", D_IDX), g, tables, True)
+    return _timed_both(unit, min_seconds, "queries/s",
+                       "decode queries at 2^20 (262143 eligible entries, fp8 main cache, "
+                       f"{'MXFP4' if fp4_idx else 'fp8'} indexer cache) through the numpy fp64 oracle: compress_insert "
+                       "x2, index_topk, attend with inverse RoPE")
+
+
+def cpu_baseline_c2(min_seconds):
+    """c128a dense 64K decode: compress_insert of the token and dense attention, repeated."""
+    import synth
+    from oracle import rope as orope
+    P = 65536
+    g = synth.rng(2, 40)
+    tables = (orope.rope_table(P + 2, R), None)
+    unit = _decode_unit(P, _host_decode_layer(g, P, 128, "bf16", None, 0), g, tables, False)
+    return _timed_both(unit, min_seconds, "queries/s",
+                       "decode queries at 65536 (512 c128a entries, dense + window 128) through the numpy fp64 oracle: "
+                       "compress_insert, attend with inverse RoPE")
+
+
+def cpu_baseline_c5(min_seconds, n_sample=8):
+    """Prefill chunk at 262144: per-token oracle work on a deterministic sample of the chunk's queries (index_topk +
+    c4a attention + dense c128a attention each) plus the chunk's compression (three caches) of one sequence, timed
+    separately and charged per token."""
+    import synth
+    from oracle import attend as oa, codecs, compress as oc, index as oi, rope as orope
+    CTX, CH = 262144, 2048
+    g = synth.rng(5, 40)
+    table, itable = orope.rope_table(CTX + CH + 2, R), orope.rope_table(CTX + CH + 2, R_IDX)
+    L = CTX + CH - 1
+    mc, ic, swa, st, ist = _host_decode_layer(g, L, 4, "bf16", "bf16", D_IDX)
+    hc, _, _, hst, _ = _host_decode_layer(g, L, 128, "bf16", None, 0)
+    pos = [CTX + int(i * (CH - 1) / (n_sample - 1)) for i in range(n_sample)]   # first, last and evenly between
+    qs = [codecs.load_rows(synth.normal_bf16_bits(g, (1, H, D)), "bf16") for _ in pos]
+    qis = [codecs.load_rows(synth.normal_bf16_bits(g, (1, H_IDX, D_IDX)), "bf16") for _ in pos]
+    w = synth.uniform_f32(g, (1, H_IDX))
+
+    def per_query(n):
+        i = n % n_sample
+        idx, _, _ = oi.index_topk(ic, [0], [pos[i]], qis[i], w, oi.WRELU, K_TOP)
+        oa.attend(mc, swa, SWA, [0], [pos[i]], qs[i], idx, 1.0 / math.sqrt(D), True, table)
+        oa.attend(hc, swa, SWA, [0], [pos[i]], qs[i], None, 1.0 / math.sqrt(D), True, table)
+
+    n_tok = 256  # compression of the chunk's first 256 tokens of one sequence into all three caches
+    kv = synth.normal_bf16_bits(g, (n_tok, D))
+    lg2, lg1 = synth.normal_bf16_bits(g, (n_tok, 2, D)), synth.normal_bf16_bits(g, (n_tok, 1, D))
+    ikv, ilg = synth.normal_bf16_bits(g, (n_tok, D_IDX)), synth.normal_bf16_bits(g, (n_tok, 2, D_IDX))
+    cu = np.array([0, n_tok], np.int32)
+    # window / state pages of the oracle layer map only the last two blocks: give the compressor the chunk's blocks
+    for raw in (st, ist, hst):
+        raw.block_table = np.full_like(raw.block_table, -1)
+        raw.block_table[0, CTX // 256 - 1], raw.block_table[0, CTX // 256] = 0, 1
+
+    def compress(_):
+        oc.compress_insert(mc, st, [CTX], cu, kv, lg2, np.ones(D), 1e-6, table, 0)
+        oc.compress_insert(ic, ist, [CTX], cu, ikv, ilg, np.ones(D_IDX), 1e-6, itable, 0)
+        oc.compress_insert(hc, hst, [CTX], cu, kv, lg1, np.ones(D), 1e-6, table, 0)
+
+    from threadpoolctl import threadpool_limits
+    threads = _blas_threads()
+    res = {}
+    for label, limit in (("", None), ("_1_thread", 1)):
+        with threadpool_limits(limits=limit):
+            nq, tq = _time_units(per_query, min_seconds)
+            nc, tc = _time_units(compress, min(min_seconds, 5.0))
+        per_tok = tq / nq + tc / (nc * n_tok)
+        res["value" + label] = 1.0 / per_tok
+        res["detail" + label] = f"{nq} queries in {tq:.1f} s, chunk compression {nc} x {n_tok} tokens in {tc:.1f} s"
+    return {"value": res["value"], "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "value_1_thread": res["value_1_thread"], "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+            "sample": f"prefill chunk at {CTX}: per token = oracle index_topk + c4a attention + dense c128a attention "
+                      f"of one of {n_sample} sampled queries (positions {pos[0]}..{pos[-1]}, evenly spaced) plus the "
+                      f"oracle compression of the chunk into the three caches per token (measured on {n_tok} tokens "
+                      f"of one sequence); {res['detail']} at {threads} BLAS threads; {res['detail_1_thread']} at 1 "
+                      "thread"}
+
+
+CPU_SIDE = {"c4a_fp8_1m": lambda sec: cpu_baseline_c4(sec), "c4a_fp8_fp4idx_1m": lambda sec: cpu_baseline_c4(sec, True),
+            "c128a_dense_64k": cpu_baseline_c2, "prefill_chunk_256k": cpu_baseline_c5}
 
 
 def main():
@@ -793,7 +1085,8 @@ def main():
     ap.add_argument("--steps-c5", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager-only", action="store_true", help="no HIP graphs (for profiler counter runs)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=5.0,
+                    help="seconds of oracle work per workload and thread setting")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this path runs per GPU with no exchange (sequences shard by data "
@@ -822,6 +1115,7 @@ def main():
         "step_mode": STEP_MODES[mode] + " (stage times below come from an eager pass with an event between stages)",
         "modes_ms_per_step": {"eager_with_stage_events": round(eager_ms / args.steps, 5),
                               **{k: round(v / args.steps, 5) for k, v in modes.items()}},
+        "step_us_percentiles": epilogue.pop("step_us_percentiles"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -831,7 +1125,7 @@ def main():
                                "(RoPE 64), indexer 64 heads x 128 WRELU, top-512 + window 128, 256-position pages",
                    "batch": B, "context_lo": LEN_LO, "context_hi": LEN_HI, "heads": H, "dim": D, "top_k": K_TOP,
                    "window": SWA, "layers_rotated": args.layers, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "kernel": "score_mfma_kernel (index score)",
+        "roofline": {"bound": "hbm", "kernel": "score_lt_kernel (index score)",
                      "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(score_gbs / HBM_PEAK_GBS, 4), "traffic": score_traffic("c3"),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated)",
@@ -842,6 +1136,10 @@ def main():
                           "alg_bytes": path_bytes, "us": round(path_ms * 1e3, 2)},
         "stages_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
         "upstream_prepare": epilogue.pop("upstream_prepare"),
+        "step_with_prepare_ms": dict(epilogue.pop("step_with_prepare_ms"),
+                                     note="prepare_qk + compress + index + attend as one graph per layer: all on one "
+                                          "stream, or the indexer pipeline on a second stream beside main compress + "
+                                          "window insert"),
         "fp8_output_epilogue": epilogue,
         "copy_gbs": round(copy_gbs, 1),
         "wall_s_timed": round(wall, 3),
@@ -865,6 +1163,10 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         res["cpu_baseline"] = cpu_baseline(lens, args.cpu_seconds)
+        for name, w in res.get("workloads", {}).items():
+            if name in CPU_SIDE and "error" not in w:
+                log(f"timing the CPU oracle on {name}")
+                w["cpu_baseline"] = CPU_SIDE[name](args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 

@@ -38,6 +38,7 @@ class StepConfig:
     theta: float = 10000.0
     eps: float = 1e-6
     random_gamma: bool = False
+    prepare: bool = False      # query norm + RoPE and the decode token's window-key insert (csa_prepare_qk) up front
 
 
 def _draw(g, shape, dtype):
@@ -87,6 +88,10 @@ class Step:
         qdt = "f32" if c.cache_dtype == "f32" else "bf16"
         self.q_dtype = qdt
         self.q = _draw(gq, (B, c.heads, c.dim), qdt)
+        if c.prepare:  # raw (un-normed, un-rotated) queries and the query norm's weights
+            self.q_raw = (_draw(gq, (B, c.heads, c.dim), "f32") * 3.0).astype(np.float32) if qdt == "f32" else \
+                _draw(gq, (B, c.heads, c.dim), qdt)
+            self.q_gamma = synth.uniform_f32(synth.rng(c.seed, 21), (c.dim,), 0.5, 1.5)
         if c.indexer:
             gqi = synth.rng(c.seed, synth.STREAM_QIDX)
             self.qi_dtype = "f32" if c.idx_dtype == "f32" else "bf16"
@@ -125,39 +130,116 @@ class Step:
                             _dev_in(lgn, c.in_dtype), gu.dev_f32(gamma), c.eps, rope_cs, mx, slots, cnt)
         return slots, cnt
 
-    def run_gpu(self):
+    def _compress_args(self, kv, lg, lo, hi):
+        """Device arguments of one compress_insert call that inserts positions lo[b] .. hi[b]-1 of every sequence."""
+        c = self.cfg
+        n = [h - l for l, h in zip(lo, hi)]
+        cu = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+        kvn = np.concatenate([kv[b][lo[b]:hi[b]] for b in range(self.B)])
+        lgn = np.concatenate([lg[b][lo[b]:hi[b]] for b in range(self.B)])
+        bound = max((max(n) + c.ratio - 1) // c.ratio, 1)
+        return dict(start=gu.dev_i32(lo), cu=gu.dev_i32(cu), kv=_dev_in(kvn, c.in_dtype), lg=_dev_in(lgn, c.in_dtype),
+                    mx=max(n), slots=torch.full((self.B, bound), -7, dtype=torch.int32, device="cuda"),
+                    cnt=torch.full((self.B,), -7, dtype=torch.int32, device="cuda"))
+
+    def _compress_call(self, cache, state, gamma, rope_cs, a):
+        csa.compress_insert(cache, state, a["start"], a["cu"], a["kv"], a["lg"], gamma, self.cfg.eps, rope_cs, a["mx"],
+                            a["slots"], a["cnt"])
+
+    def gpu_setup(self):
+        """Everything before the decode step: tables, caches built from the prefix, window pages, decode inputs and
+        every buffer the step writes (so the step itself allocates nothing and can be captured)."""
         c = self.cfg
         self.g_rope = csa.rope_table(self.rows, max(c.rope_dims, 2), c.theta)
         self.g_cache = self._gpu_cache(c.dim, c.rope_dims, c.cache_dtype)
         self.g_state = self._gpu_state(c.dim, self.coff)
+        self.g_gamma = gu.dev_f32(self.gamma)
         zeros = [0] * self.B
         lens = list(c.lens)
         ends = [L + 1 for L in lens]
-        self.g_prefill = self._gpu_compress(self.g_cache, self.g_state, self.kv, self.lg, self.gamma, self.g_rope, zeros, lens)
-        self.g_decode = self._gpu_compress(self.g_cache, self.g_state, self.kv, self.lg, self.gamma, self.g_rope, lens, ends)
+        pre = self._compress_args(self.kv, self.lg, zeros, lens)
+        self._compress_call(self.g_cache, self.g_state, self.g_gamma, self.g_rope, pre)
+        self.g_prefill = (pre["slots"], pre["cnt"])
+        self.dec_args = self._compress_args(self.kv, self.lg, lens, ends)
+        self.g_decode = (self.dec_args["slots"], self.dec_args["cnt"])
         swa_pages = gu.dev_store(self.swa_pages, c.cache_dtype)
         swa_sc = gu.dev_f32(self.swa_scales) if self.swa_scales is not None else None
         self.g_swa = csa.Raw(c.dim, 0, swa_pages, gu.dev_i32(self.bt), None, swa_sc)
-        q_seq, q_pos = gu.dev_i32(self.q_seq), gu.dev_i32(self.q_pos)
-        max_elig = max(paging.num_eligible(int(p), c.ratio, self.window) for p in self.q_pos)
-        self.max_elig = max_elig
+        self.g_qseq, self.g_qpos = gu.dev_i32(self.q_seq), gu.dev_i32(self.q_pos)
+        self.max_elig = max(paging.num_eligible(int(p), c.ratio, self.window) for p in self.q_pos)
+        if c.prepare:
+            self.g_qraw = _dev_in(self.q_raw, self.q_dtype)
+            self.g_qgamma = gu.dev_f32(self.q_gamma)
+            tok = np.stack([self.kv[b][L] for b, L in enumerate(lens)])
+            if self.q_dtype == c.in_dtype:
+                self.g_kvtok = _dev_in(tok, self.q_dtype)
+            else:  # bf16 raw rows, f32 queries: the exact widening
+                assert self.q_dtype == "f32" and c.in_dtype == "bf16", "prepare needs the token row in the query's type"
+                self.g_kvtok = gu.dev_f32(codecs.bf16_to_f64(tok))
+            self.g_q = torch.empty_like(self.g_qraw)
+        else:
+            self.g_q = _dev_in(self.q, self.q_dtype)
         self.g_topk = None
         if c.indexer:
             self.g_irope = csa.rope_table(self.rows, c.idx_rope, c.theta)
             self.g_icache = self._gpu_cache(c.idx_dim, c.idx_rope, c.idx_dtype)
             self.g_istate = self._gpu_state(c.idx_dim, 2)
-            self._gpu_compress(self.g_icache, self.g_istate, self.ikv, self.ilg, self.igamma, self.g_irope, zeros, lens)
-            self._gpu_compress(self.g_icache, self.g_istate, self.ikv, self.ilg, self.igamma, self.g_irope, lens, ends)
+            self.g_igamma = gu.dev_f32(self.igamma)
+            ipre = self._compress_args(self.ikv, self.ilg, zeros, lens)
+            self._compress_call(self.g_icache, self.g_istate, self.g_igamma, self.g_irope, ipre)
+            self.idec_args = self._compress_args(self.ikv, self.ilg, lens, ends)
             self.g_topk = torch.full((self.B, c.k), -7, dtype=torch.int32, device="cuda")
             self.g_cnt = torch.full((self.B,), -7, dtype=torch.int32, device="cuda")
             self.g_tsc = torch.full((self.B, c.k), -7.0, dtype=torch.float32, device="cuda")
-            hw = gu.dev_f32(self.head_w) if self.head_w is not None else None
-            csa.index_topk(self.g_icache, q_seq, q_pos, max_elig, _dev_in(self.q_idx, self.qi_dtype), hw, c.mode, c.k,
-                           self.g_topk, self.g_cnt, self.g_tsc)
+            self.g_hw = gu.dev_f32(self.head_w) if self.head_w is not None else None
+            self.g_qidx = _dev_in(self.q_idx, self.qi_dtype)
+            self.g_iws = csa.index_workspace(self.B, self.max_elig, c.k, c.idx_heads)
+        need = csa.attend_workspace(self.B, c.heads, c.dim, (c.k if c.indexer else self.max_elig) + c.swa_window)
+        self.g_aws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
         self.g_out = torch.full((self.B, c.heads, c.dim), -7.0, dtype=torch.float32, device="cuda")
         self.g_lse = torch.full((self.B, c.heads), -7.0, dtype=torch.float32, device="cuda")
-        csa.attend(self.g_cache, self.g_swa, c.swa_window, q_seq, q_pos, _dev_in(self.q, self.q_dtype), self.g_topk,
-                   max_elig, self.scale, True, self.g_rope, self.g_out, self.g_lse)
+        torch.cuda.synchronize()
+
+    def gpu_decode_step(self, side=None):
+        """The decode step on the current stream. With a side stream it runs the two-stream partition: on a c4a
+        layer the indexer pipeline (indexer compress, score, select) beside main compress + window insert
+        (prepare); on a c128a layer main compress beside the window insert; attention joins both."""
+        c = self.cfg
+        cur = torch.cuda.current_stream()
+
+        def main_part():
+            self._compress_call(self.g_cache, self.g_state, self.g_gamma, self.g_rope, self.dec_args)
+
+        def prep_part():
+            if c.prepare:
+                csa.prepare_qk(self.g_qraw, self.g_kvtok, self.g_qseq, self.g_qpos, self.g_qgamma, c.eps, self.g_swa,
+                               c.rope_dims, self.g_rope, self.g_q)
+
+        def index_part():
+            if c.indexer:
+                self._compress_call(self.g_icache, self.g_istate, self.g_igamma, self.g_irope, self.idec_args)
+                csa.index_topk(self.g_icache, self.g_qseq, self.g_qpos, self.max_elig, self.g_qidx, self.g_hw, c.mode,
+                               c.k, self.g_topk, self.g_cnt, self.g_tsc, workspace=self.g_iws)
+
+        if side is None:
+            main_part(); prep_part(); index_part()
+        else:
+            side.wait_stream(cur)
+            with torch.cuda.stream(side):
+                if c.indexer:
+                    index_part()
+                else:
+                    main_part()
+            if c.indexer:
+                main_part()
+            prep_part()
+            cur.wait_stream(side)
+        csa.attend(self.g_cache, self.g_swa, c.swa_window, self.g_qseq, self.g_qpos, self.g_q, self.g_topk,
+                   self.max_elig, self.scale, True, self.g_rope, self.g_out, self.g_lse, workspace=self.g_aws)
+
+    def run_gpu(self):
+        self.gpu_setup()
+        self.gpu_decode_step()
         torch.cuda.synchronize()
 
     # ------------------------------------------------------------------ oracle side
@@ -205,17 +287,27 @@ class Step:
         """The whole step on the oracle from the raw inputs: compress, index (if any), attend with inverse RoPE."""
         c = self.cfg
         self.run_oracle_compress()
-        qf = self.q_f64(self.q, self.q_dtype)
+        self.o_swa = self.oracle_swa()
+        if c.prepare:
+            from oracle import prepare as op
+            kvtok = np.stack([codecs.load_rows(self.kv[b][L], c.in_dtype) for b, L in enumerate(c.lens)])
+            self.o_q = op.prepare_qk(self.q_f64(self.q_raw, self.q_dtype), self.q_dtype, kvtok, self.q_seq, self.q_pos,
+                                     self.q_gamma, c.eps, self.o_rope, c.rope_dims, self.o_swa)
+            qf = self.q_f64(self.o_q, self.q_dtype)
+        else:
+            qf = self.q_f64(self.q, self.q_dtype)
         self.o_topk = None
         if c.indexer:
             qi = self.q_f64(self.q_idx, self.qi_dtype)
             self.o_topk, self.o_cnt, self.o_tsc = oi.index_topk(self.o_icache, self.q_seq, self.q_pos, qi, self.head_w,
                                                                c.mode, c.k)
-        self.o_out, self.o_lse = oa.attend(self.o_cache, self.oracle_swa(), c.swa_window, self.q_seq, self.q_pos, qf,
+        self.o_out, self.o_lse = oa.attend(self.o_cache, self.o_swa, c.swa_window, self.q_seq, self.q_pos, qf,
                                            self.o_topk, self.scale, True, self.o_rope)
 
     def oracle_swa(self) -> oc.Raw:
-        return oc.Raw(self.cfg.cache_dtype, self.cfg.dim, 0, self.swa_pages, None, self.swa_scales, self.bt.copy())
+        """A copy of the window pages for the oracle (its prepare step writes into it)."""
+        return oc.Raw(self.cfg.cache_dtype, self.cfg.dim, 0, self.swa_pages.copy(), None,
+                      None if self.swa_scales is None else self.swa_scales.copy(), self.bt.copy())
 
     def q_f64(self, arr, dtype):
         return codecs.load_rows(arr, "f32" if dtype == "f32" else "bf16")
@@ -241,9 +333,8 @@ class Step:
         c = self.cfg
         out = torch.full((self.B, c.heads, c.dim), -7.0, dtype=torch.float32, device="cuda")
         lse = torch.full((self.B, c.heads), -7.0, dtype=torch.float32, device="cuda")
-        csa.attend(self.g_cache, self.g_swa, c.swa_window, gu.dev_i32(self.q_seq), gu.dev_i32(self.q_pos),
-                   _dev_in(self.q, self.q_dtype), gu.dev_i32(topk), self.max_elig, self.scale, True, self.g_rope, out,
-                   lse)
+        csa.attend(self.g_cache, self.g_swa, c.swa_window, gu.dev_i32(self.q_seq), gu.dev_i32(self.q_pos), self.g_q,
+                   gu.dev_i32(topk), self.max_elig, self.scale, True, self.g_rope, out, lse)
         torch.cuda.synchronize()
         return out.cpu().numpy(), lse.cpu().numpy()
 
@@ -272,11 +363,27 @@ def verify(st: Step, out_tol: float, lse_tol: float, log=None) -> dict:
     for (gs, gc), (os_, oc_) in ((st.g_prefill, st.o_prefill), (st.g_decode, st.o_decode)):
         assert np.array_equal(gc.cpu().numpy(), oc_)
         assert np.array_equal(gs.cpu().numpy()[:, : os_.shape[1]], os_[:, : gs.shape[1]])
-    st.run_oracle_unrounded()
+    if not hasattr(st, "o_cache32"):
+        st.run_oracle_unrounded()
     gmain = (gu.host_store(st.g_cache.pages), st.g_cache.scales.cpu().numpy() if st.g_cache.scales is not None else None)
     if c.indexer:
         gidx = (gu.host_store(st.g_icache.pages),
                 st.g_icache.scales.cpu().numpy() if st.g_icache.scales is not None else None)
+    if c.prepare:  # the normed, rotated queries and the window rows the prepare step wrote
+        gq = gu.host_store(st.g_q)
+        if c.cache_dtype == "f32":
+            assert gu.rowwise_rel_err(gq, st.o_q) <= 1e-6, "prepared queries differ"
+        else:
+            gu.assert_bf16_rows(gq.reshape(-1, c.dim), st.o_q.reshape(-1, c.dim))
+        prow = np.array([paging.raw_slot(st.bt[b], int(st.q_pos[b])) for b in range(st.B)], np.int64)
+        gw = gu.host_store(st.g_swa.kv_pages)[prow]
+        ow = st.o_swa.kv_pages[prow]
+        if c.cache_dtype == "fp8":
+            gu.assert_fp8_rows(gw, st.g_swa.scales.cpu().numpy()[prow], ow, st.o_swa.scales[prow])
+        elif c.cache_dtype == "bf16":
+            gu.assert_bf16_rows(gw, ow)
+        else:
+            assert gu.rowwise_rel_err(gw, ow) <= 1e-6, "window rows differ"
     gi = st.g_topk.cpu().numpy() if c.indexer else None
     gcnt = st.g_cnt.cpu().numpy() if c.indexer else None
     g_out = st.g_out.cpu().numpy()

@@ -1,5 +1,14 @@
-"""The decode step captured in a HIP graph, with the main-cache compress_insert on a second stream beside the
-indexer pipeline (the way the benchmark runs it), replays to the eager result.
+"""The decode step captured in a HIP graph.
+
+* test_partition_graph_matches_oracle: the whole decode step of one layer, the query / window-key preparation
+  (csa_prepare_qk) included, captured with the two-stream partition of [P1] "GPU Compute Saturation" and
+  [P2] "3.2 內核": on a c4a layer the indexer pipeline (indexer compress_insert, score, select) runs on a second
+  stream beside main compress_insert + window insert; on a c128a layer main compress_insert runs beside the
+  window insert; attention joins both. Inputs come from synth; every replay (after eager work elsewhere and with
+  all outputs and written slots poisoned) is checked against the oracle run end to end with the rules of
+  tests/chain.verify.
+* test_graph_replay_matches_eager: the benchmark's capture (main compress on the side stream, bf16 or MXFP4
+  indexer cache) replays to the eager result bit for bit.
 
 Shapes are the real ones (64 heads x K=V 512 bf16, indexer 64 heads x 128 WRELU in bf16 or MXFP4, top-512 +
 window 128) at a few short contexts. Each replay runs after eager work of its own and a synchronisation; every replay's top-k lists,
@@ -14,6 +23,8 @@ import torch
 
 import long_context_compressed_compress_amd as csa
 import synth
+from oracle import index as oi, paging
+from tests.chain import Step, StepConfig, verify
 
 pytestmark = pytest.mark.gpu
 
@@ -144,3 +155,59 @@ def test_graph_replay_matches_eager(fp4_idx):
             assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
                                b.view(torch.uint8) if b.dtype == torch.bfloat16 else b), f"replay {rep}: {name} differs"
         _log(f"replay {rep}: identical to the eager step")
+
+
+PARTITION_CASES = [
+    ("c4a bf16", dict(ratio=4, lens=[3003, 4093, 811], cache_dtype="bf16", indexer=True, idx_dtype="bf16"), 2e-3),
+    ("c4a fp8", dict(ratio=4, lens=[2999, 1603], cache_dtype="fp8", indexer=True, idx_dtype="fp8"), 5e-2),
+    ("c128a bf16 dense", dict(ratio=128, lens=[4095, 3000, 511], cache_dtype="bf16", indexer=False), 2e-3),
+]
+
+
+def _poison(st: Step):
+    """Overwrite every output of the step and every slot it writes, so a replay that skips work shows."""
+    c = st.cfg
+    st.g_out.fill_(-7.0)
+    st.g_lse.fill_(-7.0)
+    st.g_q.fill_(float("nan"))
+    st.dec_args["slots"].fill_(-7)
+    st.dec_args["cnt"].fill_(-7)
+    pages = st.g_swa.kv_pages.view(torch.uint8).view(st.g_swa.kv_pages.shape[0], -1)
+    for b, L in enumerate(c.lens):
+        pages[paging.raw_slot(st.bt[b], L)].fill_(0x7F)  # NaN bf16 / fp8 bytes
+        if (L + 1 - st.window) % c.ratio == 0:          # the decode token completes entry (L + 1 - w) / ratio
+            row = paging.entry_slot(st.bt[b], (L + 1 - st.window) // c.ratio, c.ratio)
+            st.g_cache.pages.view(torch.uint8).view(st.g_cache.pages.shape[0], -1)[row].fill_(0x7F)
+            if c.indexer:
+                st.g_icache.pages.view(torch.uint8).view(st.g_icache.pages.shape[0], -1)[row].fill_(0x7F)
+    if c.indexer:
+        st.g_topk.fill_(-7)
+        st.g_cnt.fill_(-7)
+        st.idec_args["slots"].fill_(-7)
+
+
+@pytest.mark.parametrize("label,kw,tol", PARTITION_CASES, ids=[c[0] for c in PARTITION_CASES])
+def test_partition_graph_matches_oracle(label, kw, tol):
+    _log(f"partition graph: {label}")
+    base = dict(seed=90, dim=512, rope_dims=64, heads=64, in_dtype="bf16", idx_dim=128, idx_rope=64, idx_heads=64,
+                mode=oi.WRELU, k=512, prepare=True)
+    st = Step(StepConfig(**{**base, **kw}))
+    other = Step(StepConfig(**{**base, **kw, "seed": 91, "lens": [1500, 900]}))
+    st.gpu_setup()
+    other.gpu_setup()
+    st.run_oracle()
+    side = torch.cuda.Stream()
+    st.gpu_decode_step(side)  # eager warm-up of exactly the captured work
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st.gpu_decode_step(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        other.gpu_decode_step(side)   # eager work of the program between replays, on other buffers
+        _poison(st)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        res = verify(st, tol, 1e-4, log=_log)
+        _log(f"{label} replay {rep}: matches the oracle (swaps {res['swaps']}, attention err {res['attend_err']:.2e})")
