@@ -973,6 +973,451 @@ __global__ void __launch_bounds__(256) attend_valu_kernel(AttendArgs a) {
   if (tid == 0 && a.out_lse) a.out_lse[int64_t(q) * a.n_heads + h] = (l_run > 0.f) ? m_run + logf(l_run) : -INFINITY;
 }
 
+// ------------------------------------------------------------------ dense path for many queries
+// Dense attention (every eligible entry plus the window) when one launch holds many queries, as a prefill
+// chunk does: the two queries of a workgroup (consecutive queries of one sequence) share every 64-key tile,
+// so each key row fetched feeds 128 (query, head) rows. Scores are computed transposed, S^T = K Q^T, with the
+// keys of each 16-row MFMA block permuted so that a lane ends up holding one head's weights for exactly the
+// eight keys it supplies as the B operand of O^T = V^T P^T: the weights never pass through LDS and the
+// softmax needs no cross-wave reduction. Each of the 8 waves owns 16 heads of one query (Q^T fragments and
+// O^T accumulators in registers). Key rows land in LDS straight from global memory, one 1 KiB row per
+// global_load_lds_dwordx4, double-buffered: the next tile is in flight while the current one is used.
+constexpr int kDenseMinQueries = 512;  // launches with at least this many dense queries take this kernel
+constexpr int kDensePairSpan = 64;     // two queries further apart than this walk their keys separately
+constexpr float kDenseRescaleMargin = 8.0f;  // natural-log units the running maximum may lag the true one
+constexpr int kDenseQueries = 2;      // queries per workgroup (2: eight waves, two per SIMD; 1: four waves)
+
+// One 1 KiB key row from global memory into LDS: lane l moves bytes [16 l, 16 l + 16) of the row to
+// lds_byte + 16 l. Issued from inline assembly: for the compiler's own form of this copy it orders every later LDS
+// read behind the copy's completion (a vmcnt wait per read), which would serialise the next tile's copies with the
+// current tile's arithmetic. The kernel orders the copies itself: they only ever target the tile buffer no wave
+// reads, and a vmcnt(0) wait plus a barrier (both volatile) come before a buffer is read. No output register.
+__device__ __forceinline__ void dma_row(const char* src, uint32_t lds_byte) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_byte), "v"(src) : "m0");
+}
+
+// Max / sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48), on the VALU: the 32-lane swap
+// pairs rows (0, 2) and (1, 3), the 16-lane swap then pairs rows (0, 1) and (2, 3).
+__device__ __forceinline__ float rows4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// fp8 epilogue of the transposed layout: v[db][r] = output at dim db * 16 + kg * 4 + r of one head. A group of
+// GN * 16 channels is GN registers of the lane times the four lane groups of its head.
+template <int GN>
+__device__ __forceinline__ void store_fp8_t(const f32x4 (&v)[32], uint8_t* crow, float* srow, int kg) {
+#pragma unroll
+  for (int g = 0; g < 32; g += GN) {
+    float amax = 0.f;
+#pragma unroll
+    for (int n = 0; n < GN; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fabsf(v[g + n][r]));
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    const float inv = 448.0f / amax;
+#pragma unroll
+    for (int n = 0; n < GN; ++n) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w |= (amax > 0.f ? f32_to_e4m3_rne(v[g + n][r] * inv) : 0u) << (8 * r);
+      *reinterpret_cast<uint32_t*>(crow + (g + n) * 16 + kg * 4) = w;
+    }
+    if (kg == 0) srow[g / GN] = amax > 0.f ? amax / 448.0f : 1.0f;
+  }
+}
+
+template <int QPW>
+__global__ void __launch_bounds__(256 * QPW, 1) attend_dense_kernel(AttendArgs a) {
+  constexpr int NHB = 1;                  // 16-head blocks per wave
+  constexpr int NT = 256 * QPW;           // four waves (64 heads) per query
+  constexpr int WPQ = 4;                  // waves per query
+  constexpr int RPW = kTile / (4 * QPW);  // tile rows each wave moves
+  __shared__ __attribute__((aligned(16))) char kbuf[2][kTile * kRowStride];
+  __shared__ int32_t key_row[kMaxKeys];
+
+  // unit = (QPW consecutive queries, 64-head chunk); consecutive units on one XCD (workgroups are dealt to the
+  // eight XCDs in turn), so the queries of a sequence read its pages through the same L2
+  const int n_hchunk = a.n_heads / 64;
+  const int units = ((a.n_q + QPW - 1) / QPW) * n_hchunk;
+  const int per_xcd = int(gridDim.x / 8);  // the grid is a multiple of 8
+  const int unit = int(blockIdx.x % 8) * per_xcd + int(blockIdx.x / 8);
+  if (unit >= units) return;
+  const int hc = unit % n_hchunk;
+  const int q0 = QPW * (unit / n_hchunk);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform values stay in scalar registers
+  const int col = lane & 15;
+  const int kg = lane >> 4;
+  const int qi = wave / WPQ;  // query of the pair this wave serves
+  const bool has1 = QPW == 2 && q0 + 1 < a.n_q;
+  const bool wave_has_q = qi == 0 || has1;
+  const int q = wave_has_q ? q0 + qi : q0;
+  const int head = hc * 64 + (wave % WPQ) * 16 * NHB + col;  // this lane's head in block hb: head + 16 hb
+
+  // positions are 32-bit at the boundary, so every key count and position below fits an int
+  const int p_0 = a.q_pos[q0], p_1 = has1 ? a.q_pos[q0 + 1] : p_0;
+  const int seq_0 = a.q_seq[q0], seq_1 = has1 ? a.q_seq[q0 + 1] : seq_0;
+  const int ne_0 = int(attend_elig(a, q0)), ne_1 = has1 ? int(attend_elig(a, q0 + 1)) : ne_0;
+  const int lo_0 = (a.swa_window > 0) ? max(0, p_0 - a.swa_window + 1) : p_0 + 1;
+  const int lo_1 = (a.swa_window > 0) ? max(0, p_1 - a.swa_window + 1) : p_1 + 1;
+  const int64_t dp = int64_t(p_0) - p_1;
+  const bool shared = has1 && seq_0 == seq_1 && dp <= kDensePairSpan && -dp <= kDensePairSpan;
+  const int n_ps = (has1 && !shared) ? 2 : 1;
+  const int my_ne = qi ? ne_1 : ne_0, my_lo = qi ? lo_1 : lo_0, my_p = qi ? p_1 : p_0;
+
+  bf16x8 qb[NHB][16];
+  {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + (int64_t(q) * a.n_heads + head) * kD;
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks)
+        qb[hb][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + hb * 16 * kD + ks * 32 + kg * 8));
+  }
+
+  f32x4 o[32][NHB];
+#pragma unroll
+  for (int db = 0; db < 32; ++db)
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) o[db][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[NHB], l_run[NHB];
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) { m_run[hb] = -INFINITY; l_run[hb] = 0.f; }
+  const float scale = a.scale;
+  const char* pages_c = static_cast<const char*>(a.cache.pages);
+  const char* pages_w = static_cast<const char*>(a.swa.kv_pages);
+  const int per_block = kBlock / a.cache.ratio;
+  // LDS byte offset of the key this lane reads as MFMA row `col` of 16-key block kb4 in S^T: the permutation
+  // that puts the eight keys a lane supplies to PV into its own accumulator registers
+  // (blocks kb4 = 1, 2, 3 are the rows of block 0 moved by 16, 32 and 48 keys)
+  const int soff = perm_key(col >> 2, col & 3) * kRowStride + kg * 16;
+  // LDS byte offsets of the two 4-key rows a lane addresses in the transposing V^T reads of k-step c
+  const int voff0 = perm_key(kg, col >> 2) * kRowStride + 8 * (col & 3);  // + 32 rows for k-step 1
+  const int voff1 = perm_key(kg, 4 + (col >> 2)) * kRowStride + 8 * (col & 3);
+
+  for (int ps = 0; ps < n_ps; ++ps) {
+    // queries of the pair in this walk: both when they share their keys, else one walk each
+    const bool in0 = shared || ps == 0, in1 = has1 && (shared || ps == 1);
+    const bool wave_act = wave_has_q && (qi ? in1 : in0);
+    const int seq = in0 ? seq_0 : seq_1;
+    int n_cu = 0, lo_u = INT_MAX, hi_u = -1;
+    if (in0) {
+      n_cu = ne_0;
+      if (p_0 >= lo_0) { lo_u = lo_0; hi_u = p_0; }
+    }
+    if (in1) {
+      n_cu = max(n_cu, ne_1);
+      if (p_1 >= lo_1) { lo_u = min(lo_u, lo_1); hi_u = max(hi_u, p_1); }
+    }
+    if (hi_u < lo_u) { lo_u = 0; hi_u = -1; }  // no window rows (keeps the clamped table loads in range)
+    const int n_keys = n_cu + (hi_u - lo_u + 1);
+    const bool seq_c = seq >= 0 && seq < a.cache.batch;
+    const bool seq_w = seq >= 0 && seq < a.swa.batch;
+    const int32_t* bt_c = a.cache.block_table + int64_t(seq_c ? seq : 0) * a.cache.bt_stride;
+    const int32_t* bt_w = a.swa.block_table + int64_t(seq_w ? seq : 0) * a.swa.bt_stride;
+    const int bts_c = a.cache.bt_stride, bts_w = a.swa.bt_stride;
+    const int nph_c = a.cache.n_phys, nph_w = a.swa.n_phys;
+
+    for (int pass0 = 0; pass0 < n_keys; pass0 += kMaxKeys) {
+      const int n_pass = min(kMaxKeys, n_keys - pass0);
+      __syncthreads();  // the previous walk is done with the row table and both tile buffers
+      // ---- page rows of this pass's keys: key t < n_cu is entry t, else window position lo_u + t - n_cu
+      {
+        constexpr int PER = kMaxKeys / NT;
+        int32_t phys[PER];
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+          const int t = pass0 + tid + NT * j;
+          const bool is_c = t < n_cu;
+          const int e = is_c ? t : lo_u + (t - n_cu);
+          const int blk = e / (is_c ? per_block : kBlock);
+          const int bts = is_c ? bts_c : bts_w;
+          phys[j] = (is_c ? bt_c : bt_w)[blk < bts ? blk : bts - 1];  // clamped, unconditional load
+        }
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+          const int local = tid + NT * j;
+          const int t = pass0 + local;
+          const bool is_c = t < n_cu;
+          const int e = is_c ? t : lo_u + (t - n_cu);
+          const int per = is_c ? per_block : kBlock;
+          const int blk = e / per;
+          const bool ok = local < n_pass && blk < (is_c ? bts_c : bts_w) && phys[j] >= 0 &&
+                          phys[j] < (is_c ? nph_c : nph_w) && (is_c ? seq_c : seq_w);
+          key_row[local] = ok ? phys[j] * per + (e - blk * per) : -1;
+        }
+      }
+      __syncthreads();
+
+      // this wave moves tile rows RPW w .. RPW w + RPW - 1. Every row is copied unconditionally (a row that maps to
+      // no page copies page row 0, so the score loop stays one basic block); such rows are zero-filled once the copy
+      // has landed, before the barrier that publishes the tile. bad: bit j = row j of this wave maps to no page.
+      auto tile_rows = [&](int tile, int (&rows)[RPW]) -> uint32_t {
+        const int t0 = tile * kTile + wave * RPW;
+        const int my_row = (t0 + (lane % RPW) < n_pass) ? key_row[t0 + (lane % RPW)] : -1;
+        uint32_t bad = 0;
+#pragma unroll
+        for (int j = 0; j < RPW; ++j) {
+          rows[j] = __builtin_amdgcn_readlane(my_row, j);
+          bad |= uint32_t(rows[j] < 0) << j;
+        }
+        return bad;
+      };
+      auto copy_row = [&](int tile, int buf, const int (&rows)[RPW], int j) {
+        const int t = tile * kTile + wave * RPW + j;
+        const char* base = (pass0 + t < n_cu) ? pages_c : pages_w;
+        dma_row(base + int64_t(rows[j] < 0 ? 0 : rows[j]) * (2 * kD) + lane * 16,
+                uint32_t(reinterpret_cast<uintptr_t>(kbuf[buf])) + uint32_t((wave * RPW + j) * kRowStride));
+      };
+      auto zero_rows = [&](int buf, uint32_t bad) {
+        if (bad) {
+          char* dst = kbuf[buf] + wave * RPW * kRowStride;
+#pragma unroll
+          for (int j = 0; j < RPW; ++j)
+            if ((bad >> j) & 1u) *reinterpret_cast<uint4*>(dst + j * kRowStride + lane * 16) = make_uint4(0, 0, 0, 0);
+        }
+      };
+
+      const int n_tiles = (n_pass + kTile - 1) / kTile;
+      uint32_t bad_cur;
+      {
+        int rows0[RPW];
+        bad_cur = tile_rows(0, rows0);
+#pragma unroll
+        for (int j = 0; j < RPW; ++j) copy_row(0, 0, rows0, j);
+      }
+      for (int tile = 0; tile < n_tiles; ++tile) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's rows of the tile are in LDS
+        zero_rows(tile & 1, bad_cur);
+        lds_barrier();                       // every wave's rows are; every wave is done with the other buffer
+        // keys of the tile this wave's query sees: lane l tests tile key l; shifted so that the key of
+        // accumulator register r of block kb4 is bit (kb4 >> 1) * 32 + (j & 1) + 8 * (j >> 1), j = (kb4 & 1) * 4 + r
+        const int tt = tile * kTile + lane;
+        const int krow = tt < n_pass ? key_row[tt] : -1;
+        // the next tile's copies go out in four groups over the score loop below (each asm statement ends a
+        // scheduling region, so they are not spread finer); after the last
+        // tile they re-copy rows of this tile into the idle buffer, which nothing reads
+        const int ntile = tile + 1 < n_tiles ? tile + 1 : tile;
+        const int nbuf = (tile + 1) & 1;
+        int nrows[RPW];
+        bad_cur = tile_rows(ntile, nrows);
+        const char* kb = kbuf[tile & 1];
+        uint64_t kmask;
+        {
+          const int g = pass0 + tt;
+          bool ok = krow >= 0;
+          if (g < n_cu) ok = ok && g < my_ne;
+          else {
+            const int pos = lo_u + (g - n_cu);
+            ok = ok && pos >= my_lo && pos <= my_p;
+          }
+          kmask = __ballot(ok) >> (2 * kg);
+        }
+
+        // ---- S^T (64 keys x 16 NHB heads) = K Q^T
+        f32x4 s[4][NHB];
+#pragma unroll
+        for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+          for (int hb = 0; hb < NHB; ++hb) s[kb4][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // K fragments are loaded two k-steps ahead of their MFMAs (a ring of two k-steps' fragments)
+        bf16x8 kf[2][4];
+        auto load_k = [&](bf16x8 (&dst)[4], int ks) {
+#pragma unroll
+          for (int kb4 = 0; kb4 < 4; ++kb4)
+            dst[kb4] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + soff + kb4 * 16 * kRowStride + ks * 64));
+        };
+        load_k(kf[0], 0);
+        load_k(kf[1], 1);
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) {
+          if (ks % 4 == 0)
+#pragma unroll
+            for (int jj = 0; jj < RPW / 4; ++jj) copy_row(ntile, nbuf, nrows, (ks / 4) * (RPW / 4) + jj);
+#pragma unroll
+          for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+            for (int hb = 0; hb < NHB; ++hb)
+              s[kb4][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks & 1][kb4], qb[hb][ks], s[kb4][hb], 0, 0, 0);
+          if (ks + 2 < 16) load_k(kf[ks & 1], ks + 2);
+        }
+        if (!wave_act) continue;
+
+        // ---- online softmax of this lane's heads over its 16 keys of the tile (and the other lane groups'). The
+        // weights are taken against the running reference maximum m_run straight away; the tile's maximum only
+        // decides whether m_run moves, which it does when the tile exceeds it by more than kDenseRescaleMargin (or
+        // on the first keys): then the weights are recomputed and the accumulators rescaled. Weights stay below
+        // e^margin. l_part is this lane's share of the running sum; the four lane groups are added at the end.
+        bool move_any = false;
+        float mx[NHB];
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) {
+          float m = -INFINITY;
+#pragma unroll
+          for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int j = (kb4 & 1) * 4 + r;
+              const bool v = (kmask >> ((kb4 >> 1) * 32 + (j & 1) + 8 * (j >> 1))) & 1ull;
+              const float lg = v ? s[kb4][hb][r] * scale : -INFINITY;
+              s[kb4][hb][r] = lg;
+              m = fmaxf(m, lg);
+            }
+          mx[hb] = m;
+        }
+        float pw[4][NHB][4];
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+          for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pw[kb4][hb][r] = __expf(s[kb4][hb][r] - m_run[hb]);
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) {
+          mx[hb] = rows4_max(mx[hb]);
+          move_any = move_any || m_run[hb] == -INFINITY || mx[hb] > m_run[hb] + kDenseRescaleMargin;
+        }
+        if (__ballot(move_any)) {
+#pragma unroll
+          for (int hb = 0; hb < NHB; ++hb) {
+            const bool move = m_run[hb] == -INFINITY || mx[hb] > m_run[hb] + kDenseRescaleMargin;
+            const float mnew = move ? mx[hb] : m_run[hb];
+            const float corr = move ? ((m_run[hb] == -INFINITY) ? 0.f : __expf(m_run[hb] - mnew)) : 1.f;
+            m_run[hb] = mnew;
+            l_run[hb] *= corr;
+#pragma unroll
+            for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                pw[kb4][hb][r] = (s[kb4][hb][r] == -INFINITY) ? 0.f : __expf(s[kb4][hb][r] - mnew);
+#pragma unroll
+            for (int db = 0; db < 32; ++db)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) o[db][hb][r] *= corr;
+          }
+        }
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) {
+          float sum = 0.f;
+#pragma unroll
+          for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sum += pw[kb4][hb][r];
+          l_run[hb] += sum;
+        }
+
+        // ---- O^T (512 dims x 16 NHB heads) += V^T P^T, weights as bf16 hi + lo parts. The 64 (k-step, dim-block)
+        // steps read their V^T fragments kPvAhead steps ahead; the hi and lo products of two dim blocks alternate so
+        // that no MFMA waits on the one before it.
+        bf16x8 ph[2][NHB], pl[2][NHB];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int hb = 0; hb < NHB; ++hb) {
+            uint32_t wh[4], wl[4];
+#pragma unroll
+            for (int j = 0; j < 8; j += 2) {
+              const float w0 = pw[2 * c + (j >> 2)][hb][j & 3], w1 = pw[2 * c + ((j + 1) >> 2)][hb][(j + 1) & 3];
+              const uint16_t h0 = f32_to_bf16_rne(w0), h1 = f32_to_bf16_rne(w1);
+              const uint16_t l0 = f32_to_bf16_rne(w0 - bf16_to_f32(h0)), l1 = f32_to_bf16_rne(w1 - bf16_to_f32(h1));
+              wh[j >> 1] = uint32_t(h0) | (uint32_t(h1) << 16);
+              wl[j >> 1] = uint32_t(l0) | (uint32_t(l1) << 16);
+            }
+            ph[c][hb] = __builtin_bit_cast(bf16x8, make_uint4(wh[0], wh[1], wh[2], wh[3]));
+            pl[c][hb] = __builtin_bit_cast(bf16x8, make_uint4(wl[0], wl[1], wl[2], wl[3]));
+          }
+        constexpr int kPvAhead = 8;
+        bf16x8 vq[kPvAhead];
+        auto load_v = [&](int st) -> bf16x8 {
+          const int c = st >> 5, db = st & 31;
+          const uint2 e0 = lds_tr16(kb + c * 32 * kRowStride + voff0 + db * 32);
+          const uint2 e1 = lds_tr16(kb + c * 32 * kRowStride + voff1 + db * 32);
+          return __builtin_bit_cast(bf16x8, make_uint4(e0.x, e0.y, e1.x, e1.y));
+        };
+#pragma unroll
+        for (int st = 0; st < kPvAhead; ++st) vq[st] = load_v(st);
+#pragma unroll
+        for (int st = 0; st < 64; st += 2) {
+          const int c = st >> 5, db = st & 31;
+          const bf16x8 va = vq[st % kPvAhead], vb = vq[(st + 1) % kPvAhead];
+          if (st + kPvAhead < 64) vq[st % kPvAhead] = load_v(st + kPvAhead);
+          if (st + 1 + kPvAhead < 64) vq[(st + 1) % kPvAhead] = load_v(st + 1 + kPvAhead);
+#pragma unroll
+          for (int hb = 0; hb < NHB; ++hb) {
+            o[db][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, ph[c][hb], o[db][hb], 0, 0, 0);
+            o[db + 1][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, ph[c][hb], o[db + 1][hb], 0, 0, 0);
+            o[db][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl[c][hb], o[db][hb], 0, 0, 0);
+            o[db + 1][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pl[c][hb], o[db + 1][hb], 0, 0, 0);
+          }
+        }
+      }
+      // the copies are invisible to the compiler's wait tracking: wait for them here, so that no copy is in flight
+      // when the next pass reuses the buffers or the workgroup ends
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
+  }
+
+  // ---- epilogue: lane holds dims db * 16 + kg * 4 + r of head `head + 16 hb`
+  if (!wave_has_q) return;
+  const int p = my_p;
+  const int R_ = a.cache.rope_dims;
+  const int base = kD - R_;
+  const bool rot = a.fuse_inv_rope && R_ > 0 && p >= 0 && p < a.rope_rows;
+  const float* cs = rot ? a.rope_cs + int64_t(p) * R_ : a.rope_cs;
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) l_run[hb] = rows4_sum(l_run[hb]);  // the four lane groups' shares of the sum
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) {
+    const float inv_l = (l_run[hb] > 0.f) ? 1.f / l_run[hb] : 0.f;
+    f32x4 v[32];
+#pragma unroll
+    for (int db = 0; db < 32; ++db) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[db][r] = o[db][hb][r] * inv_l;
+      const int d0 = db * 16 + kg * 4;
+      if (rot && d0 + 3 >= base) {
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const int d = d0 + 2 * k2;
+          if (d >= base) {
+            const int j = (d - base) >> 1;
+            const float c = cs[2 * j], sn = cs[2 * j + 1];
+            const float x = v[db][2 * k2], y = v[db][2 * k2 + 1];
+            v[db][2 * k2] = x * c + y * sn;
+            v[db][2 * k2 + 1] = -x * sn + y * c;
+          }
+        }
+      }
+    }
+    const int64_t row = int64_t(q) * a.n_heads + head + 16 * hb;
+    if (a.out) {
+#pragma unroll
+      for (int db = 0; db < 32; ++db) *reinterpret_cast<f32x4*>(a.out + row * kD + db * 16 + kg * 4) = v[db];
+    } else {
+      uint8_t* crow = a.out_codes + row * kD;
+      float* srow_s = a.out_scales + row * (kD / a.group);
+      switch (a.group) {
+        case 16: store_fp8_t<1>(v, crow, srow_s, kg); break;
+        case 32: store_fp8_t<2>(v, crow, srow_s, kg); break;
+        case 64: store_fp8_t<4>(v, crow, srow_s, kg); break;
+        default: store_fp8_t<8>(v, crow, srow_s, kg); break;
+      }
+    }
+    if (a.out_lse && kg == 0) a.out_lse[row] = (l_run[hb] > 0.f) ? m_run[hb] + logf(l_run[hb]) : -INFINITY;
+  }
+}
 }  // namespace
 
 bool attend_supported(const csa_cache_t& c, csa_dtype_t q_dtype, int n_heads) {
@@ -990,6 +1435,11 @@ static bool use_split_path(const AttendArgs& a) {
   return a.cache.dtype != CSA_F32 && a.cache.dim == kD && a.n_heads % 64 == 0;
 }
 
+static bool use_dense_path(const AttendArgs& a) {
+  return a.topk == nullptr && a.cache.dtype == CSA_BF16 && a.cache.dim == kD && a.n_heads % 64 == 0 &&
+         a.n_q >= kDenseMinQueries;
+}
+
 static int64_t max_keys_of(const AttendArgs& a) {
   return (a.topk ? int64_t(a.k) : a.max_elig) + a.swa_window;
 }
@@ -1004,6 +1454,12 @@ size_t attend_workspace(int n_q, int n_heads, int dim, int64_t max_keys) {
 
 hipError_t launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (a.n_q == 0) return hipSuccess;
+  if (use_dense_path(a)) {
+    const int64_t units = int64_t((a.n_q + kDenseQueries - 1) / kDenseQueries) * (a.n_heads / 64);
+    hipLaunchKernelGGL((attend_dense_kernel<kDenseQueries>), dim3(unsigned((units + 7) / 8 * 8)),
+                       dim3(256 * kDenseQueries), 0, stream, a);
+    return hipGetLastError();
+  }
   if (use_split_path(a)) {
     const int n_hchunk = a.n_heads / 64;
     SplitPlan sp = split_plan(a.n_q, n_hchunk, max_keys_of(a));

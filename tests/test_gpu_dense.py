@@ -1,0 +1,188 @@
+"""GPU parity of dense attention launched with many queries (the prefill form of c128a attention).
+
+Dense c128a layers attend to every eligible compressed entry plus the raw window ([P2] "二、注意力機制為什么這么麻煩",
+[P3] "注意力计算剪枝"); a prefill chunk hands the attention thousands of queries at once ([P1] "GPU Compute
+Saturation": prefill with bf16 caches). From 512 dense queries per launch the library groups consecutive queries into
+workgroups that read each key tile once for all of them, so these cases put queries of one sequence next to each
+other (shared key walks), queries of different sequences or far-apart positions next to each other (separate walks),
+queries without eligible entries or without any key, sequence ids outside the tables and unmapped cache blocks.
+Every query is compared with the oracle (or a seeded sample of them where the oracle is slow), fp32 output within
+2e-3 of the row maximum, log-sum-exp within 1e-4; the fp8 output form is compared as in the attention parity tests.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_compressed_compress_amd as csa
+import synth
+from oracle import attend as oa, codecs, compress as oc, paging, rope as orope
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+D, R = 512, 64
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _queries(spec):
+    """spec: list of (sequence, positions) -> (q_seq, q_pos)."""
+    seqs, pos = [], []
+    for s, ps in spec:
+        seqs += [s] * len(ps)
+        pos += list(ps)
+    return np.array(seqs, np.int32), np.array(pos, np.int32)
+
+
+class DenseSetup:
+    """c128a bf16 cache of B sequences (entries beyond every query's eligibility hold NaN) and a window pool."""
+
+    def __init__(self, cfg, q_seq, q_pos, n_seq, heads, unmapped=()):
+        self.q_seq, self.q_pos, self.heads = q_seq, q_pos, heads
+        self.n_q = len(q_pos)
+        valid = (q_seq >= 0) & (q_seq < n_seq)
+        p_max = [int(q_pos[(q_seq == b)].max()) if np.any(q_seq == b) else 0 for b in range(n_seq)]
+        nb = max(p_max) // 256 + 1
+        n_phys = n_seq * nb + 3
+        self.bt = synth.random_block_table(synth.rng(cfg, synth.STREAM_BT), n_seq, nb, n_phys)
+        g = synth.rng(cfg, synth.STREAM_KV)
+        self.pages = synth.normal_bf16_bits(g, (n_phys * 2, D))
+        for b in range(n_seq):
+            n_ok = paging.num_eligible(p_max[b], 128, 128)
+            bad = [paging.entry_slot(self.bt[b], i, 128) for i in range(n_ok, nb * 2)]
+            self.pages[bad] = 0x7FC0
+        # cache blocks the GPU table leaves unmapped: (sequence, logical block)
+        self.gpu_bt = self.bt.copy()
+        for b, blk in unmapped:
+            self.gpu_bt[b, blk] = -1
+        self.unmapped = set(unmapped)
+        self.wpages = synth.normal_bf16_bits(synth.rng(cfg, synth.STREAM_SWA), (n_phys * 256, D))
+        self.q = synth.normal_bf16_bits(synth.rng(cfg, synth.STREAM_Q), (self.n_q, heads, D))
+        self.valid = valid
+        self.scale = 1.0 / math.sqrt(D)
+        self.rows = int(max(1, q_pos.max() + 1))
+        self.max_elig = max(paging.num_eligible(int(p), 128, 128) for p in q_pos)
+
+    def gpu(self, window, fuse=True, out=None, lse=None, quant_group=0):
+        cache = csa.Cache(128, 128, D, R, gu.dev_store(self.pages, "bf16"), gu.dev_i32(self.gpu_bt), None)
+        swa = csa.Raw(D, 0, gu.dev_store(self.wpages, "bf16"), gu.dev_i32(self.bt), None, None)
+        qs, qp, qd = gu.dev_i32(self.q_seq), gu.dev_i32(self.q_pos), gu.dev_bf16(self.q)
+        grope = csa.rope_table(self.rows, R)
+        need = csa.attend_workspace(self.n_q, self.heads, D, self.max_elig + window)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        if quant_group:
+            codes = torch.full((self.n_q, self.heads, D), 0xA5, dtype=torch.uint8, device="cuda")
+            scales = torch.full((self.n_q, self.heads, D // quant_group), -7.0, device="cuda")
+            lse = torch.full((self.n_q, self.heads), -7.0, device="cuda")
+            csa.attend_quant_fp8(cache, swa, window, qs, qp, qd, None, self.max_elig, self.scale, grope, quant_group,
+                                 codes, scales, lse, workspace=ws)
+            torch.cuda.synchronize()
+            return codes.cpu().numpy(), scales.cpu().numpy(), lse.cpu().numpy()
+        out = torch.full((self.n_q, self.heads, D), -7.0, device="cuda")
+        lse = torch.full((self.n_q, self.heads), -7.0, device="cuda")
+        csa.attend(cache, swa, window, qs, qp, qd, None, self.max_elig, self.scale, fuse, grope, out, lse,
+                   workspace=ws)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), lse.cpu().numpy()
+
+    def oracle(self, window, idx, fuse=True):
+        """Oracle output of queries idx; entries in unmapped blocks are left out through an explicit entry list."""
+        idx = np.asarray(idx)
+        tk = None
+        if self.unmapped:
+            k = max(1, self.max_elig)
+            tk = np.full((len(idx), k), -1, np.int32)
+            for r, qi in enumerate(idx):
+                n = paging.num_eligible(int(self.q_pos[qi]), 128, 128)
+                ent = [e for e in range(n) if (int(self.q_seq[qi]), e // 2) not in self.unmapped]
+                tk[r, :len(ent)] = ent
+        cache = oc.Cache(128, 128, D, R, "bf16", self.pages, None, self.bt)
+        swa = oc.Raw("bf16", D, 0, self.wpages, None, None, self.bt)
+        return oa.attend(cache, swa, window, self.q_seq[idx], self.q_pos[idx], codecs.load_rows(self.q[idx], "bf16"),
+                         tk, self.scale, fuse, orope.rope_table(self.rows, R))
+
+
+# (label, heads, swa window, spec, n_seq, unmapped blocks, oracle sample size or None for every query)
+CASES = [
+    ("pairs inside, across and far apart", 64, 128,
+     [(0, range(5000, 5301)), (1, range(12001, 12251)), (2, [100, 40000, 130, 20000, 7, 128, 255]),
+      (0, [6000, 6001]), (3, [9000, 9001]), (1, [12400]), (-1, [300])], 3, (), None),
+    ("no window: queries without keys", 64, 0,
+     [(0, range(3000, 3300)), (1, [5, 60, 126, 127, 128, 255, 256]), (1, range(700, 910))], 2, (), None),
+    ("1024-row window, 128 heads, unmapped blocks", 128, 1024,
+     [(0, range(9000, 9256)), (1, range(2000, 2257))], 2, ((0, 3), (0, 20), (1, 1)), 40),
+]
+
+
+@pytest.mark.parametrize("label,heads,window,spec,n_seq,unmapped,sample", CASES)
+def test_dense_many_queries(label, heads, window, spec, n_seq, unmapped, sample):
+    cfg = 500 + heads + window + len(spec)
+    q_seq, q_pos = _queries(spec)
+    st = DenseSetup(cfg, q_seq, q_pos, n_seq, heads, unmapped)
+    _log(f"dense many queries: {label}: n_q={st.n_q} heads={heads} window={window} max_elig={st.max_elig}")
+    assert st.n_q >= 512
+    g_out, g_lse = st.gpu(window)
+    g_raw, _ = st.gpu(window, fuse=False)
+    ok = st.valid
+    # queries whose sequence id is outside the tables see no key
+    assert np.all(g_out[~ok] == 0.0) and np.all(g_lse[~ok] == -np.inf)
+    assert np.all(np.isfinite(g_out))
+    idx = np.nonzero(ok)[0]
+    if sample is not None:
+        gs = synth.rng(cfg, 31)
+        idx = np.array(sorted(set([idx[0], idx[-1]] + list(gs.choice(idx, size=sample, replace=False)))))
+    o_out, o_lse = st.oracle(window, idx)
+    o_raw, _ = st.oracle(window, idx, fuse=False)
+    err = gu.rowwise_rel_err(g_out[idx], o_out)
+    err_raw = gu.rowwise_rel_err(g_raw[idx], o_raw)
+    _log(f"{label}: rowwise rel err fused {err:.3e} unfused {err_raw:.3e} over {len(idx)} queries")
+    assert err <= TOL and err_raw <= TOL
+    empty = np.isneginf(o_lse)
+    assert np.array_equal(np.isneginf(g_lse[idx]), empty)
+    assert np.allclose(g_lse[idx][~empty], o_lse[~empty], rtol=0, atol=1e-4)
+    assert np.all(g_out[idx][empty.any(axis=1)] == 0.0)
+
+
+@pytest.mark.parametrize("group", [128, 16])
+def test_dense_many_queries_fp8_output(group):
+    """Attention with the inverse RoPE + grouped fp8 epilogue (R23) on the dense many-query path: the oracle's
+    attention followed by its quantisation rule, with the bar of the other fused-epilogue tests (one e4m3 step of the
+    oracle's code times its scale plus twice the attention tolerance of the row)."""
+    from oracle import output_quant as oq
+    cfg = 640 + group
+    q_seq, q_pos = _queries([(0, range(4000, 4300)), (1, range(8000, 8250))])
+    st = DenseSetup(cfg, q_seq, q_pos, 2, 64)
+    _log(f"dense fp8 output: n_q={st.n_q} group={group}")
+    gc, gsc, g_lse = st.gpu(128, quant_group=group)
+    gs_ = synth.rng(cfg, 31)
+    idx = np.array(sorted(set([0, st.n_q - 1] + list(gs_.choice(st.n_q, size=48, replace=False)))))
+    o_raw, o_lse = st.oracle(128, idx, fuse=False)
+    table = orope.rope_table(st.rows, R)
+    ref_codes, ref_scales = oq.inv_rope_quant(o_raw, q_pos[idx], table, R, group)
+    y_ref = orope.inv_rope_queries(o_raw, q_pos[idx], table, R)
+    yerr = TOL * np.abs(y_ref).max(axis=-1, keepdims=True)
+    rs = ref_scales.astype(np.float64)
+    gsel, csel = gsc[idx], gc[idx]
+    assert np.all(np.abs(gsel - rs) <= yerr / 448.0 + 2.0 ** -22 * rs)
+    gv = oq.dequant(csel, gsel, group)
+    rv = oq.dequant(ref_codes, ref_scales, group)
+    mag = np.maximum(np.abs(codecs.e4m3_to_f64(ref_codes)), 2.0 ** -6)
+    step = np.ldexp(1.0, np.floor(np.log2(mag)).astype(int) - 3) * np.repeat(rs, group, axis=-1)
+    assert np.all(np.abs(gv - rv) <= 1.01 * step + 2.0 * yerr)
+    _log(f"identical codes vs oracle: {np.mean(csel == ref_codes):.5f}")
+    assert np.allclose(g_lse[idx], o_lse, rtol=0, atol=1e-4)
+
+
+def test_dense_many_queries_deterministic():
+    """No atomics on this path: two launches give identical bits."""
+    q_seq, q_pos = _queries([(0, range(3000, 3600))])
+    st = DenseSetup(700, q_seq, q_pos, 1, 64)
+    a_out, a_lse = st.gpu(128)
+    b_out, b_lse = st.gpu(128)
+    assert np.array_equal(a_out.view(np.uint32), b_out.view(np.uint32))
+    assert np.array_equal(a_lse.view(np.uint32), b_lse.view(np.uint32))
