@@ -166,6 +166,15 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8_hw(uint2 v) {
   return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
 }
 
+// Sum over the four 16-lane rows of a wave, on the VALU: rows (0, 1) and (2, 3) first (16-lane swap), then the two
+// pair sums (32-lane swap); every lane ends with (x0 + x1) + (x2 + x3).
+__device__ __forceinline__ float rows4_sum_pairs(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 template <int KF, int HT>
 __device__ __forceinline__ uint32_t score_page(const PageBuf<KF>& b, const bf16x8 (&qa)[HT][4],
                                                const float (&wv)[HT][4], int kg) {
@@ -194,8 +203,7 @@ __device__ __forceinline__ uint32_t score_page(const PageBuf<KF>& b, const bf16x
 #pragma unroll
       for (int i = 0; i < 4; ++i) part += wv[ht][i] * fmaxf(acc[i], 0.f);
     }
-    part += __shfl_xor(part, 16);
-    part += __shfl_xor(part, 32);
+    part = rows4_sum_pairs(part);
     if constexpr (KF == 1) part *= b.sc[u];
     if (kg == u) mine_f = part;
   }
@@ -280,47 +288,47 @@ __global__ void __launch_bounds__(256, 2) score_mfma_kernel(IndexArgs a, Workspa
 }
 
 // ------------------------------------------------------------------ MFMA score, pages shared by queries (prefill)
-// A prefill chunk has thousands of queries per sequence that all read the same pages, so a workgroup of
-// kShareQ waves takes kShareQ consecutive queries (one per wave) and stages every page of its run once
-// through LDS for all of them; kShareAhead pages stay in flight in registers while one is scored. Each wave
-// scores the page for its own query with score_page (the same arithmetic as score_mfma_kernel, so the
-// scores are identical). Queries of a workgroup that belong to different sequences are processed in
-// successive rounds, one sequence per round.
+// A prefill chunk has thousands of queries per sequence that all read the same pages, so a workgroup of kShareQ
+// waves takes kShareQ consecutive queries (one per wave) and brings every page of its run into LDS once for all of
+// them. Pages are copied global -> LDS by global_load_lds (no register staging) into a ring of kShareBufs buffers,
+// kShareDepth pages ahead of the one being scored. In LDS, the 16-byte chunk c of page row r sits at chunk
+// c ^ (r & (chunks per row - 1)) of its row (the copy picks its source chunks accordingly), so the operand reads of
+// 16 rows at one column fall in different banks. Each wave scores the page for its own query with score_page (the
+// same arithmetic as the decode kernels, so the scores are identical). Queries of a workgroup that belong to
+// different sequences are processed in successive rounds, one sequence per round.
 constexpr int kShareQ = 8;
 constexpr int kShareThreads = 64 * kShareQ;
-constexpr int kShareAhead = 4;
+constexpr int kShareDepth = 3;
+constexpr int kShareBufs = kShareDepth + 1;
 
-// Page geometry per key format (KF as for PageBuf): a page is 64 rows of RAW_ROW bytes in HBM, copied in
-// CHUNKS 16-byte chunks (1024 bf16, 512 fp8, 256 fp4: threads >= CHUNKS copy none of an fp4 page).
+// Page geometry per key format (KF as for PageBuf): 64 rows of ROW bytes; a page is DMAS copies of 1 KiB, plus for
+// fp8 / fp4 one 256-byte copy of its 64 scale words (fp8: the entry's fp32 scale; fp4: its four E8M0 bytes).
 template <int KF>
 struct SharedPage {
-  static constexpr int RAW_ROW = KF == 1 ? 128 : (KF == 2 ? 64 : 256);  // bytes per page row in HBM
-  static constexpr int ROW = RAW_ROW + 16;           // LDS bytes per page row (padded: rows start 4 banks apart)
-  static constexpr int CHUNKS = 64 * RAW_ROW / 16;   // 16-byte chunks of one page in HBM
-  static constexpr int PER_T = CHUNKS > kShareThreads ? CHUNKS / kShareThreads : 1;  // chunks each thread copies
+  static constexpr int ROW = KF == 1 ? 128 : (KF == 2 ? 64 : 256);
+  static constexpr int BYTES = 64 * ROW;
+  static constexpr int CPR = ROW / 16;  // 16-byte chunks per row
+  static constexpr int DMAS = BYTES / 1024;
+  // copies of one page a wave issues: [wave] -> count, for a constant per-wave vmcnt wait
+  __host__ __device__ static constexpr int per_wave(int w) {
+    return KF == 0 ? 2 : (KF == 1 ? (w == 0 ? 2 : 1) : (w < 4 ? 1 : (w == 4 ? 1 : 0)));
+  }
 };
 
-// Page i of the run (clamped to the last one) -> this thread's 16-byte chunks and, for fp8 / fp4, scale word `tid`
-// of the page (fp8: the entry's fp32 scale bits; fp4: the entry's four E8M0 bytes). A forced-inline function, so
-// the caller's register arrays are never address-taken (a lambda called this way was left out of line and its
-// arrays went to scratch memory).
+// LDS byte offset of bytes [16 c + o, ...) of page row r, 0 <= o < 16.
 template <int KF>
-__device__ __forceinline__ void fetch_shared_page(const IndexArgs& a, const int32_t* pg_phys, int i, int n_pg, int tid,
-                                                  uint4& c0, uint4& c1, uint32_t& sc) {
+__device__ __forceinline__ int swz(int r, int c, int o) {
   using L = SharedPage<KF>;
-  static_assert(L::PER_T == 1 || L::PER_T == 2, "one or two chunks per thread");
-  const int ii = i < n_pg ? i : n_pg - 1;
-  const int32_t phys = pg_phys[ii];
-  const int64_t page = phys >= 0 ? phys : 0;
-  const char* src = static_cast<const char*>(a.cache.pages) + page * 64 * L::RAW_ROW;
-  if constexpr (KF == 2) {
-    // threads >= CHUNKS load a copy of a chunk of the page and never store it
-    c0 = *reinterpret_cast<const uint4*>(src + (tid % L::CHUNKS) * 16);
-  } else {
-    c0 = *reinterpret_cast<const uint4*>(src + tid * 16);
-  }
-  if (L::PER_T == 2) c1 = *reinterpret_cast<const uint4*>(src + (tid + kShareThreads) * 16);
-  if (KF != 0) sc = tid < 64 ? reinterpret_cast<const uint32_t*>(a.cache.scales)[page * 64 + tid] : 0u;
+  return r * L::ROW + ((c ^ (r & (L::CPR - 1))) << 4) + o;
+}
+
+// 64 x 4 bytes from global memory into LDS: lane l moves bytes [4 l, 4 l + 4) to lds_byte + 4 l. Like dma_row,
+// issued from inline assembly with no output register; the kernel orders it with vmcnt waits and barriers.
+__device__ __forceinline__ void dma_words(const void* src, uint32_t lds_byte) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_byte), "v"(src) : "m0");
+}
+__device__ __forceinline__ void dma_chunks(const void* src, uint32_t lds_byte) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_byte), "v"(src) : "m0");
 }
 
 template <int KF, int HT>
@@ -331,8 +339,8 @@ __global__ void __launch_bounds__(kShareThreads, 1) score_shared_kernel(IndexArg
   // per-query histograms with two 16-bit bins per word (a workgroup counts at most kPagesPerBlock * 64 keys
   // per query)
   __shared__ uint32_t hist_s[kShareQ][kHistBins / 2];
-  __shared__ __attribute__((aligned(16))) char page_s[2][E * L::ROW];
-  __shared__ uint32_t scale_s[2][E];
+  __shared__ __attribute__((aligned(16))) char page_s[kShareBufs][L::BYTES];
+  __shared__ __attribute__((aligned(16))) uint32_t scale_s[kShareBufs][E];
   __shared__ int32_t pg_phys[kPagesPerBlock];
   __shared__ int32_t w_seq[kShareQ];
   __shared__ int32_t w_npages[kShareQ];
@@ -340,7 +348,7 @@ __global__ void __launch_bounds__(kShareThreads, 1) score_shared_kernel(IndexArg
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15;
   const int kg = lane >> 4;
   const int H = HT * 16;
@@ -380,6 +388,9 @@ __global__ void __launch_bounds__(kShareThreads, 1) score_shared_kernel(IndexArg
       for (int i = 0; i < 4; ++i) wv[ht][i] = a.head_w[int64_t(qq) * H + ht * 16 + kg * 4 + i];
   }
   uint32_t* keys_q = ws.keys + int64_t(q_ok ? q : 0) * a.max_elig;
+  const char* pages = static_cast<const char*>(a.cache.pages);
+  const uint32_t* scales = reinterpret_cast<const uint32_t*>(a.cache.scales);
+  const int n_dw = L::per_wave(wave);  // this wave's copies per page
   __syncthreads();
 
   bool done = w_seq[wave] < 0;  // per wave; the round bookkeeping below is uniform over the workgroup
@@ -405,58 +416,77 @@ __global__ void __launch_bounds__(kShareThreads, 1) score_shared_kernel(IndexArg
       pg_phys[tid] = (phys >= 0 && phys < a.cache.n_phys) ? phys : -1;
     }
     __syncthreads();
-    // page i of the run -> registers: each thread copies PER_T 16-byte chunks (and fp8 / fp4 threads < 64 one
-    // scale word)
-    uint4 pre0[kShareAhead], pre1[kShareAhead];  // this thread's first and second chunk of each page in flight
-    uint32_t pre_sc[kShareAhead] = {};
+    // this wave's share of the copies of page i of the run (i past the run re-copies the last page into a buffer
+    // nobody reads, so every wave always has the same number of copies in flight)
+    auto issue = [&](int i) {
+      const int ii = i < n_pg ? i : n_pg - 1;
+      const int32_t phys = pg_phys[ii];
+      const int64_t page = phys >= 0 ? phys : 0;
+      const int buf = i % kShareBufs;
+      const char* src = pages + page * L::BYTES;
+      const uint32_t dst = uint32_t(reinterpret_cast<uintptr_t>(page_s[buf]));
+      // page copy j covers LDS bytes [1024 j, 1024 j + 1024): lane l writes chunk l % CPR of row
+      // (1024 j) / ROW + l / CPR, which holds source chunk (l % CPR) ^ (row & (CPR - 1))
+      auto page_copy = [&](int j) {
+        const int r = (1024 / L::ROW) * j + lane / L::CPR;
+        const int c = (lane % L::CPR) ^ (r & (L::CPR - 1));
+        dma_chunks(src + r * L::ROW + c * 16, dst + 1024 * j);
+      };
+      if constexpr (KF == 0) {
+        page_copy(2 * wave);
+        page_copy(2 * wave + 1);
+      } else if constexpr (KF == 1) {
+        page_copy(wave);
+        if (wave == 0) dma_words(scales + page * E + lane, uint32_t(reinterpret_cast<uintptr_t>(scale_s[buf])));
+      } else {
+        if (wave < 4) page_copy(wave);
+        else if (wave == 4) dma_words(scales + page * E + lane, uint32_t(reinterpret_cast<uintptr_t>(scale_s[buf])));
+      }
+    };
 #pragma unroll
-    for (int s = 0; s < kShareAhead; ++s) fetch_shared_page<KF>(a, pg_phys, s, n_pg, tid, pre0[s], pre1[s], pre_sc[s]);
-    for (int i0 = 0; i0 < n_pg; i0 += kShareAhead) {
+    for (int s = 0; s < kShareDepth; ++s) issue(s);
+    for (int i = 0; i < n_pg; ++i) {
+      // this wave's copies of page i have landed once at most n_dw * (kShareDepth - 1) copies are in flight
+      if (n_dw == 2) __builtin_amdgcn_s_waitcnt(0x0F74);       // vmcnt(4)
+      else if (n_dw == 1) __builtin_amdgcn_s_waitcnt(0x0F72);  // vmcnt(2)
+      else __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0)
+      lds_barrier();  // every wave's copies of page i landed; every wave is done with page i - 1's buffer
+      issue(i + kShareDepth);  // into the buffer of page i - 1
+      const int64_t pg = pg_begin + i;
+      if (active && pg < w_npages[wave]) {
+        const char* buf = page_s[i % kShareBufs];
+        const uint32_t* sc = scale_s[i % kShareBufs];
+        PageBuf<KF> b;
 #pragma unroll
-      for (int s = 0; s < kShareAhead; ++s) {
-        const int i = i0 + s;
-        if (i < n_pg) {  // uniform
-          char* buf = page_s[i & 1];
+        for (int u = 0; u < 4; ++u) {
+          const int r = u * 16 + col;
+          if constexpr (KF == 2) {
+            b.v[u] = *reinterpret_cast<const uint4*>(buf + swz<KF>(r, kg, 0));
+            b.sc[u] = e8m0_to_f32((sc[r] >> (8 * kg)) & 0xFFu);
+          } else {
 #pragma unroll
-          for (int c = 0; c < L::PER_T; ++c) {
-            const int chunk = tid + kShareThreads * c;
-            const int row = chunk / (L::RAW_ROW / 16), off = (chunk % (L::RAW_ROW / 16)) * 16;
-            if (L::CHUNKS >= kShareThreads || chunk < L::CHUNKS)
-              *reinterpret_cast<uint4*>(buf + row * L::ROW + off) = c == 0 ? pre0[s] : pre1[s];
-          }
-          if (KF != 0 && tid < E) scale_s[i & 1][tid] = pre_sc[s];
-          fetch_shared_page<KF>(a, pg_phys, i + kShareAhead, n_pg, tid, pre0[s], pre1[s], pre_sc[s]);
-          lds_barrier();
-          const int64_t pg = pg_begin + i;
-          if (active && pg < w_npages[wave]) {
-            PageBuf<KF> b;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const char* rowp = buf + (u * 16 + col) * L::ROW;
-              if constexpr (KF == 2) {
-                b.v[u] = *reinterpret_cast<const uint4*>(rowp + kg * 16);
-                b.sc[u] = e8m0_to_f32((scale_s[i & 1][u * 16 + col] >> (8 * kg)) & 0xFFu);
-              } else {
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                  if constexpr (KF == 1) b.v[u][ks] = *reinterpret_cast<const uint2*>(rowp + ks * 32 + kg * 8);
-                  else b.v[u][ks] = *reinterpret_cast<const uint4*>(rowp + ks * 64 + kg * 16);
-                }
-                if constexpr (KF == 1) b.sc[u] = __uint_as_float(scale_s[i & 1][u * 16 + col]);
-              }
+            for (int ks = 0; ks < 4; ++ks) {
+              if constexpr (KF == 1)
+                b.v[u][ks] = *reinterpret_cast<const uint2*>(buf + swz<KF>(r, ks * 2 + (kg >> 1), (kg & 1) * 8));
+              else
+                b.v[u][ks] = *reinterpret_cast<const uint4*>(buf + swz<KF>(r, ks * 4 + kg, 0));
             }
-            const uint32_t key = score_page<KF, HT>(b, qa, wv, kg);
-            const int64_t e = pg * E + lane;
-            if (e < n_elig) {
-              const uint32_t k2 = pg_phys[i] >= 0 ? key : 0u;
-              keys_q[e] = k2;
-              const uint32_t bin = k2 >> (32 - kHistBits);
-              atomicAdd(&hist_s[wave][bin >> 1], 1u << ((bin & 1u) * 16));
-            }
+            if constexpr (KF == 1) b.sc[u] = __uint_as_float(sc[r]);
           }
+        }
+        const uint32_t key = score_page<KF, HT>(b, qa, wv, kg);
+        const int64_t e = pg * E + lane;
+        if (e < n_elig) {
+          const uint32_t k2 = pg_phys[i] >= 0 ? key : 0u;
+          keys_q[e] = k2;
+          const uint32_t bin = k2 >> (32 - kHistBits);
+          atomicAdd(&hist_s[wave][bin >> 1], 1u << ((bin & 1u) * 16));
         }
       }
     }
+    // the copies are invisible to the compiler's wait tracking: none may be in flight when the next round
+    // rewrites the buffers or the workgroup ends
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     if (active) done = true;
     __syncthreads();
     if (lane == 0 && active) w_seq[wave] = -1;
@@ -540,8 +570,7 @@ __device__ __forceinline__ uint32_t lt_score_page(const char* st, const uint32_t
 #pragma unroll
       for (int i = 0; i < 4; ++i) part += wv[ht][i] * fmaxf(acc[i], 0.f);
     }
-    part += __shfl_xor(part, 16);
-    part += __shfl_xor(part, 32);
+    part = rows4_sum_pairs(part);
     if constexpr (KF == 1) part *= sc;
     if (kg == u) mine_f = part;
   }
