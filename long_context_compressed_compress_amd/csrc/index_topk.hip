@@ -291,15 +291,14 @@ __global__ void __launch_bounds__(256, 2) score_mfma_kernel(IndexArgs a, Workspa
 // A prefill chunk has thousands of queries per sequence that all read the same pages, so a workgroup of kShareQ
 // waves takes kShareQ consecutive queries (one per wave) and brings every page of its run into LDS once for all of
 // them. Pages are copied global -> LDS by global_load_lds (no register staging) into a ring of kShareBufs buffers,
-// kShareDepth pages ahead of the one being scored. In LDS, the 16-byte chunk c of page row r sits at chunk
+// and scored two per workgroup barrier while the next two are in flight. In LDS, the 16-byte chunk c of page row r sits at chunk
 // c ^ (r & (chunks per row - 1)) of its row (the copy picks its source chunks accordingly), so the operand reads of
 // 16 rows at one column fall in different banks. Each wave scores the page for its own query with score_page (the
 // same arithmetic as the decode kernels, so the scores are identical). Queries of a workgroup that belong to
 // different sequences are processed in successive rounds, one sequence per round.
 constexpr int kShareQ = 8;
 constexpr int kShareThreads = 64 * kShareQ;
-constexpr int kShareDepth = 3;
-constexpr int kShareBufs = kShareDepth + 1;
+constexpr int kShareBufs = 4;  // two pages being scored, two in flight
 
 // Page geometry per key format (KF as for PageBuf): 64 rows of ROW bytes; a page is DMAS copies of 1 KiB, plus for
 // fp8 / fp4 one 256-byte copy of its 64 scale words (fp8: the entry's fp32 scale; fp4: its four E8M0 bytes).
@@ -309,10 +308,6 @@ struct SharedPage {
   static constexpr int BYTES = 64 * ROW;
   static constexpr int CPR = ROW / 16;  // 16-byte chunks per row
   static constexpr int DMAS = BYTES / 1024;
-  // copies of one page a wave issues: [wave] -> count, for a constant per-wave vmcnt wait
-  __host__ __device__ static constexpr int per_wave(int w) {
-    return KF == 0 ? 2 : (KF == 1 ? (w == 0 ? 2 : 1) : (w < 4 ? 1 : (w == 4 ? 1 : 0)));
-  }
 };
 
 // LDS byte offset of bytes [16 c + o, ...) of page row r, 0 <= o < 16.
@@ -390,7 +385,6 @@ __global__ void __launch_bounds__(kShareThreads, 1) score_shared_kernel(IndexArg
   uint32_t* keys_q = ws.keys + int64_t(q_ok ? q : 0) * a.max_elig;
   const char* pages = static_cast<const char*>(a.cache.pages);
   const uint32_t* scales = reinterpret_cast<const uint32_t*>(a.cache.scales);
-  const int n_dw = L::per_wave(wave);  // this wave's copies per page
   __syncthreads();
 
   bool done = w_seq[wave] < 0;  // per wave; the round bookkeeping below is uniform over the workgroup
@@ -417,7 +411,7 @@ __global__ void __launch_bounds__(kShareThreads, 1) score_shared_kernel(IndexArg
     }
     __syncthreads();
     // this wave's share of the copies of page i of the run (i past the run re-copies the last page into a buffer
-    // nobody reads, so every wave always has the same number of copies in flight)
+    // nobody reads)
     auto issue = [&](int i) {
       const int ii = i < n_pg ? i : n_pg - 1;
       const int32_t phys = pg_phys[ii];
@@ -443,44 +437,52 @@ __global__ void __launch_bounds__(kShareThreads, 1) score_shared_kernel(IndexArg
         else if (wave == 4) dma_words(scales + page * E + lane, uint32_t(reinterpret_cast<uintptr_t>(scale_s[buf])));
       }
     };
+    // pages are scored two per barrier: pages 2k and 2k + 1 are read while pages 2k + 2 and 2k + 3 are in flight
 #pragma unroll
-    for (int s = 0; s < kShareDepth; ++s) issue(s);
-    for (int i = 0; i < n_pg; ++i) {
-      // this wave's copies of page i have landed once at most n_dw * (kShareDepth - 1) copies are in flight
-      if (n_dw == 2) __builtin_amdgcn_s_waitcnt(0x0F74);       // vmcnt(4)
-      else if (n_dw == 1) __builtin_amdgcn_s_waitcnt(0x0F72);  // vmcnt(2)
-      else __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0)
-      lds_barrier();  // every wave's copies of page i landed; every wave is done with page i - 1's buffer
-      issue(i + kShareDepth);  // into the buffer of page i - 1
-      const int64_t pg = pg_begin + i;
-      if (active && pg < w_npages[wave]) {
-        const char* buf = page_s[i % kShareBufs];
-        const uint32_t* sc = scale_s[i % kShareBufs];
-        PageBuf<KF> b;
+    for (int s = 0; s < 2; ++s) issue(s);
+    for (int i0 = 0; i0 < n_pg; i0 += 2) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of pages i0, i0 + 1 have landed
+      lds_barrier();  // every wave's copies landed; every wave is done with pages i0 - 2 and i0 - 1
+      issue(i0 + 2);  // into the buffers of pages i0 - 2 and i0 - 1
+      issue(i0 + 3);
+      if (active) {  // both pages in one basic block (a page past the run scores a re-copied page, not stored)
+        PageBuf<KF> b[2];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int r = u * 16 + col;
-          if constexpr (KF == 2) {
-            b.v[u] = *reinterpret_cast<const uint4*>(buf + swz<KF>(r, kg, 0));
-            b.sc[u] = e8m0_to_f32((sc[r] >> (8 * kg)) & 0xFFu);
-          } else {
+        for (int h = 0; h < 2; ++h) {
+          const char* buf = page_s[(i0 + h) % kShareBufs];
+          const uint32_t* sc = scale_s[(i0 + h) % kShareBufs];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-              if constexpr (KF == 1)
-                b.v[u][ks] = *reinterpret_cast<const uint2*>(buf + swz<KF>(r, ks * 2 + (kg >> 1), (kg & 1) * 8));
-              else
-                b.v[u][ks] = *reinterpret_cast<const uint4*>(buf + swz<KF>(r, ks * 4 + kg, 0));
+          for (int u = 0; u < 4; ++u) {
+            const int r = u * 16 + col;
+            if constexpr (KF == 2) {
+              b[h].v[u] = *reinterpret_cast<const uint4*>(buf + swz<KF>(r, kg, 0));
+              b[h].sc[u] = e8m0_to_f32((sc[r] >> (8 * kg)) & 0xFFu);
+            } else {
+#pragma unroll
+              for (int ks = 0; ks < 4; ++ks) {
+                if constexpr (KF == 1)
+                  b[h].v[u][ks] = *reinterpret_cast<const uint2*>(buf + swz<KF>(r, ks * 2 + (kg >> 1), (kg & 1) * 8));
+                else
+                  b[h].v[u][ks] = *reinterpret_cast<const uint4*>(buf + swz<KF>(r, ks * 4 + kg, 0));
+              }
+              if constexpr (KF == 1) b[h].sc[u] = __uint_as_float(sc[r]);
             }
-            if constexpr (KF == 1) b.sc[u] = __uint_as_float(sc[r]);
           }
         }
-        const uint32_t key = score_page<KF, HT>(b, qa, wv, kg);
-        const int64_t e = pg * E + lane;
-        if (e < n_elig) {
-          const uint32_t k2 = pg_phys[i] >= 0 ? key : 0u;
-          keys_q[e] = k2;
-          const uint32_t bin = k2 >> (32 - kHistBits);
-          atomicAdd(&hist_s[wave][bin >> 1], 1u << ((bin & 1u) * 16));
+        uint32_t key[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) key[h] = score_page<KF, HT>(b[h], qa, wv, kg);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int i = i0 + h;
+          const int64_t pg = pg_begin + i;
+          const int64_t e = pg * E + lane;
+          if (i < n_pg && pg < w_npages[wave] && e < n_elig) {
+            const uint32_t k2 = pg_phys[i] >= 0 ? key[h] : 0u;
+            keys_q[e] = k2;
+            const uint32_t bin = k2 >> (32 - kHistBits);
+            atomicAdd(&hist_s[wave][bin >> 1], 1u << ((bin & 1u) * 16));
+          }
         }
       }
     }
