@@ -1076,6 +1076,8 @@ __global__ void __launch_bounds__(256 * QPW, 1) attend_dense_kernel(AttendArgs a
   const bool shared = has1 && seq_0 == seq_1 && dp <= kDensePairSpan && -dp <= kDensePairSpan;
   const int n_ps = (has1 && !shared) ? 2 : 1;
   const int my_ne = qi ? ne_1 : ne_0, my_lo = qi ? lo_1 : lo_0, my_p = qi ? p_1 : p_0;
+  // top-k mode (one query per workgroup): the query's list of selected entries
+  const int32_t* topk_q = (QPW == 1 && a.topk) ? a.topk + int64_t(q0) * a.k : nullptr;
 
   bf16x8 qb[NHB][16];
   {
@@ -1114,7 +1116,7 @@ __global__ void __launch_bounds__(256 * QPW, 1) attend_dense_kernel(AttendArgs a
     const int seq = in0 ? seq_0 : seq_1;
     int n_cu = 0, lo_u = INT_MAX, hi_u = -1;
     if (in0) {
-      n_cu = ne_0;
+      n_cu = topk_q ? a.k : ne_0;
       if (p_0 >= lo_0) { lo_u = lo_0; hi_u = p_0; }
     }
     if (in1) {
@@ -1133,15 +1135,22 @@ __global__ void __launch_bounds__(256 * QPW, 1) attend_dense_kernel(AttendArgs a
     for (int pass0 = 0; pass0 < n_keys; pass0 += kMaxKeys) {
       const int n_pass = min(kMaxKeys, n_keys - pass0);
       __syncthreads();  // the previous walk is done with the row table and both tile buffers
-      // ---- page rows of this pass's keys: key t < n_cu is entry t, else window position lo_u + t - n_cu
+      // ---- page rows of this pass's keys: key t < n_cu is entry t (top-k mode: list slot t, an entry outside
+      // [0, eligible) maps to no row), else window position lo_u + t - n_cu
       {
         constexpr int PER = kMaxKeys / NT;
-        int32_t phys[PER];
+        int32_t ent[PER], phys[PER];
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
           const int t = pass0 + tid + NT * j;
           const bool is_c = t < n_cu;
-          const int e = is_c ? t : lo_u + (t - n_cu);
+          ent[j] = is_c ? (topk_q ? topk_q[t < a.k ? t : 0] : t) : lo_u + (t - n_cu);  // clamped list load
+        }
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+          const int t = pass0 + tid + NT * j;
+          const bool is_c = t < n_cu;
+          const int e = ent[j] < 0 ? 0 : ent[j];
           const int blk = e / (is_c ? per_block : kBlock);
           const int bts = is_c ? bts_c : bts_w;
           phys[j] = (is_c ? bt_c : bt_w)[blk < bts ? blk : bts - 1];  // clamped, unconditional load
@@ -1151,11 +1160,11 @@ __global__ void __launch_bounds__(256 * QPW, 1) attend_dense_kernel(AttendArgs a
           const int local = tid + NT * j;
           const int t = pass0 + local;
           const bool is_c = t < n_cu;
-          const int e = is_c ? t : lo_u + (t - n_cu);
+          const int e = ent[j];
           const int per = is_c ? per_block : kBlock;
-          const int blk = e / per;
-          const bool ok = local < n_pass && blk < (is_c ? bts_c : bts_w) && phys[j] >= 0 &&
-                          phys[j] < (is_c ? nph_c : nph_w) && (is_c ? seq_c : seq_w);
+          const int blk = (e < 0 ? 0 : e) / per;
+          const bool ok = local < n_pass && e >= 0 && (!is_c || !topk_q || e < ne_0) && blk < (is_c ? bts_c : bts_w) &&
+                          phys[j] >= 0 && phys[j] < (is_c ? nph_c : nph_w) && (is_c ? seq_c : seq_w);
           key_row[local] = ok ? phys[j] * per + (e - blk * per) : -1;
         }
       }
@@ -1218,7 +1227,7 @@ __global__ void __launch_bounds__(256 * QPW, 1) attend_dense_kernel(AttendArgs a
         {
           const int g = pass0 + tt;
           bool ok = krow >= 0;
-          if (g < n_cu) ok = ok && g < my_ne;
+          if (g < n_cu) ok = ok && (topk_q != nullptr || g < my_ne);
           else {
             const int pos = lo_u + (g - n_cu);
             ok = ok && pos >= my_lo && pos <= my_p;
@@ -1435,9 +1444,11 @@ static bool use_split_path(const AttendArgs& a) {
   return a.cache.dtype != CSA_F32 && a.cache.dim == kD && a.n_heads % 64 == 0;
 }
 
-static bool use_dense_path(const AttendArgs& a) {
-  return a.topk == nullptr && a.cache.dtype == CSA_BF16 && a.cache.dim == kD && a.n_heads % 64 == 0 &&
-         a.n_q >= kDenseMinQueries;
+// Queries per workgroup of the many-query kernel for this launch, 0 when it does not take it: dense launches pair
+// consecutive queries (they share their keys), top-k launches take one query per workgroup.
+static int dense_queries(const AttendArgs& a) {
+  if (a.cache.dtype != CSA_BF16 || a.cache.dim != kD || a.n_heads % 64 != 0 || a.n_q < kDenseMinQueries) return 0;
+  return a.topk ? 1 : kDenseQueries;
 }
 
 static int64_t max_keys_of(const AttendArgs& a) {
@@ -1454,10 +1465,11 @@ size_t attend_workspace(int n_q, int n_heads, int dim, int64_t max_keys) {
 
 hipError_t launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (a.n_q == 0) return hipSuccess;
-  if (use_dense_path(a)) {
-    const int64_t units = int64_t((a.n_q + kDenseQueries - 1) / kDenseQueries) * (a.n_heads / 64);
-    hipLaunchKernelGGL((attend_dense_kernel<kDenseQueries>), dim3(unsigned((units + 7) / 8 * 8)),
-                       dim3(256 * kDenseQueries), 0, stream, a);
+  if (const int qpw = dense_queries(a)) {
+    const int64_t units = int64_t((a.n_q + qpw - 1) / qpw) * (a.n_heads / 64);
+    const dim3 grid(unsigned((units + 7) / 8 * 8));
+    if (qpw == 1) hipLaunchKernelGGL((attend_dense_kernel<1>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((attend_dense_kernel<2>), grid, dim3(512), 0, stream, a);
     return hipGetLastError();
   }
   if (use_split_path(a)) {

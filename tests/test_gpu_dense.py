@@ -1,4 +1,4 @@
-"""GPU parity of dense attention launched with many queries (the prefill form of c128a attention).
+"""GPU parity of attention launched with many queries (the prefill form of c128a dense and c4a top-k attention).
 
 Dense c128a layers attend to every eligible compressed entry plus the raw window ([P2] "二、注意力機制為什么這么麻煩",
 [P3] "注意力计算剪枝"); a prefill chunk hands the attention thousands of queries at once ([P1] "GPU Compute
@@ -6,8 +6,10 @@ Saturation": prefill with bf16 caches). From 512 dense queries per launch the li
 workgroups that read each key tile once for all of them, so these cases put queries of one sequence next to each
 other (shared key walks), queries of different sequences or far-apart positions next to each other (separate walks),
 queries without eligible entries or without any key, sequence ids outside the tables and unmapped cache blocks.
-Every query is compared with the oracle (or a seeded sample of them where the oracle is slow), fp32 output within
-2e-3 of the row maximum, log-sum-exp within 1e-4; the fp8 output form is compared as in the attention parity tests.
+Top-k launches of 512+ queries take the same kernel one query per workgroup (lists with padding, ineligible and
+repeated entries, up to top-2048 plus a 1024-row window). Every query is compared with the oracle (or a seeded sample
+of them where the oracle is slow), fp32 output within 2e-3 of the row maximum, log-sum-exp within 1e-4; the fp8
+output form is compared as in the attention parity tests.
 """
 import math
 
@@ -186,3 +188,60 @@ def test_dense_many_queries_deterministic():
     b_out, b_lse = st.gpu(128)
     assert np.array_equal(a_out.view(np.uint32), b_out.view(np.uint32))
     assert np.array_equal(a_lse.view(np.uint32), b_lse.view(np.uint32))
+
+
+@pytest.mark.parametrize("k,window,heads", [(512, 128, 64), (2048, 1024, 64)])
+def test_many_queries_topk(k, window, heads):
+    """Top-k attention with 512+ queries (the prefill form of c4a attention) takes the many-query kernel one query
+    per workgroup. Lists hold -1 padding, entries at or beyond the query's eligible count (masked) and repeated
+    entries (each slot is a key of its own, no de-duplication); top-2048 plus a 1024-row window fills the row table
+    exactly. A seeded sample of the queries is compared with the oracle."""
+    import synth as sy
+    cfg = 800 + k + window
+    n_seq = 3
+    spec = [(0, range(20000, 20200)), (1, range(9000, 9200)), (2, range(30000, 30130))]
+    q_seq, q_pos = _queries(spec)
+    n_q = len(q_pos)
+    assert n_q >= 512
+    p_max = [int(q_pos[q_seq == b].max()) for b in range(n_seq)]
+    nb = max(p_max) // 256 + 1
+    n_phys = n_seq * nb + 3
+    bt = sy.random_block_table(sy.rng(cfg, sy.STREAM_BT), n_seq, nb, n_phys)
+    pages = sy.normal_bf16_bits(sy.rng(cfg, sy.STREAM_KV), (n_phys * 64, D))
+    wpages = sy.normal_bf16_bits(sy.rng(cfg, sy.STREAM_SWA), (n_phys * 256, D))
+    q = sy.normal_bf16_bits(sy.rng(cfg, sy.STREAM_Q), (n_q, heads, D))
+    g = sy.rng(cfg, 30)
+    tk = np.full((n_q, k), -1, np.int32)
+    for i, p in enumerate(q_pos):
+        n = paging.num_eligible(int(p), 4, 8)
+        take = min(k - 8, n)
+        lst = list(g.choice(n, size=take, replace=False))
+        lst += [int(lst[0]), int(lst[1])]           # repeated entries
+        lst += [n, n + 5, 1 << 20]                 # not eligible for this query: masked
+        tk[i, :len(lst)] = np.array(lst, np.int32)
+    max_elig = max(paging.num_eligible(int(p), 4, 8) for p in q_pos)
+    scale = 1.0 / math.sqrt(D)
+    rows = int(q_pos.max()) + 1
+    cache = csa.Cache(4, 8, D, R, gu.dev_store(pages, "bf16"), gu.dev_i32(bt), None)
+    swa = csa.Raw(D, 0, gu.dev_store(wpages, "bf16"), gu.dev_i32(bt), None, None)
+    need = csa.attend_workspace(n_q, heads, D, k + window)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    out = torch.full((n_q, heads, D), -7.0, device="cuda")
+    lse = torch.full((n_q, heads), -7.0, device="cuda")
+    _log(f"many-query top-k: n_q={n_q} k={k} window={window} heads={heads}")
+    csa.attend(cache, swa, window, gu.dev_i32(q_seq), gu.dev_i32(q_pos), gu.dev_bf16(q), gu.dev_i32(tk), max_elig,
+               scale, True, csa.rope_table(rows, R), out, lse, workspace=ws)
+    torch.cuda.synchronize()
+    g_out, g_lse = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.all(np.isfinite(g_out)) and np.all(np.isfinite(g_lse))
+    gs = sy.rng(cfg, 31)
+    idx = np.array(sorted(set([0, n_q - 1] + list(gs.choice(n_q, size=30, replace=False)))))
+    # the oracle takes every listed entry below the query's eligible count (repeats included)
+    otk = np.where((tk >= 0) & (tk < np.array([paging.num_eligible(int(p), 4, 8) for p in q_pos])[:, None]), tk, -1)
+    o_out, o_lse = oa.attend(oc.Cache(4, 8, D, R, "bf16", pages, None, bt), oc.Raw("bf16", D, 0, wpages, None, None, bt),
+                             window, q_seq[idx], q_pos[idx], codecs.load_rows(q[idx], "bf16"), otk[idx], scale, True,
+                             orope.rope_table(rows, R))
+    err = gu.rowwise_rel_err(g_out[idx], o_out)
+    _log(f"many-query top-k k={k}: rowwise rel err {err:.3e} over {len(idx)} queries")
+    assert err <= TOL
+    assert np.allclose(g_lse[idx], o_lse, rtol=0, atol=1e-4)
