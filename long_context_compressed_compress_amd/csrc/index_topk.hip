@@ -827,6 +827,7 @@ __device__ __forceinline__ uint32_t wave_slot(bool take, uint32_t* counter) {
 }
 
 constexpr int kBitmapLds = 8192;  // LDS bitmap words: queries with up to 262144 eligible entries
+constexpr int kSelManyQueries = 256;  // launches of at least this many queries take the half-size select workgroups
 
 // ------------------------------------------------------------------ mark pass (few queries with many entries)
 // One workgroup per query cannot scan a long key list quickly, so for few long queries the key pass runs
@@ -914,15 +915,15 @@ __global__ void __launch_bounds__(kMarkThreads) select_mark_kernel(IndexArgs a, 
   flush_hist(h2_s, ws.hist2 + int64_t(q) * kHistBins);
 }
 
-template <bool PRE>
-__global__ void __launch_bounds__(kSelThreads) select_kernel(IndexArgs a, Workspace ws) {
-  __shared__ uint32_t tmp[kSelThreads / 64];
+template <bool PRE, int NT, int BMW, int CLDS>
+__global__ void __launch_bounds__(NT) select_kernel(IndexArgs a, Workspace ws) {
+  __shared__ uint32_t tmp[NT / 64];
   __shared__ uint32_t hist2[kHistBins];      // key bits 19..8 of the candidates
   __shared__ uint32_t dig[256];
   __shared__ uint32_t res[4];
   __shared__ uint32_t s_cnt[2];              // sure count, candidate count
-  __shared__ uint32_t bitmap_s[kBitmapLds];  // chosen entries, one bit each
-  __shared__ uint2 cand_s[kCandLds];
+  __shared__ uint32_t bitmap_s[BMW];  // chosen entries, one bit each
+  __shared__ uint2 cand_s[CLDS];
 
   const int q = blockIdx.x;
   int seq;
@@ -937,11 +938,11 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(IndexArgs a, Worksp
   const bool pre = PRE && n_elig > a.k;
   uint32_t* bits_g = ws.bits + int64_t(q) * ws.bits_stride;
   // longer queries keep their bitmap in the workspace
-  uint32_t* bitmap = n_words <= kBitmapLds ? bitmap_s : bits_g;
+  uint32_t* bitmap = n_words <= BMW ? bitmap_s : bits_g;
   uint32_t* hist2_g = ws.hist2 + int64_t(q) * kHistBins;
   // after a mark pass every global read of the set-up (score histogram, bitmap words, second histogram) is
   // issued here, before any of them is used, so they cost one round trip together
-  constexpr int PER = kHistBins / kSelThreads;
+  constexpr int PER = kHistBins / NT;
   const uint32_t* hist = ws.hist + int64_t(q) * kHistBins;
   uint32_t h[PER];
   if (pre) {
@@ -949,38 +950,38 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(IndexArgs a, Worksp
     for (int j = 0; j < PER; ++j) h[j] = hist[tid * PER + j];
   }
   if (pre) {
-    constexpr int BW = kBitmapLds / kSelThreads;  // bitmap words per thread when the bitmap fits LDS
+    constexpr int BW = BMW / NT;  // bitmap words per thread when the bitmap fits LDS
     const bool lds_bits = bitmap != bits_g;
     uint32_t bw[BW], h2[PER];
     if (lds_bits) {
 #pragma unroll
       for (int j = 0; j < BW; ++j) {
-        const int64_t w = tid + int64_t(kSelThreads) * j;
+        const int64_t w = tid + int64_t(NT) * j;
         bw[j] = bits_g[w < n_words ? w : 0];  // clamped, unconditional load
       }
     }
 #pragma unroll
-    for (int j = 0; j < PER; ++j) h2[j] = hist2_g[tid + kSelThreads * j];
+    for (int j = 0; j < PER; ++j) h2[j] = hist2_g[tid + NT * j];
     const uint32_t nc = tid == 0 ? ws.ncand[q] : 0u;
     if (lds_bits) {
 #pragma unroll
       for (int j = 0; j < BW; ++j) {
-        const int64_t w = tid + int64_t(kSelThreads) * j;
+        const int64_t w = tid + int64_t(NT) * j;
         if (w < n_words) bitmap[w] = bw[j];
       }
     }
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-      hist2[tid + kSelThreads * j] = h2[j];
-      hist2_g[tid + kSelThreads * j] = 0u;  // left zero for the next mark pass
+      hist2[tid + NT * j] = h2[j];
+      hist2_g[tid + NT * j] = 0u;  // left zero for the next mark pass
     }
     if (tid == 0) {
       s_cnt[1] = nc;
       ws.ncand[q] = 0u;
     }
   } else {
-    for (int64_t w = tid; w < n_words; w += kSelThreads) bitmap[w] = 0u;
-    for (int b = tid; b < kHistBins; b += kSelThreads) hist2[b] = 0u;
+    // every bitmap word below n_words is stored whole by the key pass, so only hist2 and the counters start at 0
+    for (int b = tid; b < kHistBins; b += NT) hist2[b] = 0u;
     if (tid < 2) s_cnt[tid] = 0u;
   }
 
@@ -995,7 +996,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(IndexArgs a, Worksp
 #pragma unroll
     for (int j = 0; j < PER; ++j) local += h[j];
     uint32_t excl;
-    const uint32_t total = block_excl_scan(local, tmp, &excl);
+    const uint32_t total = block_excl_scan<NT>(local, tmp, &excl);
     uint32_t run = total - excl - local;
     if (tid == 0) { res[0] = 0xFFFFFFFFu; res[1] = 0u; }
     __syncthreads();
@@ -1010,32 +1011,49 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(IndexArgs a, Worksp
   __threadfence_block();
   __syncthreads();
 
-  // ---- one pass over the keys: mark keys above the bin, collect keys inside it (and their next 12 bits)
-  for (int64_t base = 0; base < (pre ? 0 : n_elig); base += int64_t(kSelThreads) * kSelKeysPerThread) {
+  // ---- one pass over the keys: mark keys above the bin, collect keys inside it (and their next 12 bits).
+  // For step j a wave holds 64 consecutive keys starting on a 64-key boundary, so it owns two whole bitmap
+  // words and stores them from its ballot. Candidates are rare: a wave reserves list slots for all of its
+  // candidates of a chunk with one LDS atomic, at offsets taken from the per-step ballots.
+  const int lane = tid & 63;
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int64_t base = 0; base < (pre ? 0 : n_elig); base += int64_t(NT) * kSelKeysPerThread) {
     uint32_t key[kSelKeysPerThread];
 #pragma unroll
     for (int j = 0; j < kSelKeysPerThread; ++j) {
-      const int64_t i = base + tid + int64_t(kSelThreads) * j;
+      const int64_t i = base + tid + int64_t(NT) * j;
       key[j] = keys_q[i < n_elig ? i : 0];  // clamped, unconditional load
     }
+    uint32_t n_sure_w = 0, n_cand_w = 0, cand_off[kSelKeysPerThread];
+    uint64_t cand_m[kSelKeysPerThread];
 #pragma unroll
     for (int j = 0; j < kSelKeysPerThread; ++j) {
-      const int64_t i = base + tid + int64_t(kSelThreads) * j;
+      const int64_t i = base + tid + int64_t(NT) * j;
       const bool in = i < n_elig;
       const int bin = int(key[j] >> (32 - kHistBits));
-      const bool is_sure = in && (b0 < 0 || bin > b0);
-      const bool is_cand = in && b0 >= 0 && bin == b0;
-      const uint64_t sm = __ballot(is_sure);
-      if (sm) {
-        if ((threadIdx.x & 63) == 0) atomicAdd(&s_cnt[0], uint32_t(__popcll(sm)));
-        if (is_sure) atomicOr(&bitmap[i >> 5], 1u << (i & 31));
-      }
-      const uint32_t cs = wave_slot(is_cand, &s_cnt[1]);
-      if (is_cand) {
-        atomicAdd(&hist2[(key[j] >> 8) & (kHistBins - 1)], 1u);
-        const uint2 item = make_uint2(key[j], uint32_t(i));
-        if (cs < uint32_t(kCandLds)) cand_s[cs] = item;
-        else if (cs - kCandLds < uint32_t(a.max_elig)) cand_g[cs - kCandLds] = item;
+      const uint64_t sm = __ballot(in && (b0 < 0 || bin > b0));
+      const int64_t w0 = (base + (tid & ~63) + int64_t(NT) * j) >> 5;
+      if (lane < 2 && w0 + lane < n_words) bitmap[w0 + lane] = lane == 0 ? uint32_t(sm) : uint32_t(sm >> 32);
+      n_sure_w += uint32_t(__popcll(sm));
+      cand_m[j] = __ballot(in && b0 >= 0 && bin == b0);
+      cand_off[j] = n_cand_w;
+      n_cand_w += uint32_t(__popcll(cand_m[j]));
+    }
+    if (n_sure_w && lane == 0) atomicAdd(&s_cnt[0], n_sure_w);
+    if (n_cand_w) {
+      uint32_t wbase = 0;
+      if (lane == 0) wbase = atomicAdd(&s_cnt[1], n_cand_w);
+      wbase = uint32_t(__builtin_amdgcn_readfirstlane(int(wbase)));  // every lane is active here
+#pragma unroll
+      for (int j = 0; j < kSelKeysPerThread; ++j) {
+        if ((cand_m[j] >> lane) & 1ull) {
+          const int64_t i = base + tid + int64_t(NT) * j;
+          const uint32_t cs = wbase + cand_off[j] + uint32_t(__popcll(cand_m[j] & below));
+          atomicAdd(&hist2[(key[j] >> 8) & (kHistBins - 1)], 1u);
+          const uint2 item = make_uint2(key[j], uint32_t(i));
+          if (cs < uint32_t(CLDS)) cand_s[cs] = item;
+          else if (cs - CLDS < uint32_t(a.max_elig)) cand_g[cs - CLDS] = item;
+        }
       }
     }
   }
@@ -1043,19 +1061,19 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(IndexArgs a, Worksp
   __syncthreads();
 
   const uint32_t n_sure = s_cnt[0];
-  const uint32_t lds_n = pre ? 0u : uint32_t(kCandLds);  // the mark pass lists every candidate in the workspace
+  const uint32_t lds_n = pre ? 0u : uint32_t(CLDS);  // the mark pass lists every candidate in the workspace
   const uint32_t n_cand = min<uint32_t>(s_cnt[1], uint32_t(min<int64_t>(int64_t(lds_n) + a.max_elig, 0xFFFFFFFFll)));
   auto cand_at = [=](uint32_t j) -> uint2 { return j < lds_n ? cand_s[j] : cand_g[j - lds_n]; };
   int64_t need = kk - int64_t(n_sure);
   if (need > 0) {
     // sub-bin of key bits 19..8: largest b1 with count(candidates with bits >= b1) >= need
-    constexpr int PER = kHistBins / kSelThreads;
+    constexpr int PER = kHistBins / NT;
     uint32_t h[PER];
     uint32_t local = 0;
 #pragma unroll
     for (int j = 0; j < PER; ++j) { h[j] = hist2[tid * PER + j]; local += h[j]; }
     uint32_t excl;
-    const uint32_t total = block_excl_scan(local, tmp, &excl);
+    const uint32_t total = block_excl_scan<NT>(local, tmp, &excl);
     uint32_t run = total - excl - local;
     if (tid == 0) { res[0] = 0u; res[1] = 0u; }
     __syncthreads();
@@ -1115,12 +1133,12 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(IndexArgs a, Worksp
   __syncthreads();
 
   // ---- compaction of the bitmap in index order (each thread owns a run of consecutive words)
-  const int64_t per_t = (n_words + kSelThreads - 1) / kSelThreads;
+  const int64_t per_t = (n_words + NT - 1) / NT;
   const int64_t w0 = int64_t(tid) * per_t;
   uint32_t mine = 0;
   for (int64_t w = w0; w < w0 + per_t && w < n_words; ++w) mine += __popc(bitmap[w]);
   uint32_t off;
-  const uint32_t n_sel_all = block_excl_scan(mine, tmp, &off);
+  const uint32_t n_sel_all = block_excl_scan<NT>(mine, tmp, &off);
   const int n_sel = int(min<int64_t>(n_sel_all, kk));
   int32_t* outq = a.out_idx + int64_t(q) * a.k;
   float* outs = a.out_scores ? a.out_scores + int64_t(q) * a.k : nullptr;
@@ -1137,7 +1155,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(IndexArgs a, Worksp
       ++off;
     }
   }
-  for (int j = n_sel + tid; j < a.k; j += kSelThreads) {
+  for (int j = n_sel + tid; j < a.k; j += NT) {
     outq[j] = -1;
     if (outs) outs[j] = __uint_as_float(0x7FC00000u);
   }
@@ -1266,9 +1284,16 @@ hipError_t launch_index_select(const IndexArgs& a, hipStream_t stream) {
   if (a.n_q <= kPremarkMaxQueries && a.max_elig >= kPremarkMinElig) {
     const dim3 grid(unsigned((a.max_elig + kMarkChunk - 1) / kMarkChunk), unsigned(a.n_q));
     hipLaunchKernelGGL(select_mark_kernel, grid, dim3(kMarkThreads), 0, stream, a, ws);
-    hipLaunchKernelGGL(select_kernel<true>, dim3(a.n_q), dim3(kSelThreads), 0, stream, a, ws);
+    hipLaunchKernelGGL((select_kernel<true, kSelThreads, kBitmapLds, kCandLds>), dim3(a.n_q), dim3(kSelThreads), 0, stream,
+                       a, ws);
+  } else if (a.n_q >= kSelManyQueries) {
+    // many queries: half-size workgroups with half-size LDS tables, two per CU, so that one workgroup's
+    // scans and barriers overlap the other's key loads
+    hipLaunchKernelGGL((select_kernel<false, kSelThreads / 2, kBitmapLds / 2, kCandLds / 2>), dim3(a.n_q),
+                       dim3(kSelThreads / 2), 0, stream, a, ws);
   } else {
-    hipLaunchKernelGGL(select_kernel<false>, dim3(a.n_q), dim3(kSelThreads), 0, stream, a, ws);
+    hipLaunchKernelGGL((select_kernel<false, kSelThreads, kBitmapLds, kCandLds>), dim3(a.n_q), dim3(kSelThreads), 0,
+                       stream, a, ws);
   }
   return hipGetLastError();
 }

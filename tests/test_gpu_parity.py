@@ -245,6 +245,62 @@ def test_index_topk_all_ties_takes_lowest_indices(k, positions):
         assert np.all(sc[b][:n] == 64 * 0.5 * 128.0) and np.all(np.isnan(sc[b][n:]))
 
 
+def _run_index_one_seq(pc, positions, q, w, mode, k, q_dtype):
+    """Every query on sequence 0 of `pc`."""
+    B = len(positions)
+    max_elig = max(paging.num_eligible(p, pc.ratio, pc.window) for p in positions)
+    out = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    sc = torch.zeros((B, k), dtype=torch.float32, device="cuda")
+    qd = gu.dev_f32(q) if q_dtype == "f32" else gu.dev_bf16(q)
+    csa.index_topk(_gpu_cache(pc), gu.dev_i32(np.zeros(B, np.int64)), gu.dev_i32(positions), max_elig, qd,
+                   gu.dev_f32(w) if w is not None else None, mode, k, out, cnt, sc)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), cnt.cpu().numpy(), sc.cpu().numpy()
+
+
+def test_index_topk_many_queries_long_bit_exact():
+    """256 queries of one 600000-token sequence (up to 149999 eligible entries): the many-query select runs
+    several key chunks per query, keeps short queries' chosen-entry bitmaps in LDS and long ones (more than
+    131072 entries) in the workspace. Exact-grid keys and queries make every score exact and leave many equal
+    scores, so ties at the boundary (lowest index first) and long candidate lists take part. A query's eligible
+    entries are a prefix of the sequence's entry list, so the oracle's keys are taken once for the longest."""
+    import synth
+    P = 600000
+    positions = np.unique(np.concatenate([np.linspace(9, P, 252).astype(np.int64), [P - 1, P, 524300, 524296, 7, 8]]))
+    assert len(positions) >= 256
+    _log(f"index many queries long: {len(positions)} queries up to {P}")
+    pc = si.paged_cache(71, 4, 32, "f32", [P], grid=True)
+    q = synth.grid_values(synth.rng(71, synth.STREAM_QIDX), (len(positions), 1, 32))
+    k = 64
+    out, cnt, sc = _run_index_one_seq(pc, positions, q, None, oi.DOT, k, "f32")
+    keys = oi.eligible_keys(pc.oracle(), 0, P)
+    for b, p in enumerate(positions):
+        n = paging.num_eligible(int(p), 4, 8)
+        o_idx, o_sc, o_cnt = oi.topk(oi.scores(keys[:n], q[b], None, oi.DOT), k)
+        assert cnt[b] == o_cnt, (p, cnt[b], o_cnt)
+        assert np.array_equal(out[b], o_idx), p
+        assert np.array_equal(sc[b][:o_cnt].astype(np.float64), o_sc[:o_cnt]), p
+
+
+def test_index_topk_many_queries_all_ties():
+    """300 queries of one sequence, every score equal: each query's lowest k entries win. Up to 9999 tied
+    candidates per query overflow the many-query select's LDS list into the workspace list."""
+    positions = np.array([40000 - 131 * i for i in range(300)], np.int64)
+    _log("index many queries all ties")
+    pc = si.paged_cache(5, 4, 128, "bf16", [int(positions.max())])
+    pc.pages[:] = 0x3F80  # every key = 1.0
+    q = np.full((len(positions), 64, 128), 0x3F80, np.uint16)
+    w = np.full((len(positions), 64), 0.5, np.float32)
+    k = 512
+    out, cnt, sc = _run_index_one_seq(pc, positions, q, w, oi.WRELU, k, "bf16")
+    for b, p in enumerate(positions):
+        n = min(k, paging.num_eligible(int(p), 4, 8))
+        assert cnt[b] == n
+        assert np.array_equal(out[b][:n], np.arange(n)) and np.all(out[b][n:] == -1)
+        assert np.all(sc[b][:n] == 64 * 0.5 * 128.0) and np.all(np.isnan(sc[b][n:]))
+
+
 @pytest.mark.parametrize("dtype,positions", [("bf16", [20000, 14011, 9001, 300, 7]), ("fp8", [30000, 2100]),
                                              ("bf16", [400000, 90001, 1500]), ("fp8", [1100000, 300])])
 def test_index_topk_continuous_near_ties(dtype, positions):
