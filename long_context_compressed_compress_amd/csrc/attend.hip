@@ -986,6 +986,12 @@ constexpr int kDenseMinQueries = 512;  // launches with at least this many dense
 constexpr int kDensePairSpan = 64;     // two queries further apart than this walk their keys separately
 constexpr float kDenseRescaleMargin = 8.0f;  // natural-log units the running maximum may lag the true one
 constexpr int kDenseQueries = 2;      // queries per workgroup (2: eight waves, two per SIMD; 1: four waves)
+// Tile rows in LDS: 1056 bytes apart, and 16-byte chunk c of row r stored at c ^ bit 3 of r. Both read patterns of
+// the kernel keep this a per-lane constant (the S^T rows a 16-lane group reads share bit 3 with nothing that
+// changes along the unrolled loops, and so do the V^T rows), and it spreads the S^T reads of a 16-lane group over
+// all banks; rows padded to 1040 bytes without the flip left those reads at about 60 % of the LDS rate.
+constexpr int kDenseRowStride = kD * 2 + 32;
+__device__ __forceinline__ int dense_chunk_flip(int row) { return (row >> 3) & 1; }
 
 // One 1 KiB key row from global memory into LDS: lane l moves bytes [16 l, 16 l + 16) of the row to
 // lds_byte + 16 l. Issued from inline assembly: for the compiler's own form of this copy it orders every later LDS
@@ -1042,7 +1048,7 @@ __global__ void __launch_bounds__(256 * QPW, 1) attend_dense_kernel(AttendArgs a
   constexpr int NT = 256 * QPW;           // four waves (64 heads) per query
   constexpr int WPQ = 4;                  // waves per query
   constexpr int RPW = kTile / (4 * QPW);  // tile rows each wave moves
-  __shared__ __attribute__((aligned(16))) char kbuf[2][kTile * kRowStride];
+  __shared__ __attribute__((aligned(16))) char kbuf[2][kTile * kDenseRowStride];
   __shared__ int32_t key_row[kMaxKeys];
 
   // unit = (QPW consecutive queries, 64-head chunk); consecutive units on one XCD (workgroups are dealt to the
@@ -1103,11 +1109,16 @@ __global__ void __launch_bounds__(256 * QPW, 1) attend_dense_kernel(AttendArgs a
   const int per_block = kBlock / a.cache.ratio;
   // LDS byte offset of the key this lane reads as MFMA row `col` of 16-key block kb4 in S^T: the permutation
   // that puts the eight keys a lane supplies to PV into its own accumulator registers
-  // (blocks kb4 = 1, 2, 3 are the rows of block 0 moved by 16, 32 and 48 keys)
-  const int soff = perm_key(col >> 2, col & 3) * kRowStride + kg * 16;
-  // LDS byte offsets of the two 4-key rows a lane addresses in the transposing V^T reads of k-step c
-  const int voff0 = perm_key(kg, col >> 2) * kRowStride + 8 * (col & 3);  // + 32 rows for k-step 1
-  const int voff1 = perm_key(kg, 4 + (col >> 2)) * kRowStride + 8 * (col & 3);
+  // (blocks kb4 = 1, 2, 3 are the rows of block 0 moved by 16, 32 and 48 keys, which keeps the row's bit 3); the
+  // lane's chunk kg of each 64-byte k-step sits at kg ^ that bit
+  const int srow = perm_key(col >> 2, col & 3);
+  const int soff = srow * kDenseRowStride + (kg ^ dense_chunk_flip(srow)) * 16;
+  // LDS byte offsets of the two 4-key rows a lane addresses in the transposing V^T reads of k-step c (a lane's
+  // 8 bytes sit in chunk 2 db + bit 1 of col, flipped by the row's bit 3, which the two rows share: they differ by
+  // 16 keys)
+  const int vchunk = (((col & 3) >> 1) ^ dense_chunk_flip(perm_key(kg, col >> 2))) * 16 + 8 * (col & 1);
+  const int voff0 = perm_key(kg, col >> 2) * kDenseRowStride + vchunk;  // + 32 rows for k-step 1
+  const int voff1 = perm_key(kg, 4 + (col >> 2)) * kDenseRowStride + vchunk;
 
   for (int ps = 0; ps < n_ps; ++ps) {
     // queries of the pair in this walk: both when they share their keys, else one walk each
@@ -1184,18 +1195,19 @@ __global__ void __launch_bounds__(256 * QPW, 1) attend_dense_kernel(AttendArgs a
         }
         return bad;
       };
+      // lane l lands LDS chunk l of the row, so it copies the row's chunk l ^ (row bit 3)
       auto copy_row = [&](int tile, int buf, const int (&rows)[RPW], int j) {
         const int t = tile * kTile + wave * RPW + j;
         const char* base = (pass0 + t < n_cu) ? pages_c : pages_w;
-        dma_row(base + int64_t(rows[j] < 0 ? 0 : rows[j]) * (2 * kD) + lane * 16,
-                uint32_t(reinterpret_cast<uintptr_t>(kbuf[buf])) + uint32_t((wave * RPW + j) * kRowStride));
+        dma_row(base + int64_t(rows[j] < 0 ? 0 : rows[j]) * (2 * kD) + (lane ^ dense_chunk_flip(wave * RPW + j)) * 16,
+                uint32_t(reinterpret_cast<uintptr_t>(kbuf[buf])) + uint32_t((wave * RPW + j) * kDenseRowStride));
       };
       auto zero_rows = [&](int buf, uint32_t bad) {
         if (bad) {
-          char* dst = kbuf[buf] + wave * RPW * kRowStride;
+          char* dst = kbuf[buf] + wave * RPW * kDenseRowStride;
 #pragma unroll
           for (int j = 0; j < RPW; ++j)
-            if ((bad >> j) & 1u) *reinterpret_cast<uint4*>(dst + j * kRowStride + lane * 16) = make_uint4(0, 0, 0, 0);
+            if ((bad >> j) & 1u) *reinterpret_cast<uint4*>(dst + j * kDenseRowStride + lane * 16) = make_uint4(0, 0, 0, 0);
         }
       };
 
@@ -1246,7 +1258,7 @@ __global__ void __launch_bounds__(256 * QPW, 1) attend_dense_kernel(AttendArgs a
         auto load_k = [&](bf16x8 (&dst)[4], int ks) {
 #pragma unroll
           for (int kb4 = 0; kb4 < 4; ++kb4)
-            dst[kb4] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + soff + kb4 * 16 * kRowStride + ks * 64));
+            dst[kb4] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + soff + kb4 * 16 * kDenseRowStride + ks * 64));
         };
         load_k(kf[0], 0);
         load_k(kf[1], 1);
@@ -1351,8 +1363,8 @@ __global__ void __launch_bounds__(256 * QPW, 1) attend_dense_kernel(AttendArgs a
         bf16x8 vq[kPvAhead];
         auto load_v = [&](int st) -> bf16x8 {
           const int c = st >> 5, db = st & 31;
-          const uint2 e0 = lds_tr16(kb + c * 32 * kRowStride + voff0 + db * 32);
-          const uint2 e1 = lds_tr16(kb + c * 32 * kRowStride + voff1 + db * 32);
+          const uint2 e0 = lds_tr16(kb + c * 32 * kDenseRowStride + voff0 + db * 32);
+          const uint2 e1 = lds_tr16(kb + c * 32 * kDenseRowStride + voff1 + db * 32);
           return __builtin_bit_cast(bf16x8, make_uint4(e0.x, e0.y, e1.x, e1.y));
         };
 #pragma unroll
