@@ -530,6 +530,26 @@ __global__ void __launch_bounds__(512) attend_split_kernel(AttendArgs a, SplitPl
   const float* scales_c = a.cache.scales;
   const int64_t scales_dw = FP8 ? (int64_t(reinterpret_cast<uintptr_t>(a.swa.scales)) - int64_t(reinterpret_cast<uintptr_t>(scales_c))) : 0;
 
+  // Keys of a pass: list slots (top-k mode) or entry numbers below n_c, then window positions. Key positions,
+  // entries and window positions fit 32 bits (positions are 32-bit at the boundary). Every list load is
+  // unconditional (dense mode reads element 0 of the position array and ignores it) and lands in a register of its
+  // own; the entries are derived only after every load is out, so the loads overlap. (Overwriting a load's register
+  // under a condition before the next load is issued makes each load wait for the one before it.)
+  constexpr int PER = (kMaxKeys + 511) / 512;
+  const int32_t* lst = topk_q ? topk_q : a.q_pos;
+  const int n_c32 = int(n_c), n_keys32 = int(n_keys), lo32 = int(lo);
+  auto issue_list = [&](int pass0, int32_t (&raw)[PER]) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int t = pass0 + tid + 512 * j;
+      raw[j] = lst[(topk_q != nullptr && t < n_c32) ? t : 0];
+    }
+  };
+  // the first pass's list loads go out before the query fragments: the wait for the list (loads complete in
+  // issue order) then does not also wait for the 64 KiB of query
+  int32_t raw[PER];
+  issue_list(int(k_begin), raw);
+
   bf16x8 qa[16];
   const int head0 = hc * 64 + hg * 16;
   const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + (int64_t(q) * a.n_heads + head0 + col) * kD;
@@ -544,45 +564,50 @@ __global__ void __launch_bounds__(512) attend_split_kernel(AttendArgs a, SplitPl
   for (int i = 0; i < 4; ++i) { m_run[i] = -INFINITY; l_run[i] = 0.f; }
   const float scale = a.scale;
 
+  // page rows of the keys of a pass from its list values (block-table loads unconditional, indices clamped)
+  auto resolve = [&](int p0, const int32_t (&raw)[PER]) {
+    int32_t ent[PER], phys[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int t = p0 + tid + 512 * j;
+      ent[j] = t < n_c32 ? (topk_q ? raw[j] : t) : (t < n_keys32 ? lo32 + (t - n_c32) : -1);
+    }
+    // entries per block are a power of two (256 / ratio), as is the raw block of 256 positions
+    const int lpb = __builtin_ctz(unsigned(per_block));
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const bool is_c = p0 + tid + 512 * j < n_c32;
+      const int e = ent[j] < 0 ? 0 : ent[j];
+      const int blk = is_c ? (e >> lpb) : (e >> 8);
+      const int bts = is_c ? bts_c : bts_w;
+      phys[j] = (is_c ? bt_c : bt_w)[blk < bts ? blk : bts - 1];
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int local = tid + 512 * j;
+      const int t = p0 + local;
+      const bool is_c = t < n_c32;
+      const int e = ent[j];
+      const int sh = is_c ? lpb : 8;
+      const int blk = (e < 0 ? 0 : e) >> sh;
+      const bool ok = e >= 0 && t < n_keys32 && blk < (is_c ? bts_c : bts_w) && phys[j] >= 0 &&
+                      phys[j] < (is_c ? nph_c : nph_w) && (is_c ? (seq_c && e < n_elig) : seq_w);
+      if (local < kMaxKeys) {
+        key_row[local] = int32_t(ok ? (int64_t(phys[j]) << sh) + (e - (blk << sh)) : -1);
+        key_kind[local] = uint8_t(is_c ? 0 : 1);
+      }
+    }
+  };
+  // the first pass is resolved here, in straight-line code after the query loads, so that each wait covers only
+  // the loads it needs; later passes (more keys than the row table holds) resolve at the top of their pass
+  resolve(int(k_begin), raw);
+
   for (int64_t pass0 = k_begin; pass0 < k_end; pass0 += kMaxKeys) {
     const int n_pass = int(min<int64_t>(kMaxKeys, k_end - pass0));
-    // ---- resolve page rows of this pass (all loads unconditional, indices clamped)
-    {
-      constexpr int PER = (kMaxKeys + 511) / 512;
-      int32_t ent[PER];
-#pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int64_t t = pass0 + tid + 512 * j;
-        const int32_t v = topk_q ? topk_q[t < n_c ? t : 0] : 0;  // dense mode reads no index list
-        int64_t e = topk_q ? int64_t(v) : t;
-        if (t >= n_c) e = (t < n_keys) ? lo + (t - n_c) : -1;
-        ent[j] = int32_t(e);
-      }
-      int32_t phys[PER];
-#pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int64_t t = pass0 + tid + 512 * j;
-        const bool is_c = t < n_c;
-        const int64_t blk = ent[j] < 0 ? 0 : ent[j] / (is_c ? per_block : kBlock);
-        const int32_t* bt = is_c ? bt_c : bt_w;
-        const int bts = is_c ? bts_c : bts_w;
-        phys[j] = bt[blk < bts ? blk : bts - 1];
-      }
-#pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int local = tid + 512 * j;
-        const int64_t t = pass0 + local;
-        const bool is_c = t < n_c;
-        const int64_t e = ent[j];
-        const int per = is_c ? per_block : kBlock;
-        const int64_t blk = e < 0 ? 0 : e / per;
-        const bool ok = e >= 0 && t < n_keys && blk < (is_c ? bts_c : bts_w) && phys[j] >= 0 &&
-                        phys[j] < (is_c ? nph_c : nph_w) && (is_c ? (seq_c && e < n_elig) : seq_w);
-        if (local < kMaxKeys) {
-          key_row[local] = int32_t(ok ? int64_t(phys[j]) * per + (e - blk * per) : -1);
-          key_kind[local] = uint8_t(is_c ? 0 : 1);
-        }
-      }
+    if (pass0 != k_begin) {
+      int32_t raw2[PER];
+      issue_list(int(pass0), raw2);
+      resolve(int(pass0), raw2);
     }
     __syncthreads();
 
@@ -1145,7 +1170,10 @@ __global__ void __launch_bounds__(256 * QPW, 1) attend_dense_kernel(AttendArgs a
 
     for (int pass0 = 0; pass0 < n_keys; pass0 += kMaxKeys) {
       const int n_pass = min(kMaxKeys, n_keys - pass0);
-      __syncthreads();  // the previous walk is done with the row table and both tile buffers
+      // the previous walk or pass is done with the row table and both tile buffers. Not needed before the first
+      // pass: skipping it there lets the list and table loads below go out while the query loads are in flight
+      // (the barrier waits for every outstanding load)
+      if (ps > 0 || pass0 > 0) __syncthreads();
       // ---- page rows of this pass's keys: key t < n_cu is entry t (top-k mode: list slot t, an entry outside
       // [0, eligible) maps to no row), else window position lo_u + t - n_cu
       {
