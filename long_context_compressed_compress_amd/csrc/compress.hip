@@ -154,36 +154,51 @@ __device__ __forceinline__ void compress_insert_body(const CompressArgs& a, int6
 #pragma unroll
   for (int k = 0; k < CH; ++k) { m[k] = -INFINITY; s[k] = 0.f; acc[k] = 0.f; }
 
+  // The window's state rows lie in at most two 256-position blocks (the window is at most 256 positions long):
+  // both table entries are loaded once, unconditionally (clamped), then the rows of a chunk of up to 8 window rows
+  // are all loaded before any is used, so a chunk costs one memory round trip. Rows of new positions come from the
+  // inputs, older ones from the state pages; a row that maps to no page reads row 0 and counts as zeros.
+  static_assert(WINDOW <= kBlock, "a window spans at most two blocks");
   constexpr int ROWS = (WINDOW + G - 1) / G;  // window rows per lane group
-  constexpr int UNROLL = ROWS < 8 ? ROWS : 8;  // c4a windows unroll fully; c128a windows in steps of 8 rows
-#pragma unroll UNROLL
-  for (int tt = 0; tt < ROWS; ++tt) {
-    const int t = grp + tt * G;
-    if (t >= WINDOW) break;
-    const int64_t pos = first + t;
-    const int role = t / RATIO;
-    // rows of new positions come from the inputs, older ones from the state pages
-    const bool from_new = pos >= start;
-    const int64_t r = from_new ? -1 : (st_bt ? raw_row(st_bt, a.state.bt_stride, a.state.n_phys, pos) : -1);
-    const bool have = from_new || r >= 0;
-    const TIn* xs = from_new ? kv_new + (cu_b + (pos - start)) * D : st_kv + (r >= 0 ? r : 0) * D;
-    const TIn* ls = from_new ? lg_new + ((cu_b + (pos - start)) * ROLES + role) * D
-                             : st_lg + ((r >= 0 ? r : 0) * ROLES + role) * D;
-    float x[CH], l[CH];
-    load_vec<TIn, CH>(xs + ch0, x);
-    load_vec<TIn, CH>(ls + ch0, l);
-    if (!have) {
-      zero_vec(x);
-      zero_vec(l);
+  constexpr int CHUNK = ROWS < 8 ? ROWS : 8;  // c4a windows in one chunk; c128a windows in chunks of 8 rows
+  const int bts = a.state.bt_stride;
+  const int32_t* bt_any = st_bt ? st_bt : a.state.block_table;  // a row that exists, read when b has none
+  const int64_t blk0 = first / kBlock;
+  const int32_t ph0 = bt_any[blk0 < bts ? blk0 : bts - 1];
+  const int32_t ph1 = bt_any[blk0 + 1 < bts ? blk0 + 1 : bts - 1];
+#pragma unroll 1
+  for (int t0 = 0; t0 < ROWS; t0 += CHUNK) {
+    float x[CHUNK][CH], l[CHUNK][CH];
+    bool have[CHUNK];
+#pragma unroll
+    for (int k = 0; k < CHUNK; ++k) {
+      const int t = grp + (t0 + k) * G;
+      const int64_t pos = first + t;
+      const int role = (t < WINDOW ? t : WINDOW - 1) / RATIO;
+      const bool from_new = pos >= start;
+      const int64_t blk = pos / kBlock;
+      const int32_t ph = blk == blk0 ? ph0 : ph1;
+      const bool mapped = st_bt != nullptr && blk < bts && ph >= 0 && ph < a.state.n_phys;
+      const int64_t r = mapped ? int64_t(ph) * kBlock + (pos - blk * kBlock) : 0;
+      have[k] = from_new || mapped;
+      const TIn* xs = from_new ? kv_new + (cu_b + (pos - start)) * D : st_kv + r * D;
+      const TIn* ls = from_new ? lg_new + ((cu_b + (pos - start)) * ROLES + role) * D : st_lg + (r * ROLES + role) * D;
+      load_vec<TIn, CH>(xs + ch0, x[k]);
+      load_vec<TIn, CH>(ls + ch0, l[k]);
     }
 #pragma unroll
-    for (int k = 0; k < CH; ++k) {
-      const float mn = fmaxf(m[k], l[k]);
-      const float f_old = __expf(m[k] - mn);  // exp(-inf) = 0 on the first row
-      const float f_new = __expf(l[k] - mn);
-      s[k] = s[k] * f_old + f_new;
-      acc[k] = acc[k] * f_old + f_new * x[k];
-      m[k] = mn;
+    for (int k = 0; k < CHUNK; ++k) {
+      if (grp + (t0 + k) * G >= WINDOW) break;
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const float xv = have[k] ? x[k][c] : 0.f, lv = have[k] ? l[k][c] : 0.f;
+        const float mn = fmaxf(m[c], lv);
+        const float f_old = __expf(m[c] - mn);  // exp(-inf) = 0 on the first row
+        const float f_new = __expf(lv - mn);
+        s[c] = s[c] * f_old + f_new;
+        acc[c] = acc[c] * f_old + f_new * xv;
+        m[c] = mn;
+      }
     }
   }
   // merge the G row groups (butterfly over the group bits of the lane id)
