@@ -824,19 +824,46 @@ __global__ void __launch_bounds__(256) attend_combine_kernel(AttendArgs a, Split
   const int h = (blockIdx.x % hq) * 4 + (threadIdx.x >> 6);
   const int d0 = (threadIdx.x & 63) * 8;
   if (q >= a.n_q) return;
+  // Loads go out a chunk of splits at a time (indices clamped, every load unconditional, surplus splits of a chunk
+  // masked afterwards), so a chunk costs one memory round trip: first the (max, sum) pairs of up to kMlChunk splits
+  // for the common maximum, then the partial outputs of kOChunk splits at a time. The sums are added in split
+  // order as in a plain loop.
+  constexpr int kMlChunk = 16, kOChunk = 8;
+  const int ns = sp.n_split;
+  const float2* ml = reinterpret_cast<const float2*>(part_ml);
+  auto slot_of = [&](int s) { return (int64_t(q) * ns + (s < ns ? s : ns - 1)) * a.n_heads + h; };
   float M = -INFINITY;
-  for (int s = 0; s < sp.n_split; ++s) M = fmaxf(M, part_ml[2 * ((int64_t(q) * sp.n_split + s) * a.n_heads + h)]);
+  for (int s0 = 0; s0 < ns; s0 += kMlChunk) {
+    float2 v[kMlChunk];
+#pragma unroll
+    for (int j = 0; j < kMlChunk; ++j) v[j] = ml[slot_of(s0 + j)];
+#pragma unroll
+    for (int j = 0; j < kMlChunk; ++j)
+      if (s0 + j < ns) M = fmaxf(M, v[j].x);
+  }
   float L = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < sp.n_split; ++s) {
-    const int64_t slot = (int64_t(q) * sp.n_split + s) * a.n_heads + h;
-    const float m = part_ml[2 * slot], l = part_ml[2 * slot + 1];
-    const float w = (m == -INFINITY) ? 0.f : __expf(m - M);
-    L += w * l;
-    const float4* src = reinterpret_cast<const float4*>(part_o + slot * kD + d0);
-    const float4 x0 = src[0], x1 = src[1];
-    acc[0] += w * x0.x; acc[1] += w * x0.y; acc[2] += w * x0.z; acc[3] += w * x0.w;
-    acc[4] += w * x1.x; acc[5] += w * x1.y; acc[6] += w * x1.z; acc[7] += w * x1.w;
+  for (int s0 = 0; s0 < ns; s0 += kOChunk) {
+    float2 v[kOChunk];
+    float4 x0[kOChunk], x1[kOChunk];
+#pragma unroll
+    for (int j = 0; j < kOChunk; ++j) {
+      const int64_t slot = slot_of(s0 + j);
+      v[j] = ml[slot];
+      const float4* src = reinterpret_cast<const float4*>(part_o + slot * kD + d0);
+      x0[j] = src[0];
+      x1[j] = src[1];
+    }
+#pragma unroll
+    for (int j = 0; j < kOChunk; ++j) {
+      // a surplus split of the last chunk gets weight 0 (its clamped loads read a real split, so the products are
+      // exact zeros); a branch here would let the compiler move the loads below it, one round trip each
+      const float m = v[j].x, l = v[j].y;
+      const float w = (s0 + j >= ns || m == -INFINITY) ? 0.f : __expf(m - M);
+      L += w * l;
+      acc[0] += w * x0[j].x; acc[1] += w * x0[j].y; acc[2] += w * x0[j].z; acc[3] += w * x0[j].w;
+      acc[4] += w * x1[j].x; acc[5] += w * x1[j].y; acc[6] += w * x1[j].z; acc[7] += w * x1[j].w;
+    }
   }
   const float inv = (L > 0.f) ? 1.f / L : 0.f;
 #pragma unroll
