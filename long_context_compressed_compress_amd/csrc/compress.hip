@@ -48,19 +48,31 @@ __device__ __forceinline__ void zero_vec(float (&v)[N]) {
   for (int k = 0; k < N; ++k) v[k] = 0.f;
 }
 
-// Largest b < batch with cu[b] <= row (cu non-decreasing, cu[0] = 0 <= row). The whole wave calls it for one row:
-// each lane tests one offset, so a batch of up to 64 sequences costs one memory round trip (a binary search
-// would cost one per step).
-__device__ __forceinline__ int find_seq(const int32_t* cu, int batch, int row) {
+// The sequence of an appended row: the largest b < batch with cu[b] <= row (cu non-decreasing, cu[0] = 0 <= row),
+// with its start position and first row. The whole wave calls it for one row: each lane tests one sequence and
+// loads its cu and start position together, so a batch of up to 64 sequences costs one memory round trip (a
+// binary search would cost one per step); the found lane's values are broadcast.
+__device__ __forceinline__ void find_seq_start(const int32_t* cu, const int32_t* start_pos, int batch, int row,
+                                               int& b_out, int& start_out, int& cu_out) {
   const int lane = threadIdx.x & 63;
-  int found = 0;
+  int found = 0, f_start = 0, f_cu = 0;
   for (int base = 0; base < batch; base += 64) {
     const int b = base + lane;
-    const uint64_t le = __ballot(b < batch && cu[b] <= row);
-    if (le) found = base + 63 - __clzll((unsigned long long)le);
+    const int bc = b < batch ? b : batch - 1;  // clamped, unconditional loads
+    const int c = cu[bc], sp = start_pos[bc];
+    asm volatile("" ::"v"(sp));  // keeps the start-position load beside the cu load (it would sink below the ballot)
+    const uint64_t le = __ballot(b < batch && c <= row);
+    if (le) {
+      const int src = 63 - __clzll((unsigned long long)le);
+      found = base + src;
+      f_start = __shfl(sp, src);
+      f_cu = __shfl(c, src);
+    }
     if (le != ~0ull) break;  // a lane of this chunk is past the row: later chunks are too
   }
-  return found;
+  b_out = found;
+  start_out = f_start;
+  cu_out = f_cu;
 }
 
 // The work of one 256-thread block of a compress_insert grid (block = its index within that grid).
@@ -85,18 +97,36 @@ __device__ __forceinline__ void compress_insert_body(const CompressArgs& a, int6
   if (gw < n_append) {
     // ---------------- append one raw token to the state pages
     const int row = int(gw);
-    const int b = find_seq(a.cu_new, a.batch, row);
+    int b, start_b, cu_b;
+    find_seq_start(a.cu_new, a.start_pos, a.batch, row, b, start_b, cu_b);
     if (b >= a.state.batch) return;
-    const int64_t pos = int64_t(a.start_pos[b]) + (row - a.cu_new[b]);
+    const int64_t pos = int64_t(start_b) + (row - cu_b);
     const int64_t r = raw_row(a.state.block_table + int64_t(b) * a.state.bt_stride, a.state.bt_stride, a.state.n_phys, pos);
     if (r < 0) return;
+    // every chunk of the kv and logit rows is loaded before any is stored: one round trip for the copy
     constexpr int V16_ROW = D * int(sizeof(TIn)) / 16;  // 16-byte chunks per D-row
+    constexpr int NKV = (V16_ROW + 63) / 64, NLG = (V16_ROW * ROLES + 63) / 64;
     const uint4* src_kv = reinterpret_cast<const uint4*>(kv_new + int64_t(row) * D);
     uint4* dst_kv = reinterpret_cast<uint4*>(st_kv + r * D);
-    for (int c = lane; c < V16_ROW; c += 64) dst_kv[c] = src_kv[c];
     const uint4* src_lg = reinterpret_cast<const uint4*>(lg_new + int64_t(row) * ROLES * D);
     uint4* dst_lg = reinterpret_cast<uint4*>(st_lg + r * ROLES * D);
-    for (int c = lane; c < V16_ROW * ROLES; c += 64) dst_lg[c] = src_lg[c];
+    uint4 vk[NKV], vl[NLG];
+#pragma unroll
+    for (int j = 0; j < NKV; ++j) {
+      const int c = lane + 64 * j;
+      vk[j] = src_kv[c < V16_ROW ? c : 0];
+    }
+#pragma unroll
+    for (int j = 0; j < NLG; ++j) {
+      const int c = lane + 64 * j;
+      vl[j] = src_lg[c < V16_ROW * ROLES ? c : 0];
+    }
+#pragma unroll
+    for (int j = 0; j < NKV; ++j)
+      if (lane + 64 * j < V16_ROW) dst_kv[lane + 64 * j] = vk[j];
+#pragma unroll
+    for (int j = 0; j < NLG; ++j)
+      if (lane + 64 * j < V16_ROW * ROLES) dst_lg[lane + 64 * j] = vl[j];
     return;
   }
 

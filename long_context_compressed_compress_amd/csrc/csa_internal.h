@@ -94,13 +94,14 @@ __host__ __device__ __forceinline__ int64_t num_eligible(int64_t p, int ratio, i
   return n >= window ? (n - window) / ratio + 1 : 0;
 }
 
-// Page row of entry i of block-table row `bt`, or -1 when the table does not map it.
+// Page row of entry i of block-table row `bt`, or -1 when the table does not map it. The table load is
+// unconditional (index clamped into the row, which is at least one block wide), so it can be issued early and
+// overlap other loads: a load inside a branch is waited for before the branch closes.
 __device__ __forceinline__ int64_t entry_row(const int32_t* bt, int bt_stride, int n_phys, int64_t i, int per_block) {
   const int64_t blk = i / per_block;
-  if (i < 0 || blk >= bt_stride) return -1;
-  const int32_t phys = bt[blk];
-  if (phys < 0 || phys >= n_phys) return -1;
-  return int64_t(phys) * per_block + (i - blk * per_block);
+  const bool in = i >= 0 && blk < bt_stride;
+  const int32_t phys = bt[in ? blk : 0];
+  return (in && phys >= 0 && phys < n_phys) ? int64_t(phys) * per_block + (i - blk * per_block) : -1;
 }
 
 __device__ __forceinline__ int64_t raw_row(const int32_t* bt, int bt_stride, int n_phys, int64_t pos) {
