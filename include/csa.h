@@ -296,7 +296,8 @@ csa_status_t csa_inv_rope(int32_t n_q, int32_t n_heads, int32_t dim, int32_t rop
  *     a position whose block is unmapped is skipped.
  *   q_in, q_out [n_tok][n_heads][D] and kv_in [n_tok][D] in q_dtype; D = swa->dim. Type pairs:
  *   (CSA_F32 q, CSA_F32 window) or (CSA_BF16 q, CSA_BF16 or CSA_FP8_E4M3 window). n_heads in [1, 128].
- *   q_out must not alias q_in. Caller-owned buffers; nothing is allocated.
+ *   q_out must not alias q_in and must be 16-byte aligned (CSA_ERR_INVALID_ARG otherwise). Caller-owned
+ *   buffers; nothing is allocated.
  * ------------------------------------------------------------------------------------------- */
 csa_status_t csa_prepare_qk(int32_t n_tok, int32_t n_heads, const int32_t* tok_seq, const int32_t* tok_pos,
                             const void* q_in, csa_dtype_t q_dtype, const float* q_gamma, float rms_eps,

@@ -399,7 +399,7 @@ csa_status_t csa_prepare_qk(int32_t n_tok, int32_t n_heads, const int32_t* tok_s
   if (rope_dims > 0 && (!rope_cs || rope_rows < 1)) return CSA_ERR_INVALID_ARG;
   if (!(rms_eps >= 0.f) || !isfinite(rms_eps)) return CSA_ERR_INVALID_ARG;
   if (n_tok == 0) return CSA_OK;
-  if (!tok_seq || !tok_pos || !q_in || !q_out || !q_gamma || !kv_in) return CSA_ERR_INVALID_ARG;
+  if (!tok_seq || !tok_pos || !q_in || !q_out || !q_gamma || !kv_in || !aligned(q_out, 16)) return CSA_ERR_INVALID_ARG;
   csa::PrepareArgs a{n_tok, n_heads, tok_seq, tok_pos, q_in, q_out, q_gamma, rms_eps, kv_in, *swa, rope_dims,
                      rope_cs, rope_rows};
   return hip_status(csa::launch_prepare_qk(a, q_dtype, stream));

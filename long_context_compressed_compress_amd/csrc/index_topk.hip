@@ -1017,12 +1017,16 @@ __global__ void __launch_bounds__(NT) select_kernel(IndexArgs a, Workspace ws) {
   // candidates of a chunk with one LDS atomic, at offsets taken from the per-step ballots.
   const int lane = tid & 63;
   const uint64_t below = (1ull << lane) - 1ull;
+  // key positions of a query fit 32 bits (fewer than 2^29 entries): 32-bit byte offsets from the query's keys keep
+  // the 16 addresses of a chunk cheap enough that all its loads go out before the first is used
+  const char* keys_b = reinterpret_cast<const char*>(keys_q);
+  const uint32_t n_el32 = uint32_t(n_elig);
   for (int64_t base = 0; base < (pre ? 0 : n_elig); base += int64_t(NT) * kSelKeysPerThread) {
     uint32_t key[kSelKeysPerThread];
 #pragma unroll
     for (int j = 0; j < kSelKeysPerThread; ++j) {
-      const int64_t i = base + tid + int64_t(NT) * j;
-      key[j] = keys_q[i < n_elig ? i : 0];  // clamped, unconditional load
+      const uint32_t i = uint32_t(base) + uint32_t(tid + NT * j);
+      key[j] = *reinterpret_cast<const uint32_t*>(keys_b + ((i < n_el32 ? i : 0u) << 2));  // clamped, unconditional
     }
     uint32_t n_sure_w = 0, n_cand_w = 0, cand_off[kSelKeysPerThread];
     uint64_t cand_m[kSelKeysPerThread];

@@ -199,7 +199,7 @@ def test_prepare_qk_validation(L):
                  None)
     for bad in (dict(h=0), dict(h=129), dict(n=-1), dict(seq=None), dict(q=None), dict(g=None), dict(kv=None),
                 dict(out=None), dict(swa=None), dict(qd=csa.F32), dict(r=3), dict(r=1024), dict(cs=None),
-                dict(rows=0), dict(eps=-1.0), dict(eps=float("nan"))):
+                dict(rows=0), dict(eps=-1.0), dict(eps=float("nan")), dict(out=FAKE + 8)):
         assert call(**bad) == INVALID, bad
     assert call(swa=_raw(dim=512, roles=2, dtype=csa.BF16)) == INVALID       # a state descriptor, not a window
     assert call(swa=_raw(dim=100, roles=0, dtype=csa.BF16)) == INVALID
