@@ -633,33 +633,36 @@ __global__ void __launch_bounds__(256, 2) score_lt_kernel(IndexArgs a, Workspace
     uint32_t land_sc[AHEAD] = {};
 #pragma unroll
     for (int s = 0; s < AHEAD; ++s)
-      if (s < n_mine) lt_fetch<KF>(a, pg_phys[wave + 4 * s], lane, land[s], land_sc[s]);
-    for (int j0 = 0; j0 < n_mine; j0 += AHEAD) {
+      lt_fetch<KF>(a, pg_phys[wave + 4 * (s < n_mine ? s : n_mine - 1)], lane, land[s], land_sc[s]);
+    // The at most kLtPages / 4 steps of this wave are unrolled into straight-line code that a step leaves by a
+    // uniform break once the wave's pages are done, and every prefetch is issued (past the last page it re-reads
+    // that page). The compiler then knows at every step which loads are older than the other buffer's and waits
+    // only for them; in a loop (or with the body or the prefetch under a condition) it waited for both buffers at
+    // the top of a step: one page in flight instead of two.
 #pragma unroll
-      for (int s = 0; s < AHEAD; ++s) {
-        const int j = j0 + s;
-        if (j < n_mine) {  // uniform over the wave
-          // stage page j: byte offset 16 * (lane + 64 i) of the page is row (lane + 64 i) / (RAW_ROW / 16)
+    for (int j = 0; j < kLtPages / 4; ++j) {
+      if (j >= n_mine) break;  // uniform over the wave
+      const int s = j % AHEAD;
+      // stage page j: byte offset 16 * (lane + 64 i) of the page is row (lane + 64 i) / (RAW_ROW / 16)
 #pragma unroll
-          for (int i = 0; i < L::LOADS; ++i) {
-            const int chunk = lane + 64 * i;
-            const int row = chunk / (L::RAW_ROW / 16), off = (chunk % (L::RAW_ROW / 16)) * 16;
-            *reinterpret_cast<u32x4*>(st + row * L::ROW + off) = land[s][i];
-          }
-          if (KF != 0) scale_s[wave][lane] = land_sc[s];
-          const int32_t phys_j = pg_phys[wave + 4 * j];
-          if (j + AHEAD < n_mine) lt_fetch<KF>(a, pg_phys[wave + 4 * (j + AHEAD)], lane, land[s], land_sc[s]);
-          __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the stage is written before this wave reads it
-          __builtin_amdgcn_wave_barrier();
-          const uint32_t key = lt_score_page<KF, HT>(st, scale_s[wave], qa, wv, col, kg);
-          const int64_t e = (first + 4 * int64_t(j)) * E + lane;
-          if (e < n_elig) {
-            const uint32_t k2 = phys_j >= 0 ? key : 0u;
-            keys_q[e] = k2;
-            const uint32_t bin = k2 >> (32 - kHistBits);
-            atomicAdd(&hist_s[bin >> 1], 1u << ((bin & 1u) * 16));
-          }
-        }
+      for (int i = 0; i < L::LOADS; ++i) {
+        const int chunk = lane + 64 * i;
+        const int row = chunk / (L::RAW_ROW / 16), off = (chunk % (L::RAW_ROW / 16)) * 16;
+        *reinterpret_cast<u32x4*>(st + row * L::ROW + off) = land[s][i];
+      }
+      if (KF != 0) scale_s[wave][lane] = land_sc[s];
+      const int32_t phys_j = pg_phys[wave + 4 * j];
+      const int jn = j + AHEAD < n_mine ? j + AHEAD : n_mine - 1;
+      lt_fetch<KF>(a, pg_phys[wave + 4 * jn], lane, land[s], land_sc[s]);
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the stage is written before this wave reads it
+      __builtin_amdgcn_wave_barrier();
+      const uint32_t key = lt_score_page<KF, HT>(st, scale_s[wave], qa, wv, col, kg);
+      const int64_t e = (first + 4 * int64_t(j)) * E + lane;
+      if (e < n_elig) {
+        const uint32_t k2 = phys_j >= 0 ? key : 0u;
+        keys_q[e] = k2;
+        const uint32_t bin = k2 >> (32 - kHistBits);
+        atomicAdd(&hist_s[bin >> 1], 1u << ((bin & 1u) * 16));
       }
     }
   }
