@@ -171,7 +171,9 @@ STEP_MODES = {"eager": "eager launches on one stream with an event between stage
               "graph_2stream": "one HIP graph per layer, main-cache compress_insert on a second stream beside the "
                                "indexer pipeline",
               "graph_partition": "one HIP graph per layer, the indexer pipeline (its compress_insert, score, select) on "
-                                 "a second stream beside the main-cache compress_insert"}
+                                 "a second stream beside the main-cache compress_insert",
+              "graph_fused": "one HIP graph per layer, every call on one stream, both caches' compress_insert inside "
+                             "the index-score launch (csa_compress_index_score)"}
 
 
 def capture_graphs(torch, layers, fn):
@@ -221,16 +223,17 @@ def replay_percentiles(torch, graphs, steps):
 LAST_PERCENTILES = {}
 
 
-def best_graph_mode(torch, layers, steps, warmup, sequential, two_stream, partitioned=None):
+def best_graph_mode(torch, layers, steps, warmup, sequential, two_stream, partitioned=None, fused=None):
     """Time the step as one HIP graph per layer in each stream arrangement given (all on one stream; main-cache
-    compress on a second stream; the indexer pipeline on a second stream); returns (ms of the fastest, its name, ms
-    of each). The per-step percentiles of the fastest are left in LAST_PERCENTILES. With --eager-only (profiler
+    compress on a second stream; the indexer pipeline on a second stream; all on one stream with the compress inside
+    the index-score launch); returns (ms of the fastest, its name, ms of each). The per-step percentiles of the fastest are left in LAST_PERCENTILES. With --eager-only (profiler
     runs) no graph is built and (None, "eager", {}) comes back."""
     LAST_PERCENTILES.clear()
     if EAGER_ONLY:
         return None, "eager", {}
     modes, kept = {}, {}
-    for name, fn in (("graph", sequential), ("graph_2stream", two_stream), ("graph_partition", partitioned)):
+    for name, fn in (("graph", sequential), ("graph_2stream", two_stream), ("graph_partition", partitioned),
+                     ("graph_fused", fused)):
         if fn is None:
             continue
         graphs = capture_graphs(torch, layers, fn)
@@ -242,12 +245,13 @@ def best_graph_mode(torch, layers, steps, warmup, sequential, two_stream, partit
     return modes[best], best, modes
 
 
-def partition_modes(torch, layers, steps, warmup, prepare, main_compress, index_path, attend, pair=None):
+def partition_modes(torch, layers, steps, warmup, prepare, main_compress, index_path, attend, pair=None, fused=None):
     """The step with the query / window-key preparation in front (csa_prepare_qk), captured two ways: every call on
     one stream (the indexer and main compress as one paired launch when `pair` is given), and the pages' two-stream
     partition -- on a c4a layer the indexer pipeline (its compress, score, select) on a second stream beside main
     compress + window insert, on a c128a layer (index_path None) main compress beside the window insert; attention
-    joins. Returns ms per step of each, or {} without graphs."""
+    joins; with `fused` (both compresses, score and select in csa_compress_index_score + csa_index_select) also that
+    on one stream. Returns ms per step of each, or {} without graphs."""
     if EAGER_ONLY:
         return {}
     side = torch.cuda.Stream()
@@ -276,8 +280,16 @@ def partition_modes(torch, layers, steps, warmup, prepare, main_compress, index_
         cur.wait_stream(side)
         attend(ly)
 
+    def single_fused(ly):
+        prepare(ly)
+        fused(ly)
+        attend(ly)
+
     out = {}
-    for name, fn in (("single_stream", single), ("partition_2stream", split)):
+    for name, fn in (("single_stream", single), ("partition_2stream", split),
+                     ("single_stream_fused", single_fused if fused is not None else None)):
+        if fn is None:
+            continue
         graphs = capture_graphs(torch, layers, fn)
         out[name] = time_graphs(torch, graphs, steps, warmup) / steps
         del graphs
@@ -389,11 +401,16 @@ def run_gpu(args, lens):
                     csa.index_select(ly.icache, ly.seq, ly.pos, max_elig, K_TOP, topk, ws)),
         lambda ly: csa.attend(ly.cache, ly.swa, SWA, ly.seq, ly.pos, ly.q, topk, max_elig, scale, True, rope_main, out,
                               workspace=att_ws))
+    fused_index = lambda ly: (
+        csa.compress_index_score(ly.cache, ly.state, ly.kv1, ly.lg1, ly.gamma, rope_main, ly.icache, ly.istate, ly.ikv1,
+                                 ly.ilg1, ly.igamma, rope_idx, ly.pos, ly.cu1, 1e-6, ly.seq, ly.pos, max_elig,
+                                 ly.q_idx, ly.head_w, csa.SCORE_WRELU, K_TOP, ws),
+        csa.index_select(ly.icache, ly.seq, ly.pos, max_elig, K_TOP, topk, ws))
     wall0 = time.time()
     fn = overlapped(torch, side, *parts)
     fn_p = partitioned(torch, torch.cuda.Stream(), *parts)
     total_ms, mode, modes = best_graph_mode(torch, layers, args.steps, args.warmup, lambda ly: step(ly, None), fn,
-                                            fn_p)
+                                            fn_p, lambda ly: (fused_index(ly), parts[2](ly)))
     wall = time.time() - wall0
     pct = dict(LAST_PERCENTILES)
     for ly in layers:
@@ -412,7 +429,8 @@ def run_gpu(args, lens):
                               workspace=att_ws),
         pair=lambda ly: csa.compress_insert_pair(ly.cache, ly.state, ly.kv1, ly.lg1, ly.gamma, rope_main, ly.icache,
                                                  ly.istate, ly.ikv1, ly.ilg1, ly.igamma, rope_idx, ly.pos, ly.cu1, 1e-6,
-                                                 1))
+                                                 1),
+        fused=fused_index)
     epilogue = time_output_epilogue(torch, csa, layers, step, out, topk, max_elig, scale, rope_main, att_ws)
     epilogue["step_with_prepare_ms"] = f4
     epilogue["step_us_percentiles"] = pct
@@ -625,10 +643,15 @@ def run_c4(args, torch, csa, fp4_idx=False):
                     csa.index_select(ly.icache, ly.seq, ly.pos, max_elig, K_TOP, topk, ws)),
         lambda ly: csa.attend(ly.cache, ly.swa, SWA, ly.seq, ly.pos, ly.q, topk, max_elig, 1.0 / math.sqrt(D), True,
                               rope, out, workspace=att_ws))
+    fused_index = lambda ly: (
+        csa.compress_index_score(ly.cache, ly.state, ly.kv1, ly.lg1, ly.gamma, rope, ly.icache, ly.istate, ly.ikv1,
+                                 ly.ilg1, ly.igamma, rope, ly.pos, ly.cu1, 1e-6, ly.seq, ly.pos, max_elig, ly.q_idx,
+                                 ly.head_w, csa.SCORE_WRELU, K_TOP, ws),
+        csa.index_select(ly.icache, ly.seq, ly.pos, max_elig, K_TOP, topk, ws))
     fn = overlapped(torch, side, *parts)
     fn_p = partitioned(torch, torch.cuda.Stream(), *parts)
     total_ms, mode, modes = best_graph_mode(torch, layers, args.steps, args.warmup, lambda ly: step(ly, None), fn,
-                                            fn_p)
+                                            fn_p, lambda ly: (fused_index(ly), parts[2](ly)))
     total_ms = eager_ms if total_ms is None else total_ms
     pct = dict(LAST_PERCENTILES)
     for ly in layers:
@@ -644,7 +667,8 @@ def run_c4(args, torch, csa, fp4_idx=False):
         lambda ly: csa.attend(ly.cache, ly.swa, SWA, ly.seq, ly.pos, ly.q, topk, max_elig, 1.0 / math.sqrt(D), True,
                               rope, out, workspace=att_ws),
         pair=lambda ly: csa.compress_insert_pair(ly.cache, ly.state, ly.kv1, ly.lg1, ly.gamma, rope, ly.icache,
-                                                 ly.istate, ly.ikv1, ly.ilg1, ly.igamma, rope, ly.pos, ly.cu1, 1e-6, 1))
+                                                 ly.istate, ly.ikv1, ly.ilg1, ly.igamma, rope, ly.pos, ly.cu1, 1e-6, 1),
+        fused=fused_index)
     sb, kb, ab = (B * x for x in _decode_bytes(max_elig, P, D + 4, row_i + 4, K_TOP, True))
     del layers, pool_m, pool_ms, pool_i, pool_is, ws
     torch.cuda.empty_cache()

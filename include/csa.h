@@ -201,6 +201,35 @@ csa_status_t csa_index_select(const csa_cache_t* idx_cache, int32_t n_q, const i
                               size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * csa_compress_index_score -- a c4a decode step's csa_compress_insert_pair (main cache a, indexer cache b)
+ * followed by csa_index_score over cache b, in one launch where the configuration allows.
+ * [P1] "GPU Compute Saturation" (the small kernels of a decode step fused so each launch's fixed latency is
+ * paid once) / [P2] "3.2 內核": the indexer-cache compressor feeds the indexer, and the decode step's
+ * latency is the sum of its launches. Arguments: those of csa_compress_insert_pair, then those of
+ * csa_index_score with idx_cache = cache_b. Decode form only: every sequence appends exactly one token
+ * (total_new == batch, max_new_per_seq == 1) and query q is sequence q's new token (n_q == batch, and on
+ * the device q_seq[q] == q, q_pos[q] == start_pos[q]); otherwise CSA_ERR_INVALID_ARG for the host-checked
+ * parts, and unspecified (memory-safe) results for the device-side part. Results are those of the two calls
+ * in turn. A c4a main cache of dim 512 (bf16 or fp8) with an indexer cache of dim 128 (bf16, fp8 or MXFP4,
+ * with the main cache's dtype or an fp8 main cache), bf16 inputs and a WRELU score of 64 heads over fewer
+ * than 256 queries runs as one launch: the workgroup that scores query q's last page first runs sequence q's
+ * compress units (main and indexer, append and entry), so the entry the query's own token completes is in
+ * that page before it is read; anything else runs as the two launches. Validation: both argument sets as for
+ * the two calls, before any HIP call. The workspace rules are those of csa_index_score.
+ * ------------------------------------------------------------------------------------------- */
+csa_status_t csa_compress_index_score(const csa_cache_t* cache_a, const csa_raw_t* state_a, const void* kv_a,
+                                      const void* logit_a, const float* gamma_a, const float* rope_cs_a,
+                                      int32_t rope_rows_a, const csa_cache_t* cache_b, const csa_raw_t* state_b,
+                                      const void* kv_b, const void* logit_b, const float* gamma_b,
+                                      const float* rope_cs_b, int32_t rope_rows_b, int32_t batch,
+                                      const int32_t* start_pos, const int32_t* cu_new, int32_t total_new,
+                                      int32_t max_new_per_seq, float rms_eps, int32_t n_q, const int32_t* q_seq,
+                                      const int32_t* q_pos, int64_t max_elig, const void* q_idx,
+                                      csa_dtype_t q_dtype, int32_t n_heads, const float* head_w,
+                                      csa_score_t mode, int32_t k, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * csa_index_topk_noalloc -- csa_index_topk for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. Same arguments, meaning and
  * results as csa_index_topk, without the workspace: the score keys, histograms, candidate list and

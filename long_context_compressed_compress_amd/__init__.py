@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
             "csa_compress_insert": (I32, [CP, RP, I32, P, P, I32, I32, P, P, P, F, P, I32, P, I32, P, P]),
             "csa_compress_insert_pair": (I32, [CP, RP, P, P, P, P, I32, CP, RP, P, P, P, P, I32, I32, P, P, I32, I32, F,
                                                P]),
+            "csa_compress_index_score": (I32, [CP, RP, P, P, P, P, I32, CP, RP, P, P, P, P, I32, I32, P, P, I32, I32, F,
+                                               I32, P, P, I64, P, I32, I32, P, I32, I32, P, SZ, P]),
             "csa_index_topk_workspace": (SZ, [I32, I64, I32, I32]),
             "csa_index_topk": (I32, [CP, I32, P, P, I64, P, I32, I32, P, I32, I32, P, P, P, P, SZ, P]),
             "csa_index_workspace_clear": (I32, [P, SZ, I32, P]),
@@ -186,6 +188,24 @@ def compress_insert_pair(cache_a: Cache, state_a: Raw, kv_a: torch.Tensor, logit
         ctypes.byref(ca), ctypes.byref(sa), _ptr(kv_a), _ptr(logit_a), _ptr(gamma_a), _ptr(rope_a), rope_a.shape[0],
         ctypes.byref(cb), ctypes.byref(sb), _ptr(kv_b), _ptr(logit_b), _ptr(gamma_b), _ptr(rope_b), rope_b.shape[0],
         start_pos.shape[0], _ptr(start_pos), _ptr(cu_new), kv_a.shape[0], max_new_per_seq, rms_eps, _stream(stream)))
+
+
+def compress_index_score(cache_a: Cache, state_a: Raw, kv_a: torch.Tensor, logit_a: torch.Tensor,
+                         gamma_a: torch.Tensor, rope_a: torch.Tensor, cache_b: Cache, state_b: Raw,
+                         kv_b: torch.Tensor, logit_b: torch.Tensor, gamma_b: torch.Tensor, rope_b: torch.Tensor,
+                         start_pos: torch.Tensor, cu_new: torch.Tensor, rms_eps: float, q_seq: torch.Tensor,
+                         q_pos: torch.Tensor, max_elig: int, q_idx: torch.Tensor, head_w: Optional[torch.Tensor],
+                         mode: int, k: int, workspace: torch.Tensor, stream=None) -> None:
+    """A decode step's compress_insert_pair (main cache a, indexer cache b; one new token per sequence) followed by
+    index_score over cache b for query q = sequence q's token, in one launch where the configuration allows."""
+    ca, sa, cb, sb = cache_a.desc(), state_a.desc(), cache_b.desc(), state_b.desc()
+    n_q, n_heads = q_idx.shape[0], q_idx.shape[1]
+    _check("csa_compress_index_score", lib().csa_compress_index_score(
+        ctypes.byref(ca), ctypes.byref(sa), _ptr(kv_a), _ptr(logit_a), _ptr(gamma_a), _ptr(rope_a), rope_a.shape[0],
+        ctypes.byref(cb), ctypes.byref(sb), _ptr(kv_b), _ptr(logit_b), _ptr(gamma_b), _ptr(rope_b), rope_b.shape[0],
+        start_pos.shape[0], _ptr(start_pos), _ptr(cu_new), kv_a.shape[0], 1, rms_eps, n_q, _ptr(q_seq), _ptr(q_pos),
+        max_elig, _ptr(q_idx), dtype_code(q_idx), n_heads, _ptr(head_w), mode, k, _ptr(workspace), workspace.numel(),
+        _stream(stream)))
 
 
 def index_topk_workspace(n_q: int, max_elig: int, k: int, n_heads: int) -> int:

@@ -198,6 +198,36 @@ csa_status_t csa_index_score(const csa_cache_t* idx_cache, int32_t n_q, const in
   return hip_status(csa::launch_index_score(a, stream));
 }
 
+csa_status_t csa_compress_index_score(const csa_cache_t* cache_a, const csa_raw_t* state_a, const void* kv_a,
+                                      const void* logit_a, const float* gamma_a, const float* rope_cs_a,
+                                      int32_t rope_rows_a, const csa_cache_t* cache_b, const csa_raw_t* state_b,
+                                      const void* kv_b, const void* logit_b, const float* gamma_b,
+                                      const float* rope_cs_b, int32_t rope_rows_b, int32_t batch,
+                                      const int32_t* start_pos, const int32_t* cu_new, int32_t total_new,
+                                      int32_t max_new_per_seq, float rms_eps, int32_t n_q, const int32_t* q_seq,
+                                      const int32_t* q_pos, int64_t max_elig, const void* q_idx,
+                                      csa_dtype_t q_dtype, int32_t n_heads, const float* head_w,
+                                      csa_score_t mode, int32_t k, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+  csa::CompressArgs a, b;
+  csa_status_t st = compress_args(cache_a, state_a, batch, start_pos, cu_new, total_new, max_new_per_seq, kv_a,
+                                  logit_a, gamma_a, rms_eps, rope_cs_a, rope_rows_a, nullptr, 0, nullptr, &a);
+  if (st != CSA_OK) return st;
+  st = compress_args(cache_b, state_b, batch, start_pos, cu_new, total_new, max_new_per_seq, kv_b, logit_b, gamma_b,
+                     rms_eps, rope_cs_b, rope_rows_b, nullptr, 0, nullptr, &b);
+  if (st != CSA_OK) return st;
+  st = index_check(cache_b, n_q, q_seq, q_pos, max_elig, k, workspace, workspace_bytes);
+  if (st != CSA_OK) return st;
+  st = score_check(cache_b, n_q, q_idx, q_dtype, n_heads, head_w, mode);
+  if (st != CSA_OK) return st;
+  // the decode form: one new token per sequence, query q = sequence q's token
+  if (n_q != batch || total_new != batch || (batch > 0 && max_new_per_seq != 1)) return CSA_ERR_INVALID_ARG;
+  if (batch == 0) return CSA_OK;
+  csa::IndexArgs ia{*cache_b, n_q, q_seq, q_pos, max_elig, q_idx, q_dtype, n_heads, head_w, mode, k,
+                    nullptr, nullptr, nullptr, workspace};
+  return hip_status(csa::launch_compress_index_score(a, b, ia, stream));
+}
+
 csa_status_t csa_index_select(const csa_cache_t* idx_cache, int32_t n_q, const int32_t* q_seq, const int32_t* q_pos,
                               int64_t max_elig, int32_t k, int32_t* out_idx, int32_t* out_count, float* out_scores,
                               void* workspace, size_t workspace_bytes, hipStream_t stream) {

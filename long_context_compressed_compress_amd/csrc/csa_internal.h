@@ -154,6 +154,13 @@ bool index_supported(const csa_cache_t& c, csa_dtype_t q_dtype, int n_heads, csa
 hipError_t launch_index_clear(void* ws, int n_q, hipStream_t stream);
 hipError_t launch_index_score(const IndexArgs& a, hipStream_t stream);
 hipError_t launch_index_select(const IndexArgs& a, hipStream_t stream);
+// The decode step's compress_insert of a c4a main cache and its indexer cache, done inside the index-score launch
+// where the configuration allows (else the two launches in turn); one new token per sequence, query q = sequence q.
+struct FusedCompress {
+  CompressArgs main, idx;
+};
+hipError_t launch_compress_index_score(const CompressArgs& main, const CompressArgs& idx, const IndexArgs& a,
+                                       hipStream_t stream);
 
 struct AttendArgs {
   csa_cache_t cache;

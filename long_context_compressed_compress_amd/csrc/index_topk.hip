@@ -24,7 +24,7 @@
 //                   once (csa_index_workspace_clear).
 // The chosen set is unique (score order plus index order is total), so the result does not depend
 // on how work is split or on the order of atomics.
-#include "csa_internal.h"
+#include "compress_unit.h"
 
 namespace csa {
 namespace {
@@ -211,10 +211,27 @@ __device__ __forceinline__ uint32_t score_page(const PageBuf<KF>& b, const bf16x
   return mine;
 }
 
+// The decode step's compress_insert of both caches run inside the index-score launch (csa_compress_index_score):
+// one new token per sequence, query q being sequence q's token. The workgroup that scores query q's last page
+// (run 0 when the query has none) first runs sequence q's four compress units, one per wave (indexer append and
+// entry, main append and entry), then a barrier: the entry the query's own token completes is in that page before
+// any wave of the workgroup reads it, and no other workgroup reads that page. OA: main cache output type
+// (1 bf16, 2 fp8); the indexer output type follows the page format KF (bf16, fp8, MXFP4).
+template <int KF, int OA>
+__device__ __forceinline__ void fused_compress(const FusedCompress& fc, int b) {
+  constexpr int OB = KF == 0 ? 1 : (KF == 1 ? 2 : 3);
+  switch (threadIdx.x >> 6) {  // wave-uniform
+    case 0: compress_unit<uint16_t, OB, 128, 4, 8>(fc.idx, b); break;
+    case 1: compress_unit<uint16_t, OB, 128, 4, 8>(fc.idx, int64_t(fc.idx.total_new) + b); break;
+    case 2: compress_unit<uint16_t, OA, 512, 4, 8>(fc.main, b); break;
+    default: compress_unit<uint16_t, OA, 512, 4, 8>(fc.main, int64_t(fc.main.total_new) + b); break;
+  }
+}
+
 // Decode score for MXFP4 pages: one workgroup per (query, run of pages), blockIdx.x = run. An fp4 row is 64 bytes,
 // so the operand-layout loads of a 16-entry tile read whole 128-byte lines and no LDS stage is needed.
-template <int KF, int HT>
-__global__ void __launch_bounds__(256, 2) score_mfma_kernel(IndexArgs a, Workspace ws, int run) {
+template <int KF, int HT, int OA = 0>
+__global__ void __launch_bounds__(256, 2) score_mfma_kernel(IndexArgs a, Workspace ws, int run, FusedCompress fc) {
   constexpr int DIM = 128;
   constexpr int E = 64;
   __shared__ uint32_t hist_s[kHistBins];
@@ -224,6 +241,12 @@ __global__ void __launch_bounds__(256, 2) score_mfma_kernel(IndexArgs a, Workspa
   const int64_t n_elig = query_elig(a, q, &seq);
   const int64_t n_pages = (n_elig + E - 1) / E;
   const int64_t pg_begin = int64_t(blockIdx.x) * run;
+  if constexpr (OA != 0) {
+    if (int64_t(blockIdx.x) == (n_pages > 0 ? (n_pages - 1) / run : 0)) {  // uniform per block
+      fused_compress<KF, OA>(fc, q);
+      __syncthreads();
+    }
+  }
   if (pg_begin >= n_pages) return;  // uniform per block
   const int64_t pg_end = min(n_pages, pg_begin + run);
   for (int b = threadIdx.x; b < kHistBins; b += blockDim.x) hist_s[b] = 0u;
@@ -579,8 +602,8 @@ __device__ __forceinline__ uint32_t lt_score_page(const char* st, const uint32_t
   return score_key(mine_f);
 }
 
-template <int KF, int HT>
-__global__ void __launch_bounds__(256, 2) score_lt_kernel(IndexArgs a, Workspace ws) {
+template <int KF, int HT, int OA = 0>
+__global__ void __launch_bounds__(256, 2) score_lt_kernel(IndexArgs a, Workspace ws, FusedCompress fc) {
   using L = LtPage<KF>;
   constexpr int DIM = 128;
   constexpr int E = 64;
@@ -594,6 +617,12 @@ __global__ void __launch_bounds__(256, 2) score_lt_kernel(IndexArgs a, Workspace
   const int64_t n_elig = query_elig(a, q, &seq);
   const int64_t n_pages = (n_elig + E - 1) / E;
   const int64_t pg_begin = int64_t(blockIdx.x) * kLtPages;
+  if constexpr (OA != 0) {
+    if (int64_t(blockIdx.x) == (n_pages > 0 ? (n_pages - 1) / kLtPages : 0)) {  // uniform per block
+      fused_compress<KF, OA>(fc, q);
+      __syncthreads();
+    }
+  }
   if (pg_begin >= n_pages) return;  // uniform per block
   const int64_t pg_end = min(n_pages, pg_begin + kLtPages);
   for (int b = threadIdx.x; b < kHistBins / 2; b += blockDim.x) hist_s[b] = 0u;
@@ -1222,14 +1251,14 @@ void launch_score_shared(int kf, dim3 grid, const IndexArgs& a, const Workspace&
 
 template <int HT>
 void launch_score_fp4(dim3 grid, const IndexArgs& a, const Workspace& ws, int run, hipStream_t stream) {
-  hipLaunchKernelGGL((score_mfma_kernel<2, HT>), grid, dim3(256), 0, stream, a, ws, run);
+  hipLaunchKernelGGL((score_mfma_kernel<2, HT>), grid, dim3(256), 0, stream, a, ws, run, FusedCompress{});
 }
 
 template <int HT>
 void launch_score_lt(int kf, dim3 grid, const IndexArgs& a, const Workspace& ws, hipStream_t stream) {
-  if (kf == 2) hipLaunchKernelGGL((score_lt_kernel<2, HT>), grid, dim3(256), 0, stream, a, ws);
-  else if (kf == 1) hipLaunchKernelGGL((score_lt_kernel<1, HT>), grid, dim3(256), 0, stream, a, ws);
-  else hipLaunchKernelGGL((score_lt_kernel<0, HT>), grid, dim3(256), 0, stream, a, ws);
+  if (kf == 2) hipLaunchKernelGGL((score_lt_kernel<2, HT>), grid, dim3(256), 0, stream, a, ws, FusedCompress{});
+  else if (kf == 1) hipLaunchKernelGGL((score_lt_kernel<1, HT>), grid, dim3(256), 0, stream, a, ws, FusedCompress{});
+  else hipLaunchKernelGGL((score_lt_kernel<0, HT>), grid, dim3(256), 0, stream, a, ws, FusedCompress{});
 }
 
 hipError_t launch_index_score(const IndexArgs& a, hipStream_t stream) {
@@ -1277,6 +1306,41 @@ hipError_t launch_index_score(const IndexArgs& a, hipStream_t stream) {
     if (a.cache.dtype == CSA_F32) hipLaunchKernelGGL((score_valu_kernel<0>), grid, dim3(256), lds, stream, a, ws);
     else if (a.cache.dtype == CSA_BF16) hipLaunchKernelGGL((score_valu_kernel<1>), grid, dim3(256), lds, stream, a, ws);
     else hipLaunchKernelGGL((score_valu_kernel<2>), grid, dim3(256), lds, stream, a, ws);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_compress_index_score(const CompressArgs& main, const CompressArgs& idx, const IndexArgs& a,
+                                       hipStream_t stream) {
+  // fused: the paired-compress configurations (c4a main D 512 bf16 / fp8 + indexer D 128 bf16 / fp8 / MXFP4, bf16
+  // inputs) with the decode score path of 64 indexer heads; anything else runs the two launches one after the other
+  const bool main_ok = main.state.dtype == CSA_BF16 && main.cache.ratio == 4 && main.cache.dim == 512 &&
+                       (main.cache.dtype == CSA_BF16 || main.cache.dtype == CSA_FP8_E4M3);
+  const bool idx_ok = idx.state.dtype == CSA_BF16 && idx.cache.ratio == 4 && idx.cache.dim == 128 &&
+                      (idx.cache.dtype == CSA_BF16 || idx.cache.dtype == CSA_FP8_E4M3 || idx.cache.dtype == CSA_FP4_E2M1);
+  const bool types_ok = main.cache.dtype == idx.cache.dtype || main.cache.dtype == CSA_FP8_E4M3;
+  const bool score_ok = a.n_q > 0 && a.n_q < kQueryFastMin && a.max_elig > 0 && a.mode == CSA_SCORE_WRELU &&
+                        a.n_heads == 64 && a.cache.ratio == 4 && a.cache.dim == 128 && a.cache.dtype != CSA_F32;
+  if (!(main_ok && idx_ok && types_ok && score_ok)) {
+    const hipError_t e = launch_compress_pair(main, idx, stream);
+    return e != hipSuccess ? e : launch_index_score(a, stream);
+  }
+  const FusedCompress fc{main, idx};
+  Workspace ws = carve(a.ws, a.n_q, a.max_elig);
+  const int64_t max_pages = (a.max_elig + 63) / 64;
+  const bool fp8_main = main.cache.dtype == CSA_FP8_E4M3;
+  if (a.cache.dtype == CSA_FP4_E2M1) {
+    const int run = kPagesPerBlock;
+    const dim3 grid(unsigned((max_pages + run - 1) / run), unsigned(a.n_q));
+    if (fp8_main) hipLaunchKernelGGL((score_mfma_kernel<2, 4, 2>), grid, dim3(256), 0, stream, a, ws, run, fc);
+    else hipLaunchKernelGGL((score_mfma_kernel<2, 4, 1>), grid, dim3(256), 0, stream, a, ws, run, fc);
+  } else {
+    const dim3 grid(unsigned((max_pages + kLtPages - 1) / kLtPages), unsigned(a.n_q));
+    const bool fp8_idx = a.cache.dtype == CSA_FP8_E4M3;
+    if (fp8_idx && fp8_main) hipLaunchKernelGGL((score_lt_kernel<1, 4, 2>), grid, dim3(256), 0, stream, a, ws, fc);
+    else if (fp8_idx) hipLaunchKernelGGL((score_lt_kernel<1, 4, 1>), grid, dim3(256), 0, stream, a, ws, fc);
+    else if (fp8_main) hipLaunchKernelGGL((score_lt_kernel<0, 4, 2>), grid, dim3(256), 0, stream, a, ws, fc);
+    else hipLaunchKernelGGL((score_lt_kernel<0, 4, 1>), grid, dim3(256), 0, stream, a, ws, fc);
   }
   return hipGetLastError();
 }

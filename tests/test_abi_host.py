@@ -223,6 +223,32 @@ def test_compress_pair_validation(L):
     assert call(batch=0) == OK
 
 
+def test_compress_index_score_validation(L):
+    """Both argument sets checked as for the two calls, plus the decode form: one new token per sequence and
+    one query per sequence."""
+    f = L.csa_compress_index_score
+    good_c, good_s = _cache(dim=512), _raw(dim=512)
+    idx_c, idx_s = _cache(dim=128), _raw(dim=128)
+
+    def call(ca=good_c, sa=good_s, cb=idx_c, sb=idx_s, batch=2, total=2, max_new=1, n_q=2, q=FAKE, heads=64,
+             w=FAKE, mode=csa.SCORE_WRELU, k=512, ws=FAKE, ws_bytes=1 << 30, gb=FAKE):
+        return f(ctypes.byref(ca), ctypes.byref(sa), FAKE, FAKE, FAKE, FAKE, 10, ctypes.byref(cb), ctypes.byref(sb),
+                 FAKE, FAKE, gb, FAKE, 10, batch, FAKE, FAKE, total, max_new, 1e-6, n_q, FAKE, FAKE, 1000, q,
+                 csa.BF16, heads, w, mode, k, ws, ws_bytes, None)
+    assert call(cb=_cache(dim=100)) == INVALID
+    assert call(sb=_raw(dim=512)) == INVALID
+    assert call(gb=None) == INVALID
+    assert call(q=None) == INVALID
+    assert call(w=None) == INVALID
+    assert call(ws=None) == WORKSPACE
+    assert call(ws_bytes=16) == WORKSPACE
+    assert call(mode=csa.SCORE_DOT, heads=64) == INVALID
+    assert call(n_q=3) == INVALID                     # one query per sequence
+    assert call(total=3, max_new=2) == INVALID        # one new token per sequence
+    assert call(max_new=2) == INVALID
+    assert call(batch=0, total=0, n_q=0) == OK
+
+
 def test_fp4_cache_validation(L):
     """MXFP4 caches: E8M0 exponents required and 4-byte aligned; scored only by the dim-128 WRELU MFMA path with
     a multiple of 16 heads; never an attention cache or a state/window dtype."""
