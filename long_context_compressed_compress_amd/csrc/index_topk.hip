@@ -37,11 +37,14 @@ struct Workspace {
   uint32_t* hist;   // [n_q][kHistBins]: score histogram of key bits 31..20
   uint32_t* hist2;  // [n_q][kHistBins]: bits 19..8 of the boundary-bin candidates (pre-marked selects)
   uint32_t* ncand;  // [n_q]: candidates listed by the mark pass (pre-marked selects)
-  uint32_t* keys;   // [n_q][max_elig]: order-preserving score keys
+  uint32_t* keys;   // [n_q][key_stride]: order-preserving score keys (rows 256-byte aligned)
   uint2* cand;      // [n_q][max_elig] (key, index): candidates beyond the LDS list
   uint32_t* bits;   // [n_q][bits_stride]: chosen-entry bitmap (long queries, pre-marked selects)
   int64_t bits_stride;
+  int64_t key_stride;  // max_elig rounded up to a multiple of 64
 };
+
+__host__ __device__ inline int64_t key_stride_of(int64_t max_elig) { return (max_elig + 63) / 64 * 64; }
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -60,7 +63,8 @@ __host__ __device__ inline Workspace carve(void* base, int n_q, int64_t max_elig
   w.ncand = reinterpret_cast<uint32_t*>(p);
   p += align256(size_t(n_q) * 4);
   w.keys = reinterpret_cast<uint32_t*>(p);
-  p += align256(size_t(n_q) * size_t(max_elig) * 4);
+  w.key_stride = key_stride_of(max_elig);
+  p += align256(size_t(n_q) * size_t(w.key_stride) * 4);
   w.cand = reinterpret_cast<uint2*>(p);
   p += align256(size_t(n_q) * size_t(max_elig) * 8);
   w.bits_stride = (max_elig + 31) / 32;
@@ -278,7 +282,7 @@ __global__ void __launch_bounds__(256, 2) score_mfma_kernel(IndexArgs a, Workspa
     for (int i = 0; i < 4; ++i) wv[ht][i] = a.head_w[int64_t(q) * H + ht * 16 + kg * 4 + i];
   __syncthreads();
 
-  uint32_t* keys_q = ws.keys + int64_t(q) * a.max_elig;
+  uint32_t* keys_q = ws.keys + int64_t(q) * ws.key_stride;
   // this wave's pages: pg_begin + wave, +4, ... < pg_end
   const int64_t first = __builtin_amdgcn_readfirstlane(int(pg_begin + wave));
   const int n_mine = first < pg_end ? int((pg_end - 1 - first) / 4 + 1) : 0;
@@ -405,7 +409,7 @@ __global__ void __launch_bounds__(kShareThreads, 1) score_shared_kernel(IndexArg
 #pragma unroll
       for (int i = 0; i < 4; ++i) wv[ht][i] = a.head_w[int64_t(qq) * H + ht * 16 + kg * 4 + i];
   }
-  uint32_t* keys_q = ws.keys + int64_t(q_ok ? q : 0) * a.max_elig;
+  uint32_t* keys_q = ws.keys + int64_t(q_ok ? q : 0) * ws.key_stride;
   const char* pages = static_cast<const char*>(a.cache.pages);
   const uint32_t* scales = reinterpret_cast<const uint32_t*>(a.cache.scales);
   __syncthreads();
@@ -652,7 +656,7 @@ __global__ void __launch_bounds__(256, 2) score_lt_kernel(IndexArgs a, Workspace
     for (int i = 0; i < 4; ++i) wv[ht][i] = a.head_w[int64_t(q) * H + ht * 16 + kg * 4 + i];
   lds_barrier();  // pg_phys and the cleared histogram are visible; the loads above stay in flight
 
-  uint32_t* keys_q = ws.keys + int64_t(q) * a.max_elig;
+  uint32_t* keys_q = ws.keys + int64_t(q) * ws.key_stride;
   char* st = stage_s[wave];
   // this wave's pages: pg_begin + wave, +4, ... < pg_end
   const int64_t first = __builtin_amdgcn_readfirstlane(int(pg_begin + wave));
@@ -744,7 +748,7 @@ __global__ void __launch_bounds__(256) score_valu_kernel(IndexArgs a, Workspace 
       }
       key = score_key(total * sc);
     }
-    ws.keys[int64_t(q) * a.max_elig + e] = key;
+    ws.keys[int64_t(q) * ws.key_stride + e] = key;
     atomicAdd(&hist_s[key >> (32 - kHistBits)], 1u);
   }
   flush_hist(hist_s, ws.hist + int64_t(q) * kHistBins);
@@ -756,7 +760,7 @@ __global__ void __launch_bounds__(256) score_valu_kernel(IndexArgs a, Workspace 
 // inside it (candidates) with a histogram of their bits 19..8, a last 8-bit digit and, for exact ties,
 // the lowest indices first; the bitmap read in word order gives the chosen entries in ascending index.
 constexpr int kSelThreads = 1024;
-constexpr int kSelKeysPerThread = 16;
+constexpr int kSelLoads = 8;  // 16-byte key loads per thread and chunk of the key pass
 constexpr int kCandLds = 6144;  // candidates held in LDS; more spill to the workspace list
 
 __device__ __forceinline__ uint32_t dpp_sum16(uint32_t v) {
@@ -764,6 +768,17 @@ __device__ __forceinline__ uint32_t dpp_sum16(uint32_t v) {
   v += uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
   v += uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0x141, 0xF, 0xF, false));  // row_half_mirror
   v += uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0x140, 0xF, 0xF, false));  // row_mirror
+  return v;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (row shifts within each row of 16, then the row broadcasts).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x111, 0xF, 0xF, false));  // row_shr:1
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x112, 0xF, 0xF, false));  // row_shr:2
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x114, 0xF, 0xF, false));  // row_shr:4
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x118, 0xF, 0xF, false));  // row_shr:8
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x142, 0xA, 0xF, false));  // row_bcast:15 into rows 1, 3
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x143, 0xC, 0xF, false));  // row_bcast:31 into rows 2, 3
   return v;
 }
 
@@ -887,7 +902,7 @@ __global__ void __launch_bounds__(kMarkThreads) select_mark_kernel(IndexArgs a, 
   const int64_t c1 = min<int64_t>(n_elig, c0 + kMarkChunk);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const uint32_t* keys_q = ws.keys + int64_t(q) * a.max_elig;
+  const uint32_t* keys_q = ws.keys + int64_t(q) * ws.key_stride;
   uint32_t key[kMarkKeysPerThread];
 #pragma unroll
   for (int j = 0; j < kMarkKeysPerThread; ++j) {
@@ -947,14 +962,14 @@ __global__ void __launch_bounds__(kMarkThreads) select_mark_kernel(IndexArgs a, 
   flush_hist(h2_s, ws.hist2 + int64_t(q) * kHistBins);
 }
 
-template <bool PRE, int NT, int BMW, int CLDS>
-__global__ void __launch_bounds__(NT) select_kernel(IndexArgs a, Workspace ws) {
+template <bool PRE, int NT, int BMW, int CLDS, bool BMG>
+__global__ void __launch_bounds__(NT, 4) select_kernel(IndexArgs a, Workspace ws) {  // 4 waves per SIMD: 1024 threads per CU
   __shared__ uint32_t tmp[NT / 64];
   __shared__ uint32_t hist2[kHistBins];      // key bits 19..8 of the candidates
   __shared__ uint32_t dig[256];
   __shared__ uint32_t res[4];
   __shared__ uint32_t s_cnt[2];              // sure count, candidate count
-  __shared__ uint32_t bitmap_s[BMW];  // chosen entries, one bit each
+  __shared__ uint32_t bitmap_s[BMG ? 1 : BMW];  // chosen entries, one bit each
   __shared__ uint2 cand_s[CLDS];
 
   const int q = blockIdx.x;
@@ -963,14 +978,17 @@ __global__ void __launch_bounds__(NT) select_kernel(IndexArgs a, Workspace ws) {
   const int64_t kk = min<int64_t>(a.k, n_elig);  // entries to choose
   const int tid = threadIdx.x;
   uint2* cand_g = ws.cand + int64_t(q) * a.max_elig;  // overflow of the candidate list
-  const uint32_t* keys_q = ws.keys + int64_t(q) * a.max_elig;
+  const uint32_t* keys_q = ws.keys + int64_t(q) * ws.key_stride;
   const int64_t n_words = (n_elig + 31) / 32;
   // the mark pass has already scanned this query's keys (bitmap words of keys above the boundary bin,
   // candidate list and hist2 in the workspace)
   const bool pre = PRE && n_elig > a.k;
   uint32_t* bits_g = ws.bits + int64_t(q) * ws.bits_stride;
-  // longer queries keep their bitmap in the workspace
-  uint32_t* bitmap = n_words <= BMW ? bitmap_s : bits_g;
+  // The chosen-entry bitmap is in LDS when every query of the launch has at most BMW words (BMG false), else in the
+  // workspace. The choice is made per launch at compile time so that the LDS variant's bitmap accesses are LDS
+  // instructions: through a pointer that may point to either they are flat accesses, which count with the key loads,
+  // and the key pass then waited for each bitmap store before going on to its next key.
+  uint32_t* bitmap = BMG ? bits_g : bitmap_s;
   uint32_t* hist2_g = ws.hist2 + int64_t(q) * kHistBins;
   // after a mark pass every global read of the set-up (score histogram, bitmap words, second histogram) is
   // issued here, before any of them is used, so they cost one round trip together
@@ -983,7 +1001,7 @@ __global__ void __launch_bounds__(NT) select_kernel(IndexArgs a, Workspace ws) {
   }
   if (pre) {
     constexpr int BW = BMW / NT;  // bitmap words per thread when the bitmap fits LDS
-    const bool lds_bits = bitmap != bits_g;
+    constexpr bool lds_bits = !BMG;
     uint32_t bw[BW], h2[PER];
     if (lds_bits) {
 #pragma unroll
@@ -1044,54 +1062,76 @@ __global__ void __launch_bounds__(NT) select_kernel(IndexArgs a, Workspace ws) {
   __syncthreads();
 
   // ---- one pass over the keys: mark keys above the bin, collect keys inside it (and their next 12 bits).
-  // For step j a wave holds 64 consecutive keys starting on a 64-key boundary, so it owns two whole bitmap
-  // words and stores them from its ballot. Candidates are rare: a wave reserves list slots for all of its
-  // candidates of a chunk with one LDS atomic, at offsets taken from the per-step ballots.
+  // A thread reads 4 consecutive keys per 16-byte load, so one load instruction of a wave covers 256 keys; each
+  // group of 8 lanes holds one 32-key bitmap word, which it assembles with three lane exchanges and its first
+  // lane stores. Every per-key step is vector arithmetic: with a ballot, a mask branch and scalar mask arithmetic
+  // per key, 16 waves on one CU were bound by its instruction issue, not by the loads. Candidates (rare) get list
+  // slots once per wave and chunk: a wave prefix sum of the lanes' counts and one LDS atomic.
   const int lane = tid & 63;
-  const uint64_t below = (1ull << lane) - 1ull;
-  // key positions of a query fit 32 bits (fewer than 2^29 entries): 32-bit byte offsets from the query's keys keep
-  // the 16 addresses of a chunk cheap enough that all its loads go out before the first is used
-  const char* keys_b = reinterpret_cast<const char*>(keys_q);
   const uint32_t n_el32 = uint32_t(n_elig);
-  for (int64_t base = 0; base < (pre ? 0 : n_elig); base += int64_t(NT) * kSelKeysPerThread) {
-    uint32_t key[kSelKeysPerThread];
+  const uint32_t n4 = (n_el32 + 3) / 4;
+  const uint4* keys4 = reinterpret_cast<const uint4*>(keys_q);  // key rows are 256-byte aligned
+  uint32_t n_sure_l = 0;
+  for (uint32_t base4 = 0; base4 < (pre ? 0u : n4); base4 += uint32_t(NT) * kSelLoads) {
+    uint4 kv[kSelLoads];
 #pragma unroll
-    for (int j = 0; j < kSelKeysPerThread; ++j) {
-      const uint32_t i = uint32_t(base) + uint32_t(tid + NT * j);
-      key[j] = *reinterpret_cast<const uint32_t*>(keys_b + ((i < n_el32 ? i : 0u) << 2));  // clamped, unconditional
+    for (int j = 0; j < kSelLoads; ++j) {
+      const uint32_t u = base4 + uint32_t(tid + NT * j);
+      kv[j] = keys4[u < n4 ? u : 0u];  // clamped, unconditional; a row's last load stays inside its stride
     }
-    uint32_t n_sure_w = 0, n_cand_w = 0, cand_off[kSelKeysPerThread];
-    uint64_t cand_m[kSelKeysPerThread];
+    uint32_t cbits = 0;  // candidate flags: bit 4 j + c for key c of load j
 #pragma unroll
-    for (int j = 0; j < kSelKeysPerThread; ++j) {
-      const int64_t i = base + tid + int64_t(NT) * j;
-      const bool in = i < n_elig;
-      const int bin = int(key[j] >> (32 - kHistBits));
-      const uint64_t sm = __ballot(in && (b0 < 0 || bin > b0));
-      const int64_t w0 = (base + (tid & ~63) + int64_t(NT) * j) >> 5;
-      if (lane < 2 && w0 + lane < n_words) bitmap[w0 + lane] = lane == 0 ? uint32_t(sm) : uint32_t(sm >> 32);
-      n_sure_w += uint32_t(__popcll(sm));
-      cand_m[j] = __ballot(in && b0 >= 0 && bin == b0);
-      cand_off[j] = n_cand_w;
-      n_cand_w += uint32_t(__popcll(cand_m[j]));
+    for (int j = 0; j < kSelLoads; ++j) {
+      const uint32_t u = base4 + uint32_t(tid + NT * j);
+      const uint32_t k4[4] = {kv[j].x, kv[j].y, kv[j].z, kv[j].w};
+      uint32_t sure = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const bool in = 4 * u + c < n_el32;
+        const int bin = int(k4[c] >> (32 - kHistBits));
+        sure |= uint32_t(in && bin > b0) << c;  // b0 = -1 when every eligible entry is chosen
+        cbits |= uint32_t(in && bin == b0) << (4 * j + c);
+      }
+      n_sure_l += __popc(sure);
+      // word (base4 + NT j) / 8 + tid / 8 holds keys 4 (base4 + NT j + (tid & ~7)) .. +31
+      uint32_t wd = sure << (4 * (lane & 7));
+      wd |= uint32_t(__builtin_amdgcn_mov_dpp(int(wd), 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+      wd |= uint32_t(__builtin_amdgcn_mov_dpp(int(wd), 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+      wd |= uint32_t(__builtin_amdgcn_mov_dpp(int(wd), 0x141, 0xF, 0xF, false));  // row_half_mirror
+      const uint32_t word = (base4 + uint32_t(NT * j)) / 8 + uint32_t(tid >> 3);
+      if ((lane & 7) == 0 && word < uint32_t(n_words)) bitmap[word] = wd;
     }
-    if (n_sure_w && lane == 0) atomicAdd(&s_cnt[0], n_sure_w);
-    if (n_cand_w) {
+    const uint32_t nc = uint32_t(__popc(cbits));
+    if (__ballot(nc != 0u)) {  // uniform over the wave
+      const uint32_t incl = wave_incl_scan(nc);
+      const uint32_t total = uint32_t(__builtin_amdgcn_readlane(int(incl), 63));
       uint32_t wbase = 0;
-      if (lane == 0) wbase = atomicAdd(&s_cnt[1], n_cand_w);
+      if (lane == 0) wbase = atomicAdd(&s_cnt[1], total);
       wbase = uint32_t(__builtin_amdgcn_readfirstlane(int(wbase)));  // every lane is active here
+      uint32_t cs = wbase + incl - nc;
 #pragma unroll
-      for (int j = 0; j < kSelKeysPerThread; ++j) {
-        if ((cand_m[j] >> lane) & 1ull) {
-          const int64_t i = base + tid + int64_t(NT) * j;
-          const uint32_t cs = wbase + cand_off[j] + uint32_t(__popcll(cand_m[j] & below));
-          atomicAdd(&hist2[(key[j] >> 8) & (kHistBins - 1)], 1u);
-          const uint2 item = make_uint2(key[j], uint32_t(i));
-          if (cs < uint32_t(CLDS)) cand_s[cs] = item;
-          else if (cs - CLDS < uint32_t(a.max_elig)) cand_g[cs - CLDS] = item;
+      for (int j = 0; j < kSelLoads; ++j) {
+        const uint32_t cj = (cbits >> (4 * j)) & 0xFu;
+        if (cj) {
+          const uint32_t u = base4 + uint32_t(tid + NT * j);
+          const uint32_t k4[4] = {kv[j].x, kv[j].y, kv[j].z, kv[j].w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            if ((cj >> c) & 1u) {
+              atomicAdd(&hist2[(k4[c] >> 8) & (kHistBins - 1)], 1u);
+              const uint2 item = make_uint2(k4[c], 4 * u + c);
+              if (cs < uint32_t(CLDS)) cand_s[cs] = item;
+              else if (cs - CLDS < uint32_t(a.max_elig)) cand_g[cs - CLDS] = item;
+              ++cs;
+            }
+          }
         }
       }
     }
+  }
+  if (!pre) {
+    const uint32_t sure_w = uint32_t(__builtin_amdgcn_readlane(int(wave_incl_scan(n_sure_l)), 63));
+    if (lane == 0 && sure_w) atomicAdd(&s_cnt[0], sure_w);
   }
   __threadfence_block();
   __syncthreads();
@@ -1219,7 +1259,8 @@ __global__ void empty_rows_kernel(IndexArgs a) {
 
 size_t index_workspace(int n_q, int64_t max_elig, int k) {
   (void)k;
-  return clean_bytes(n_q) + align256(size_t(n_q) * size_t(max_elig) * 4) + align256(size_t(n_q) * size_t(max_elig) * 8) +
+  return clean_bytes(n_q) + align256(size_t(n_q) * size_t(key_stride_of(max_elig)) * 4) +
+         align256(size_t(n_q) * size_t(max_elig) * 8) +
          align256(size_t(n_q) * size_t((max_elig + 31) / 32) * 4);
 }
 
@@ -1345,6 +1386,14 @@ hipError_t launch_compress_index_score(const CompressArgs& main, const CompressA
   return hipGetLastError();
 }
 
+template <bool PRE, int NT, int BMW, int CLDS>
+void launch_select(const IndexArgs& a, const Workspace& ws, hipStream_t stream) {
+  if ((a.max_elig + 31) / 32 <= BMW)
+    hipLaunchKernelGGL((select_kernel<PRE, NT, BMW, CLDS, false>), dim3(a.n_q), dim3(NT), 0, stream, a, ws);
+  else
+    hipLaunchKernelGGL((select_kernel<PRE, NT, BMW, CLDS, true>), dim3(a.n_q), dim3(NT), 0, stream, a, ws);
+}
+
 hipError_t launch_index_select(const IndexArgs& a, hipStream_t stream) {
   if (a.n_q == 0) return hipSuccess;
   if (a.max_elig == 0) {
@@ -1355,16 +1404,13 @@ hipError_t launch_index_select(const IndexArgs& a, hipStream_t stream) {
   if (a.n_q <= kPremarkMaxQueries && a.max_elig >= kPremarkMinElig) {
     const dim3 grid(unsigned((a.max_elig + kMarkChunk - 1) / kMarkChunk), unsigned(a.n_q));
     hipLaunchKernelGGL(select_mark_kernel, grid, dim3(kMarkThreads), 0, stream, a, ws);
-    hipLaunchKernelGGL((select_kernel<true, kSelThreads, kBitmapLds, kCandLds>), dim3(a.n_q), dim3(kSelThreads), 0, stream,
-                       a, ws);
+    launch_select<true, kSelThreads, kBitmapLds, kCandLds>(a, ws, stream);
   } else if (a.n_q >= kSelManyQueries) {
     // many queries: half-size workgroups with half-size LDS tables, two per CU, so that one workgroup's
     // scans and barriers overlap the other's key loads
-    hipLaunchKernelGGL((select_kernel<false, kSelThreads / 2, kBitmapLds / 2, kCandLds / 2>), dim3(a.n_q),
-                       dim3(kSelThreads / 2), 0, stream, a, ws);
+    launch_select<false, kSelThreads / 2, kBitmapLds / 2, kCandLds / 2>(a, ws, stream);
   } else {
-    hipLaunchKernelGGL((select_kernel<false, kSelThreads, kBitmapLds, kCandLds>), dim3(a.n_q), dim3(kSelThreads), 0,
-                       stream, a, ws);
+    launch_select<false, kSelThreads, kBitmapLds, kCandLds>(a, ws, stream);
   }
   return hipGetLastError();
 }
