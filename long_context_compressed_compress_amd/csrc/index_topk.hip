@@ -860,19 +860,6 @@ __device__ __forceinline__ void wave0_digit_asc(const uint32_t* dig, int nbins, 
   }
 }
 
-// Wave-aggregated append into an LDS list through an LDS counter; returns the slot of this lane's item.
-__device__ __forceinline__ uint32_t wave_slot(bool take, uint32_t* counter) {
-  const uint64_t mask = __ballot(take);
-  const int lane = threadIdx.x & 63;
-  uint32_t base = 0;
-  if (mask) {
-    const int leader = __ffsll((unsigned long long)mask) - 1;
-    if (lane == leader) base = atomicAdd(counter, uint32_t(__popcll(mask)));
-    base = __shfl(base, leader);
-  }
-  return base + uint32_t(__popcll(mask & ((1ull << lane) - 1ull)));
-}
-
 constexpr int kBitmapLds = 8192;  // LDS bitmap words: queries with up to 262144 eligible entries
 constexpr int kSelManyQueries = 256;  // launches of at least this many queries take the half-size select workgroups
 
@@ -883,8 +870,8 @@ constexpr int kSelManyQueries = 256;  // launches of at least this many queries 
 // bin; every word of the chunk is written, so the bitmap needs no clearing), lists the keys inside the bin
 // as candidates and counts their bits 19..8 in hist2. The select pass then only resolves the boundary bin.
 constexpr int kMarkThreads = 256;
-constexpr int kMarkKeysPerThread = 32;
-constexpr int kMarkChunk = kMarkThreads * kMarkKeysPerThread;  // 8192 keys = 256 bitmap words
+constexpr int kMarkLoads = 8;  // 16-byte key loads per thread
+constexpr int kMarkChunk = kMarkThreads * kMarkLoads * 4;  // 8192 keys = 256 bitmap words
 constexpr int kPremarkMaxQueries = 64;
 constexpr int64_t kPremarkMinElig = 65536;
 
@@ -902,12 +889,14 @@ __global__ void __launch_bounds__(kMarkThreads) select_mark_kernel(IndexArgs a, 
   const int64_t c1 = min<int64_t>(n_elig, c0 + kMarkChunk);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const uint32_t* keys_q = ws.keys + int64_t(q) * ws.key_stride;
-  uint32_t key[kMarkKeysPerThread];
+  // 4 consecutive keys per 16-byte load (key rows are 256-byte aligned and c0 is a multiple of the chunk)
+  const uint4* keys4 = reinterpret_cast<const uint4*>(ws.keys + int64_t(q) * ws.key_stride);
+  const uint32_t u0 = uint32_t(c0 / 4), u1 = uint32_t((c1 + 3) / 4);
+  uint4 kv[kMarkLoads];
 #pragma unroll
-  for (int j = 0; j < kMarkKeysPerThread; ++j) {
-    const int64_t i = c0 + tid + int64_t(kMarkThreads) * j;
-    key[j] = keys_q[i < c1 ? i : c0];  // clamped, unconditional load
+  for (int j = 0; j < kMarkLoads; ++j) {
+    const uint32_t u = u0 + uint32_t(tid + kMarkThreads * j);
+    kv[j] = keys4[u < u1 ? u : u0];  // clamped, unconditional load
   }
   for (int b = tid; b < kHistBins; b += kMarkThreads) h2_s[b] = 0u;
   // boundary bin: the largest b0 with count(bins >= b0) >= k
@@ -933,24 +922,61 @@ __global__ void __launch_bounds__(kMarkThreads) select_mark_kernel(IndexArgs a, 
   uint32_t* bits_q = ws.bits + int64_t(q) * ws.bits_stride;
   uint2* cand_q = ws.cand + int64_t(q) * a.max_elig;
   const int64_t n_words = (n_elig + 31) / 32;
+  // Per load j a wave covers 256 consecutive keys; each group of 8 lanes assembles one 32-key bitmap word with
+  // lane exchanges (all vector arithmetic). The words are stored after the loop, with every key already read.
+  const uint32_t c1u = uint32_t(c1);
+  uint32_t wd[kMarkLoads];
+  uint32_t cbits = 0;  // candidate flags: bit 4 j + c for key c of load j
 #pragma unroll
-  for (int j = 0; j < kMarkKeysPerThread; ++j) {
-    const int64_t i = c0 + tid + int64_t(kMarkThreads) * j;
-    const bool in = i < c1;
-    const uint32_t bin = key[j] >> (32 - kHistBits);
-    const bool is_sure = in && bin > b0 && b0 != 0xFFFFFFFFu;
-    const bool is_cand = in && bin == b0;
-    // a wave's 64 keys are consecutive and start on a 64-key boundary: it owns two whole bitmap words
-    const uint64_t sm = __ballot(is_sure);
-    const int64_t w0 = (c0 + (tid & ~63) + int64_t(kMarkThreads) * j) >> 5;
-    if (lane < 2 && w0 + lane < n_words) bits_q[w0 + lane] = lane == 0 ? uint32_t(sm) : uint32_t(sm >> 32);
-    // candidates go to an LDS list (a returning device-scope atomic per wave would serialise on the
-    // query's counter across XCDs)
-    const uint32_t cs = wave_slot(is_cand, &res[1]);
-    if (is_cand) {
-      cand_s[cs] = make_uint2(key[j], uint32_t(i));
-      atomicAdd(&h2_s[(key[j] >> 8) & (kHistBins - 1)], 1u);
+  for (int j = 0; j < kMarkLoads; ++j) {
+    const uint32_t u = u0 + uint32_t(tid + kMarkThreads * j);
+    const uint32_t k4[4] = {kv[j].x, kv[j].y, kv[j].z, kv[j].w};
+    uint32_t sure = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bool in = 4 * u + c < c1u;
+      const uint32_t bin = k4[c] >> (32 - kHistBits);
+      sure |= uint32_t(in && bin > b0 && b0 != 0xFFFFFFFFu) << c;
+      cbits |= uint32_t(in && bin == b0) << (4 * j + c);
     }
+    uint32_t w = sure << (4 * (lane & 7));
+    w |= uint32_t(__builtin_amdgcn_mov_dpp(int(w), 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+    w |= uint32_t(__builtin_amdgcn_mov_dpp(int(w), 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+    w |= uint32_t(__builtin_amdgcn_mov_dpp(int(w), 0x141, 0xF, 0xF, false));  // row_half_mirror
+    wd[j] = w;
+  }
+  // candidates go to an LDS list (a returning device-scope atomic per wave would serialise on the query's
+  // counter across XCDs): one LDS reservation per wave from a wave prefix sum of the lanes' counts
+  const uint32_t nc = uint32_t(__popc(cbits));
+  if (__ballot(nc != 0u)) {  // uniform over the wave
+    const uint32_t incl = wave_incl_scan(nc);
+    const uint32_t total = uint32_t(__builtin_amdgcn_readlane(int(incl), 63));
+    uint32_t wbase = 0;
+    if (lane == 0) wbase = atomicAdd(&res[1], total);
+    wbase = uint32_t(__builtin_amdgcn_readfirstlane(int(wbase)));  // every lane is active here
+    uint32_t cs = wbase + incl - nc;  // < kMarkChunk: at most one candidate per key of the chunk
+#pragma unroll
+    for (int j = 0; j < kMarkLoads; ++j) {
+      const uint32_t cj = (cbits >> (4 * j)) & 0xFu;
+      if (cj) {
+        const uint32_t u = u0 + uint32_t(tid + kMarkThreads * j);
+        const uint32_t k4[4] = {kv[j].x, kv[j].y, kv[j].z, kv[j].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if ((cj >> c) & 1u) {
+            cand_s[cs++] = make_uint2(k4[c], 4 * u + c);
+            atomicAdd(&h2_s[(k4[c] >> 8) & (kHistBins - 1)], 1u);
+          }
+        }
+      }
+    }
+  }
+  // word (u0 + 256 j) / 8 + tid / 8 holds keys 4 (u0 + 256 j + (tid & ~7)) .. +31; every word of the chunk below
+  // n_words is stored whole
+#pragma unroll
+  for (int j = 0; j < kMarkLoads; ++j) {
+    const uint32_t word = (u0 + uint32_t(kMarkThreads * j)) / 8 + uint32_t(tid >> 3);
+    if ((lane & 7) == 0 && word < uint32_t(n_words)) bits_q[word] = wd[j];
   }
   __syncthreads();
   const uint32_t n_local = res[1];  // <= kMarkChunk
