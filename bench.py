@@ -173,7 +173,12 @@ STEP_MODES = {"eager": "eager launches on one stream with an event between stage
               "graph_partition": "one HIP graph per layer, the indexer pipeline (its compress_insert, score, select) on "
                                  "a second stream beside the main-cache compress_insert",
               "graph_fused": "one HIP graph per layer, every call on one stream, both caches' compress_insert inside "
-                             "the index-score launch (csa_compress_index_score)"}
+                             "the index-score launch (csa_compress_index_score)",
+              "graph_layers": "HIP graphs that each hold one step of several consecutive layers in order (as a "
+                              "whole-model decode graph holds every layer), every call on one stream",
+              "graph_fused_layers": "HIP graphs that each hold one step of several consecutive layers in order (as a "
+                                    "whole-model decode graph holds every layer), every call on one stream, both "
+                                    "caches' compress_insert inside the index-score launch (csa_compress_index_score)"}
 
 
 def capture_graphs(torch, layers, fn):
@@ -190,32 +195,45 @@ def capture_graphs(torch, layers, fn):
     return graphs
 
 
-def time_graphs(torch, graphs, steps, warmup):
-    """Replay the per-layer step graphs in rotation; ms for `steps` replays between two events."""
-    for i in range(warmup):
+def capture_layers_graph(torch, layers, fn):
+    """One HIP graph holding one step of every layer, in layer order (fn(layer) for each, on the capturing stream)."""
+    for ly in layers:
+        fn(ly)  # eager warm-up of exactly the captured work
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for ly in layers:
+            fn(ly)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graphs(torch, graphs, steps, warmup, per=1):
+    """Replay the step graphs in rotation (each replay runs `per` steps); ms for `steps` steps between two events."""
+    for i in range(max(1, warmup // per)):
         graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
-    for i in range(steps):
+    for i in range(steps // per):
         graphs[i % len(graphs)].replay()
     t1.record()
     torch.cuda.synchronize()
     return t0.elapsed_time(t1)
 
 
-def replay_percentiles(torch, graphs, steps):
+def replay_percentiles(torch, graphs, steps, per=1):
     """Each replay between its own pair of events (a separate pass after the timed region): p10 / median / p90 of
-    the per-step time in microseconds."""
+    the per-step time in microseconds (a replay's time over its `per` steps)."""
     ev = []
-    for i in range(steps):
+    for i in range(steps // per):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         graphs[i % len(graphs)].replay()
         b.record()
         ev.append((a, b))
     torch.cuda.synchronize()
-    v = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    v = np.array([a.elapsed_time(b) * 1e3 / per for a, b in ev])
     return {"p10": round(float(np.percentile(v, 10)), 2), "median": round(float(np.median(v)), 2),
             "p90": round(float(np.percentile(v, 90)), 2), "n": int(len(v))}
 
@@ -226,7 +244,9 @@ LAST_PERCENTILES = {}
 def best_graph_mode(torch, layers, steps, warmup, sequential, two_stream, partitioned=None, fused=None):
     """Time the step as one HIP graph per layer in each stream arrangement given (all on one stream; main-cache
     compress on a second stream; the indexer pipeline on a second stream; all on one stream with the compress inside
-    the index-score launch); returns (ms of the fastest, its name, ms of each). The per-step percentiles of the fastest are left in LAST_PERCENTILES. With --eager-only (profiler
+    the index-score launch), and as graphs that each hold one step of gcd(steps, layers) consecutive layers in order
+    (the fused step where given, else the one-stream step), replayed in rotation so that exactly `steps` steps run
+    and every layer as often; returns (ms of the fastest, its name, ms of each). The per-step percentiles of the fastest are left in LAST_PERCENTILES. With --eager-only (profiler
     runs) no graph is built and (None, "eager", {}) comes back."""
     LAST_PERCENTILES.clear()
     if EAGER_ONLY:
@@ -238,9 +258,17 @@ def best_graph_mode(torch, layers, steps, warmup, sequential, two_stream, partit
             continue
         graphs = capture_graphs(torch, layers, fn)
         modes[name] = time_graphs(torch, graphs, steps, warmup)
-        kept[name] = graphs
+        kept[name] = (graphs, 1)
+    per = math.gcd(steps, len(layers))  # layers per graph: exactly `steps` steps, every layer equally often
+    if per > 1:
+        name = "graph_fused_layers" if fused is not None else "graph_layers"
+        graphs = [capture_layers_graph(torch, layers[i:i + per], fused if fused is not None else sequential)
+                  for i in range(0, len(layers), per)]
+        modes[name] = time_graphs(torch, graphs, steps, warmup, per=per)
+        kept[name] = (graphs, per)
     best = min(modes, key=modes.get)
-    LAST_PERCENTILES.update(replay_percentiles(torch, kept[best], steps))
+    LAST_PERCENTILES.update(replay_percentiles(torch, kept[best][0], steps, per=kept[best][1]))
+    LAST_PERCENTILES["steps_per_replay"] = kept[best][1]
     del kept
     return modes[best], best, modes
 

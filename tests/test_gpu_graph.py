@@ -9,6 +9,8 @@
   tests/chain.verify.
 * test_graph_replay_matches_eager: the benchmark's capture (main compress on the side stream, bf16 or MXFP4
   indexer cache) replays to the eager result bit for bit.
+* test_fused_layers_graph_replay_matches_eager: the fused decode step (both compresses inside the index-score
+  launch) of two layers in one graph replays to the eager result bit for bit.
 
 Shapes are the real ones (64 heads x K=V 512 bf16, indexer 64 heads x 128 WRELU in bf16 or MXFP4, top-512 +
 window 128) at a few short contexts. Each replay runs after eager work of its own and a synchronisation; every replay's top-k lists,
@@ -111,6 +113,16 @@ class _Layer:
         csa.attend(self.cache, self.swa, SWA, self.seq, self.pos, self.q, self.topk, self.max_elig,
                    1.0 / math.sqrt(D), True, self.rope, self.out, self.lse, workspace=self.att_ws)
 
+    def step_fused(self):
+        """The step with both caches' compress inside the index-score launch, every call on the current stream."""
+        csa.compress_index_score(self.cache, self.state, self.kv1, self.lg1, self.gamma, self.rope, self.icache,
+                                 self.istate, self.ikv1, self.ilg1, self.igamma, self.rope, self.pos, self.cu1, 1e-6,
+                                 self.seq, self.pos, self.max_elig, self.q_idx, self.head_w, csa.SCORE_WRELU, K_TOP,
+                                 self.ws)
+        csa.index_select(self.icache, self.seq, self.pos, self.max_elig, K_TOP, self.topk, self.ws)
+        csa.attend(self.cache, self.swa, SWA, self.seq, self.pos, self.q, self.topk, self.max_elig,
+                   1.0 / math.sqrt(D), True, self.rope, self.out, self.lse, workspace=self.att_ws)
+
     def results(self):
         torch.cuda.synchronize()
         return [t.clone() for t in (self.topk, self.out, self.lse, self.cache.pages, self.ipages_u8, self.iscales,
@@ -155,6 +167,47 @@ def test_graph_replay_matches_eager(fp4_idx):
             assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
                                b.view(torch.uint8) if b.dtype == torch.bfloat16 else b), f"replay {rep}: {name} differs"
         _log(f"replay {rep}: identical to the eager step")
+
+
+NAMES = ["topk", "out", "lse", "pages", "idx pages", "idx scales", "state", "idx state"]
+
+
+def _same(a, b):
+    return torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
+                       b.view(torch.uint8) if b.dtype == torch.bfloat16 else b)
+
+
+@pytest.mark.parametrize("fp4_idx", [False, True])
+def test_fused_layers_graph_replay_matches_eager(fp4_idx):
+    """One graph holding the fused step (csa_compress_index_score, select, attention) of two layers in order, as the
+    benchmark's multi-layer graphs do: every replay equals the eager fused step, which equals the unfused step."""
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    a, b = _Layer(83, fp4_idx), _Layer(84, fp4_idx)
+    a2 = _Layer(83, fp4_idx)  # the same layer again, stepped with the separate calls
+    other = _Layer(85, fp4_idx)
+    _log(f"fused layers graph: contexts {a.lens} / {b.lens}, fp4 indexer cache {fp4_idx}")
+    a.step_fused()
+    b.step_fused()
+    ref = [a.results(), b.results()]
+    a2.step(side)
+    for name, x, y in zip(NAMES, a2.results(), ref[0]):
+        assert _same(x, y), f"fused eager step differs from the separate calls: {name}"
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        a.step_fused()
+        b.step_fused()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        other.step_fused()        # eager work of the program between replays, on other buffers
+        a.poison()
+        b.poison()
+        torch.cuda.synchronize()
+        g.replay()
+        for ly, r in zip((a, b), ref):
+            for name, x, y in zip(NAMES, ly.results(), r):
+                assert _same(x, y), f"replay {rep}: {name} differs"
+        _log(f"replay {rep}: both layers identical to the eager fused step")
 
 
 PARTITION_CASES = [
