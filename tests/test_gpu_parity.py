@@ -362,6 +362,14 @@ ATTEND_CASES = [
     (4, 512, 16, "bf16", 2048, [9000]),
     # many queries: one key split per query, output written directly by the attention workgroup
     (4, 512, 64, "bf16", 64, [300 + (37 * i) % 400 for i in range(520)]),
+    # 16 queries of 64 heads (key splits and their merge); short contexts leave top-k slots unfilled and windows
+    # partly before position 0
+    (4, 512, 64, "bf16", 512, [9000, 3001, 40, 5, 21000, 2059, 777, 20000, 12, 14000, 3, 4100, 9999, 2047, 700, 131]),
+    (4, 512, 64, "fp8", 512, [7000, 2222, 17, 19000, 4095, 300, 15000, 1030, 8, 10000, 2500, 611, 12345, 77, 4000,
+                              5555, 3001]),
+    (128, 512, 64, "bf16", 0, [70000, 4100, 1000, 130, 3, 65535, 32768, 127, 128, 255, 9000, 50000, 20000, 700, 16000,
+                               60000]),
+    (4, 512, 128, "bf16", 2048, [12000, 9500, 30000, 100, 2060, 8191, 20000, 700]),  # 128 heads, top-2048 + window
 ]
 
 
@@ -600,6 +608,11 @@ def test_bf16_chain_end_to_end(cache_dtype):
     (4, 64, "bf16", 64, 32, [300 + (37 * i) % 400 for i in range(520)]),  # one split: the attention epilogue
     (128, 32, "bf16", 0, 16, [3000, 127, 1025]),                          # 16-head groups, dense c128a
     (4, 16, "fp8", 2048, 128, [9000]),
+    # 16 queries x 64 heads: several key splits, the fp8 groups written by the merge
+    (4, 64, "bf16", 512, 64, [9000, 3001, 40, 5, 21000, 2059, 777, 20000, 12, 14000, 3, 4100, 9999, 2047, 700, 131]),
+    (128, 64, "fp8", 0, 16, [70000, 4100, 1000, 130, 3, 65535, 32768, 127, 128, 255, 9000, 50000, 20000, 700, 16000,
+                             60000]),
+    (4, 64, "bf16", 512, 128, [9000, 3001, 40, 5, 21000, 2059, 777, 20000, 12, 14000, 3, 4100, 9999, 2047, 700, 131]),
 ])
 def test_attend_quant_fp8_parity(ratio, heads, dtype, k, group, positions):
     """csa_attend_quant_fp8 against the oracle's attention followed by its inverse RoPE + grouped fp8 rule (R23).
