@@ -817,6 +817,7 @@ __global__ void __launch_bounds__(512) attend_split_kernel(AttendArgs a, SplitPl
 
 // Merge the key splits of each (query, head): o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s, then the
 // optional inverse RoPE. One 256-thread workgroup per (query, 4 heads); a thread owns 8 consecutive dims.
+template <int NSC>
 __global__ void __launch_bounds__(256) attend_combine_kernel(AttendArgs a, SplitPlan sp, const float* part_o,
                                                              const float* part_ml) {
   const int hq = a.n_heads / 4;
@@ -824,61 +825,98 @@ __global__ void __launch_bounds__(256) attend_combine_kernel(AttendArgs a, Split
   const int h = (blockIdx.x % hq) * 4 + (threadIdx.x >> 6);
   const int d0 = (threadIdx.x & 63) * 8;
   if (q >= a.n_q) return;
-  // Loads go out a chunk of splits at a time (indices clamped, every load unconditional, surplus splits of a chunk
-  // masked afterwards), so a chunk costs one memory round trip: first the (max, sum) pairs of up to kMlChunk splits
-  // for the common maximum, then the partial outputs of kOChunk splits at a time. The sums are added in split
-  // order as in a plain loop.
-  constexpr int kMlChunk = 16, kOChunk = 8;
+  const int64_t p = a.q_pos[q];
   const int ns = sp.n_split;
   const float2* ml = reinterpret_cast<const float2*>(part_ml);
   auto slot_of = [&](int s) { return (int64_t(q) * ns + (s < ns ? s : ns - 1)) * a.n_heads + h; };
-  float M = -INFINITY;
-  for (int s0 = 0; s0 < ns; s0 += kMlChunk) {
-    float2 v[kMlChunk];
-#pragma unroll
-    for (int j = 0; j < kMlChunk; ++j) v[j] = ml[slot_of(s0 + j)];
-#pragma unroll
-    for (int j = 0; j < kMlChunk; ++j)
-      if (s0 + j < ns) M = fmaxf(M, v[j].x);
-  }
-  float L = 0.f;
+  const int R_ = a.cache.rope_dims;
+  const int base = kD - R_;
+  const bool rot = a.fuse_inv_rope && R_ > 0 && p >= 0 && p < a.rope_rows;
+  float M = -INFINITY, L = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < ns; s0 += kOChunk) {
-    float2 v[kOChunk];
-    float4 x0[kOChunk], x1[kOChunk];
+  float2 csv[4] = {};  // (cos, sin) of the rotation pair of dims d0 + 2 k, k < 4
+  // the rotation's table row: loaded once the position is in (a scalar load issued first), beside the split loads
+  auto load_cs = [&]() {
+    if (!rot) return;  // uniform; the table may be absent without the rotation
+    const float2* row = reinterpret_cast<const float2*>(a.rope_cs + p * int64_t(R_));
 #pragma unroll
-    for (int j = 0; j < kOChunk; ++j) {
-      const int64_t slot = slot_of(s0 + j);
+    for (int k = 0; k < 4; ++k) {
+      const int d = d0 + 2 * k;
+      csv[k] = row[d >= base ? (d - base) >> 1 : 0];  // clamped into the row
+    }
+  };
+  if constexpr (NSC > 0) {
+    // Up to NSC splits: every (max, sum) pair and partial output goes out before any is used, so they cost one
+    // memory round trip; surplus slots re-read the last split and get weight 0. The sums are added in split order
+    // as in a plain loop.
+    float2 v[NSC];
+    float4 x0[NSC], x1[NSC];
+#pragma unroll
+    for (int j = 0; j < NSC; ++j) {
+      const int64_t slot = slot_of(j);
       v[j] = ml[slot];
       const float4* src = reinterpret_cast<const float4*>(part_o + slot * kD + d0);
       x0[j] = src[0];
       x1[j] = src[1];
     }
+    load_cs();
 #pragma unroll
-    for (int j = 0; j < kOChunk; ++j) {
-      // a surplus split of the last chunk gets weight 0 (its clamped loads read a real split, so the products are
-      // exact zeros); a branch here would let the compiler move the loads below it, one round trip each
+    for (int j = 0; j < NSC; ++j)
+      if (j < ns) M = fmaxf(M, v[j].x);
+#pragma unroll
+    for (int j = 0; j < NSC; ++j) {
       const float m = v[j].x, l = v[j].y;
-      const float w = (s0 + j >= ns || m == -INFINITY) ? 0.f : __expf(m - M);
+      const float w = (j >= ns || m == -INFINITY) ? 0.f : __expf(m - M);
       L += w * l;
       acc[0] += w * x0[j].x; acc[1] += w * x0[j].y; acc[2] += w * x0[j].z; acc[3] += w * x0[j].w;
       acc[4] += w * x1[j].x; acc[5] += w * x1[j].y; acc[6] += w * x1[j].z; acc[7] += w * x1[j].w;
+    }
+  } else {
+    // Any number of splits: a chunk of splits at a time (indices clamped, every load unconditional, surplus splits
+    // of a chunk masked afterwards), so a chunk costs one memory round trip: first the (max, sum) pairs of up to
+    // kMlChunk splits for the common maximum, then the partial outputs of kOChunk splits at a time.
+    constexpr int kMlChunk = 16, kOChunk = 8;
+    load_cs();
+    for (int s0 = 0; s0 < ns; s0 += kMlChunk) {
+      float2 v[kMlChunk];
+#pragma unroll
+      for (int j = 0; j < kMlChunk; ++j) v[j] = ml[slot_of(s0 + j)];
+#pragma unroll
+      for (int j = 0; j < kMlChunk; ++j)
+        if (s0 + j < ns) M = fmaxf(M, v[j].x);
+    }
+    for (int s0 = 0; s0 < ns; s0 += kOChunk) {
+      float2 v[kOChunk];
+      float4 x0[kOChunk], x1[kOChunk];
+#pragma unroll
+      for (int j = 0; j < kOChunk; ++j) {
+        const int64_t slot = slot_of(s0 + j);
+        v[j] = ml[slot];
+        const float4* src = reinterpret_cast<const float4*>(part_o + slot * kD + d0);
+        x0[j] = src[0];
+        x1[j] = src[1];
+      }
+#pragma unroll
+      for (int j = 0; j < kOChunk; ++j) {
+        // a surplus split of the last chunk gets weight 0 (its clamped loads read a real split, so the products are
+        // exact zeros); a branch here would let the compiler move the loads below it, one round trip each
+        const float m = v[j].x, l = v[j].y;
+        const float w = (s0 + j >= ns || m == -INFINITY) ? 0.f : __expf(m - M);
+        L += w * l;
+        acc[0] += w * x0[j].x; acc[1] += w * x0[j].y; acc[2] += w * x0[j].z; acc[3] += w * x0[j].w;
+        acc[4] += w * x1[j].x; acc[5] += w * x1[j].y; acc[6] += w * x1[j].z; acc[7] += w * x1[j].w;
+      }
     }
   }
   const float inv = (L > 0.f) ? 1.f / L : 0.f;
 #pragma unroll
   for (int k = 0; k < 8; ++k) acc[k] *= inv;
-  const int64_t p = a.q_pos[q];
-  const int R_ = a.cache.rope_dims;
-  const int base = kD - R_;
-  if (a.fuse_inv_rope && R_ > 0 && p >= 0 && p < a.rope_rows) {
-    const float* cs = a.rope_cs + p * int64_t(R_);
+  if (rot) {
 #pragma unroll
     for (int k = 0; k < 8; k += 2) {
       const int d = d0 + k;
       if (d >= base) {
-        const int j = (d - base) >> 1;
-        const float c = cs[2 * j], sn = cs[2 * j + 1];
+        const float c = csv[k / 2].x, sn = csv[k / 2].y;
         const float u = acc[k], v = acc[k + 1];
         acc[k] = u * c + v * sn;
         acc[k + 1] = -u * sn + v * c;
@@ -1551,9 +1589,13 @@ hipError_t launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStre
       hipLaunchKernelGGL((attend_split_kernel<true>), grid, dim3(512), 0, stream, a, sp, part_o, part_ml);
     else
       hipLaunchKernelGGL((attend_split_kernel<false>), grid, dim3(512), 0, stream, a, sp, part_o, part_ml);
-    if (sp.n_split > 1)
-      hipLaunchKernelGGL(attend_combine_kernel, dim3(unsigned(int64_t(a.n_q) * (a.n_heads / 4))), dim3(256), 0, stream,
-                         a, sp, part_o, part_ml);
+    if (sp.n_split > 1) {
+      const dim3 cgrid(unsigned(int64_t(a.n_q) * (a.n_heads / 4)));
+      if (sp.n_split <= 4) hipLaunchKernelGGL((attend_combine_kernel<4>), cgrid, dim3(256), 0, stream, a, sp, part_o, part_ml);
+      else if (sp.n_split <= 8) hipLaunchKernelGGL((attend_combine_kernel<8>), cgrid, dim3(256), 0, stream, a, sp, part_o, part_ml);
+      else if (sp.n_split <= 16) hipLaunchKernelGGL((attend_combine_kernel<16>), cgrid, dim3(256), 0, stream, a, sp, part_o, part_ml);
+      else hipLaunchKernelGGL((attend_combine_kernel<0>), cgrid, dim3(256), 0, stream, a, sp, part_o, part_ml);
+    }
     return hipGetLastError();
   }
   const bool mfma = a.cache.dtype != CSA_F32 && a.cache.dim == kD && a.n_heads % 16 == 0;
