@@ -551,8 +551,9 @@ struct LtPage {
 };
 
 // Page `phys` (clamped to 0 when unmapped) -> this lane's registers: 16 bytes of each 1 KiB of the page; fp8 / fp4:
-// lane l also takes entry l's scale word (fp8 scale bits, fp4 the four E8M0 bytes). The page loads are non-temporal
-// (each page is read once per step): measured 9 % faster on the 128K bf16 decode score than cached loads.
+// lane l also takes entry l's scale word (fp8 scale bits, fp4 the four E8M0 bytes). bf16 page loads are non-temporal
+// (each page is read once per step): 9 % faster on the 128K bf16 decode score than cached loads; on fp8 pages they
+// measured no faster, so those stay cached.
 template <int KF>
 __device__ __forceinline__ void lt_fetch(const IndexArgs& a, int32_t phys, int lane, u32x4 (&c)[LtPage<KF>::LOADS],
                                          uint32_t& sc) {
@@ -560,7 +561,10 @@ __device__ __forceinline__ void lt_fetch(const IndexArgs& a, int32_t phys, int l
   const int64_t page = phys >= 0 ? phys : 0;
   const char* src = static_cast<const char*>(a.cache.pages) + page * 64 * L::RAW_ROW + lane * 16;
 #pragma unroll
-  for (int i = 0; i < L::LOADS; ++i) c[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + i * 1024));
+  for (int i = 0; i < L::LOADS; ++i) {
+    if constexpr (KF == 0) c[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + i * 1024));
+    else c[i] = *reinterpret_cast<const u32x4*>(src + i * 1024);
+  }
   if (KF != 0) sc = reinterpret_cast<const uint32_t*>(a.cache.scales)[page * 64 + lane];
 }
 
