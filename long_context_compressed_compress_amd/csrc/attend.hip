@@ -311,10 +311,9 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a) {
           uint32_t w[8];
 #pragma unroll
           for (int h = 0; h < 4; ++h) {
-            const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(int(src[h]), false);
-            const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(int(src[h]), true);
-            w[2 * h] = __builtin_amdgcn_perm(__float_as_uint(f01[1]), __float_as_uint(f01[0]), 0x07060302u);
-            w[2 * h + 1] = __builtin_amdgcn_perm(__float_as_uint(f23[1]), __float_as_uint(f23[0]), 0x07060302u);
+            // exact pair conversion e4m3 -> bf16 (scale 1)
+            w[2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src[h], 1.0f, false));
+            w[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src[h], 1.0f, true));
           }
           uint4* dst = reinterpret_cast<uint4*>(k_lds + r * kRowStride + cc * 32);
           dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
@@ -653,10 +652,9 @@ __global__ void __launch_bounds__(512) attend_split_kernel(AttendArgs a, SplitPl
           uint32_t w[8];
 #pragma unroll
           for (int h = 0; h < 4; ++h) {
-            const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(int(src[h]), false);
-            const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(int(src[h]), true);
-            w[2 * h] = __builtin_amdgcn_perm(__float_as_uint(f01[1]), __float_as_uint(f01[0]), 0x07060302u);
-            w[2 * h + 1] = __builtin_amdgcn_perm(__float_as_uint(f23[1]), __float_as_uint(f23[0]), 0x07060302u);
+            // exact pair conversion e4m3 -> bf16 (scale 1)
+            w[2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src[h], 1.0f, false));
+            w[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src[h], 1.0f, true));
           }
           uint4* dst = reinterpret_cast<uint4*>(k_lds + r * kRowStride + cc * 32);
           dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
