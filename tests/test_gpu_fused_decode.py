@@ -57,6 +57,10 @@ FUSED_CASES = [
     # configurations outside the one-launch form: the call runs the two launches
     ("bf16", "fp8", 64, [3000, 259, 6]),
     ("bf16", "bf16", 32, [3000, 259, 6]),
+    # no query has an eligible entry at the first step (max_elig 0: the two launches and the empty-row select), the
+    # first entries complete during the later steps
+    ("bf16", "bf16", 64, [0, 1, 2]),
+    ("fp8", "fp4", 64, [2, 0]),
 ]
 
 
