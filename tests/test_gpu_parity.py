@@ -261,8 +261,9 @@ def _run_index_one_seq(pc, positions, q, w, mode, k, q_dtype):
 
 def test_index_topk_many_queries_long_bit_exact():
     """256 queries of one 600000-token sequence (up to 149999 eligible entries): the many-query select runs
-    several key chunks per query, keeps short queries' chosen-entry bitmaps in LDS and long ones (more than
-    131072 entries) in the workspace. Exact-grid keys and queries make every score exact and leave many equal
+    several key chunks per query and, as the launch's longest query has more than 131072 entries, keeps every
+    query's chosen-entry bitmap in the workspace (shorter launches keep them in LDS; the other many-query tests
+    cover those). Exact-grid keys and queries make every score exact and leave many equal
     scores, so ties at the boundary (lowest index first) and long candidate lists take part. A query's eligible
     entries are a prefix of the sequence's entry list, so the oracle's keys are taken once for the longest."""
     import synth
