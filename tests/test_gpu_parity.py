@@ -284,6 +284,29 @@ def test_index_topk_many_queries_long_bit_exact():
         assert np.array_equal(sc[b][:o_cnt].astype(np.float64), o_sc[:o_cnt]), p
 
 
+def test_index_topk_long_queries_bitmap_in_workspace():
+    """80 queries of one 1.1M-token sequence (up to 274999 eligible entries): more than 64 queries, so no mark pass;
+    the 1024-thread select runs several key chunks per query and, as the launch's longest query has more than
+    262144 entries, keeps every query's chosen-entry bitmap in the workspace. Exact-grid keys and queries as in the
+    many-query test above."""
+    import synth
+    P = 1100000
+    positions = np.unique(np.concatenate([np.linspace(9, P, 76).astype(np.int64), [P - 1, P, 1048576, 7]]))
+    assert 64 < len(positions) < 256
+    _log(f"index long queries, bitmap in the workspace: {len(positions)} queries up to {P}")
+    pc = si.paged_cache(73, 4, 32, "f32", [P], grid=True)
+    q = synth.grid_values(synth.rng(73, synth.STREAM_QIDX), (len(positions), 1, 32))
+    k = 64
+    out, cnt, sc = _run_index_one_seq(pc, positions, q, None, oi.DOT, k, "f32")
+    keys = oi.eligible_keys(pc.oracle(), 0, P)
+    for b, p in enumerate(positions):
+        n = paging.num_eligible(int(p), 4, 8)
+        o_idx, o_sc, o_cnt = oi.topk(oi.scores(keys[:n], q[b], None, oi.DOT), k)
+        assert cnt[b] == o_cnt, (p, cnt[b], o_cnt)
+        assert np.array_equal(out[b], o_idx), p
+        assert np.array_equal(sc[b][:o_cnt].astype(np.float64), o_sc[:o_cnt]), p
+
+
 def test_index_topk_many_queries_all_ties():
     """300 queries of one sequence, every score equal: each query's lowest k entries win. Up to 9999 tied
     candidates per query overflow the many-query select's LDS list into the workspace list."""
