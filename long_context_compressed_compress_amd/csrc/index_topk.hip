@@ -170,6 +170,19 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8_hw(uint2 v) {
   return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
 }
 
+// ReLU of an MFMA result as one v_med3_f32 (the median of x, 0 and +inf). fmaxf(x, 0) costs two instructions here:
+// the compiler first quiets a possible signalling NaN in the MFMA result. The infinity passes through an empty asm
+// statement so that the optimiser cannot fold the median back into fmaxf. For every non-NaN x the value is
+// fmaxf(x, 0)'s, up to the sign of a zero result, which adds nothing to the weighted sums it feeds (they start at +0).
+// The fp8 and fp4 page scores take it (their pages also need conversion work: 1M-entry decode scores 2.5 % and 5 %
+// faster); the bf16 score keeps fmaxf, which measured 2 % faster there.
+__device__ __forceinline__ float opaque_inf() {
+  float v = __builtin_inff();
+  asm("" : "+v"(v));
+  return v;
+}
+__device__ __forceinline__ float relu_med3(float x, float inf) { return __builtin_amdgcn_fmed3f(x, 0.f, inf); }
+
 // Sum over the four 16-lane rows of a wave, on the VALU: rows (0, 1) and (2, 3) first (16-lane swap), then the two
 // pair sums (32-lane swap); every lane ends with (x0 + x1) + (x2 + x3).
 __device__ __forceinline__ float rows4_sum_pairs(float x) {
@@ -184,6 +197,7 @@ __device__ __forceinline__ uint32_t score_page(const PageBuf<KF>& b, const bf16x
                                                const float (&wv)[HT][4], int kg) {
   uint32_t mine = 0u;
   float mine_f = 0.f;
+  const float inf = opaque_inf();
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     bf16x8 kb[4];
@@ -205,7 +219,7 @@ __device__ __forceinline__ uint32_t score_page(const PageBuf<KF>& b, const bf16x
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ht][ks], kb[ks], acc, 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) part += wv[ht][i] * fmaxf(acc[i], 0.f);
+      for (int i = 0; i < 4; ++i) part += wv[ht][i] * (KF == 0 ? fmaxf(acc[i], 0.f) : relu_med3(acc[i], inf));
     }
     part = rows4_sum_pairs(part);
     if constexpr (KF == 1) part *= b.sc[u];
@@ -575,6 +589,7 @@ __device__ __forceinline__ uint32_t lt_score_page(const char* st, const uint32_t
                                                   const float (&wv)[HT][4], int col, int kg) {
   using L = LtPage<KF>;
   float mine_f = 0.f;
+  const float inf = opaque_inf();
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const char* rowp = st + (u * 16 + col) * L::ROW;
@@ -602,7 +617,7 @@ __device__ __forceinline__ uint32_t lt_score_page(const char* st, const uint32_t
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ht][ks], kb[ks], acc, 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) part += wv[ht][i] * fmaxf(acc[i], 0.f);
+      for (int i = 0; i < 4; ++i) part += wv[ht][i] * (KF == 0 ? fmaxf(acc[i], 0.f) : relu_med3(acc[i], inf));
     }
     part = rows4_sum_pairs(part);
     if constexpr (KF == 1) part *= sc;
