@@ -1254,7 +1254,12 @@ __global__ void __launch_bounds__(NT, 4) select_kernel(IndexArgs a, Workspace ws
   __threadfence_block();
   __syncthreads();
 
-  // ---- compaction of the bitmap in index order (each thread owns a run of consecutive words)
+  // ---- compaction of the bitmap in index order (each thread owns a run of consecutive words). The chosen indices
+  // go to LDS first (the candidate list is done with), then every output slot is written from there with all of
+  // its key loads in flight together: reading each chosen entry's key where its bit is found cost one memory round
+  // trip per chosen entry of the thread's run, one after the other.
+  static_assert(2 * CLDS >= 2048, "the LDS index list holds the largest k");
+  int32_t* chosen_s = reinterpret_cast<int32_t*>(cand_s);
   const int64_t per_t = (n_words + NT - 1) / NT;
   const int64_t w0 = int64_t(tid) * per_t;
   uint32_t mine = 0;
@@ -1262,24 +1267,36 @@ __global__ void __launch_bounds__(NT, 4) select_kernel(IndexArgs a, Workspace ws
   uint32_t off;
   const uint32_t n_sel_all = block_excl_scan<NT>(mine, tmp, &off);
   const int n_sel = int(min<int64_t>(n_sel_all, kk));
-  int32_t* outq = a.out_idx + int64_t(q) * a.k;
-  float* outs = a.out_scores ? a.out_scores + int64_t(q) * a.k : nullptr;
-  for (int64_t w = w0; w < w0 + per_t && w < n_words; ++w) {
+  for (int64_t w = w0; w < w0 + per_t && w < n_words && off < uint32_t(n_sel); ++w) {
     uint32_t bits = bitmap[w];
-    while (bits) {
+    while (bits && off < uint32_t(n_sel)) {
       const int b = __ffs(bits) - 1;
       bits &= bits - 1;
-      const int32_t e = int32_t(w * 32 + b);
-      if (off < uint32_t(a.k)) {
-        outq[off] = e;
-        if (outs) outs[off] = key_score(keys_q[e]);
-      }
-      ++off;
+      chosen_s[off++] = int32_t(w * 32 + b);
     }
   }
-  for (int j = n_sel + tid; j < a.k; j += NT) {
-    outq[j] = -1;
-    if (outs) outs[j] = __uint_as_float(0x7FC00000u);
+  __syncthreads();
+  int32_t* outq = a.out_idx + int64_t(q) * a.k;
+  constexpr int R = (2048 + NT - 1) / NT;  // output slots per thread at the largest k
+  int32_t e[R];
+  uint32_t kv[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int j = tid + NT * r;
+    e[r] = j < n_sel ? chosen_s[j] : -1;
+  }
+  if (a.out_scores) {  // uniform
+#pragma unroll
+    for (int r = 0; r < R; ++r) kv[r] = keys_q[e[r] > 0 ? e[r] : 0];  // unconditional; row 0 exists
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int j = tid + NT * r;
+    if (j < a.k) {
+      outq[j] = e[r];
+      if (a.out_scores)
+        a.out_scores[int64_t(q) * a.k + j] = e[r] >= 0 ? key_score(kv[r]) : __uint_as_float(0x7FC00000u);
+    }
   }
   if (tid == 0 && a.out_count) a.out_count[q] = n_sel;
   // leave this query's histogram zeroed for the next score pass on this workspace
