@@ -807,12 +807,7 @@ template <int NT = kSelThreads>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, uint32_t* excl) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int NW = NT / 64;
-  uint32_t incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t t = __shfl_up(incl, off);
-    if (lane >= off) incl += t;
-  }
+  const uint32_t incl = wave_incl_scan(v);  // DPP: no LDS round trip per step as with lane shuffles
   if (lane == 63) tmp[wave] = incl;
   __syncthreads();
   uint32_t base = 0, total = 0;
@@ -838,13 +833,8 @@ __device__ __forceinline__ void wave0_digit_desc(const uint32_t* dig, int nbins,
     const int b = lane * per + j;
     if (b < nbins) own += dig[b];
   }
-  uint32_t suf = own;  // inclusive suffix over lanes
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t t = __shfl_down(suf, off);
-    if (lane + off < 64) suf += t;
-  }
-  uint32_t run = suf - own;  // digits above this lane's range
+  const uint32_t incl = wave_incl_scan(own);
+  uint32_t run = uint32_t(__builtin_amdgcn_readlane(int(incl), 63)) - incl;  // digits above this lane's range
   for (int j = per - 1; j >= 0; --j) {
     const int b = lane * per + j;
     if (b >= nbins) continue;
@@ -864,13 +854,7 @@ __device__ __forceinline__ void wave0_digit_asc(const uint32_t* dig, int nbins, 
     const int b = lane * per + j;
     if (b < nbins) own += dig[b];
   }
-  uint32_t pre = own;  // inclusive prefix over lanes
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t t = __shfl_up(pre, off);
-    if (lane >= off) pre += t;
-  }
-  uint32_t run = pre - own;
+  uint32_t run = wave_incl_scan(own) - own;  // digits below this lane's range
   for (int j = 0; j < per; ++j) {
     const int b = lane * per + j;
     if (b >= nbins) continue;
