@@ -197,6 +197,8 @@ INDEX_GRID_CASES = [
     ("bf16", 64, 128, oi.WRELU, 512, [300 + 13 * i for i in range(300)]),
     ("fp8", 64, 128, oi.WRELU, 512, [700 + 29 * i for i in range(288)]),
     ("bf16", 16, 128, oi.WRELU, 100, [5000 - 17 * i for i in range(260)]),
+    # many queries at the largest k: the half-size select writes four output slots per thread
+    ("bf16", 64, 128, oi.WRELU, 2048, [9000 + 7 * i for i in range(256)]),
     # many queries with few or no eligible entries (positions 0..39: 0..9 entries each)
     ("bf16", 64, 128, oi.WRELU, 4, [i % 40 for i in range(280)]),
 ]
