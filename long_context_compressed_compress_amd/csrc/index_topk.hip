@@ -174,8 +174,9 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8_hw(uint2 v) {
 // the compiler first quiets a possible signalling NaN in the MFMA result. The infinity passes through an empty asm
 // statement so that the optimiser cannot fold the median back into fmaxf. For every non-NaN x the value is
 // fmaxf(x, 0)'s, up to the sign of a zero result, which adds nothing to the weighted sums it feeds (they start at +0).
-// The fp8 and fp4 page scores take it (their pages also need conversion work: 1M-entry decode scores 2.5 % and 5 %
-// faster); the bf16 score keeps fmaxf, which measured 2 % faster there.
+// The prefill score (pages shared by 8 queries, bound by MFMA and VALU issue: 4.67 -> 4.16 ms for 2 x 2048 queries
+// at 256K) and the fp8 and MXFP4 decode scores take it (1M-entry decode 2.5 % and 5 % faster); the bf16 decode score
+// keeps fmaxf, which measured 2 % faster there (that kernel waits on HBM, not on instruction issue).
 __device__ __forceinline__ float opaque_inf() {
   float v = __builtin_inff();
   asm("" : "+v"(v));
@@ -219,7 +220,7 @@ __device__ __forceinline__ uint32_t score_page(const PageBuf<KF>& b, const bf16x
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ht][ks], kb[ks], acc, 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) part += wv[ht][i] * (KF == 0 ? fmaxf(acc[i], 0.f) : relu_med3(acc[i], inf));
+      for (int i = 0; i < 4; ++i) part += wv[ht][i] * relu_med3(acc[i], inf);
     }
     part = rows4_sum_pairs(part);
     if constexpr (KF == 1) part *= b.sc[u];
