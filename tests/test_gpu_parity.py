@@ -192,6 +192,8 @@ INDEX_GRID_CASES = [
     ("fp8", 2, 32, oi.WRELU, 1, [4000, 10]),
     # more than 2^18 eligible entries: the chosen-entry bitmap lives in the workspace, not in LDS
     ("bf16", 16, 128, oi.WRELU, 512, [1200000, 40000]),
+    # few queries of more than 2^16 entries (separate mark pass, bitmap in LDS) at the largest k
+    ("fp8", 64, 128, oi.WRELU, 2048, [400000, 300000]),
     # many queries in one launch: pages shared by the queries of a workgroup (one sequence per query here, so
     # every workgroup runs one round per query), bf16 and fp8 pages, 64 and 16 heads
     ("bf16", 64, 128, oi.WRELU, 512, [300 + 13 * i for i in range(300)]),
@@ -228,7 +230,8 @@ def test_index_topk_exact_grid_bit_exact(dtype, heads, dim, mode, k, positions):
 
 
 @pytest.mark.parametrize("k,positions", [(512, [5000, 3000, 30000]), (2048, [5000, 3000, 30000]),
-                                         (512, [300000, 70000, 2000]), (2048, [1100000, 2000])])
+                                         (512, [300000, 70000, 2000]), (2048, [400000, 90000, 2000]),
+                                         (2048, [1100000, 2000])])
 def test_index_topk_all_ties_takes_lowest_indices(k, positions):
     """Every score equal: the lowest k indices win. 30000 tokens give 7498 tied candidates, more than
     the select kernel's LDS list holds, so its workspace overflow list takes part. With few queries of more
